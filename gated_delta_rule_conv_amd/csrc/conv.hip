@@ -1,0 +1,220 @@
+// Depthwise causal conv1d with per-sequence conv state, gfx950.
+//
+// For a sequence with conv state cs (K-1 rows, oldest first) and tokens x_0..x_{L-1},
+// z = [cs ; x] and y_t[c] = act(b[c] + sum_{j<K} w[c][j] z_{t+j}[c]); the new conv
+// state is the last K-1 rows of z. ("System Design" (project_6), "GDN Kernel Dispatch
+// Detail": the depthwise causal Conv1d ahead of the L2 norm, and the conv state update
+// that opens the decode branch; aprender #5279, "Where concurrency is lost": conv
+// kernels with a sequence dimension and per-sequence conv state.)
+//
+// Layout: x / y rows are tokens, channels contiguous. Each thread owns 8 adjacent
+// channels (one 16-byte bf16 load or two 16-byte fp32 loads per row), so a wave
+// streams 512 channels = 1 KiB (bf16) of a row per load and stores 2 KiB of fp32.
+// The op is purely HBM-bound (8 flops per element), so there is no LDS staging: a
+// thread walks a strip of tokens keeping the K-1 previous rows of z in registers.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVec = 8;
+constexpr int kStrip = 16;  // tokens per block in prefill mode
+
+template <typename T, int K>
+struct ConvTaps {
+  float w[K][kVec];
+  float b[kVec];
+
+  __device__ __forceinline__ void load(const T* __restrict__ wp, const T* __restrict__ bp, int ch0) {
+    // w is [C][K]: the 8*K taps of channels ch0..ch0+7 are contiguous and 16-byte aligned.
+    float flat[K * kVec];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      float tmp[kVec];
+      Vec8<T>::load(wp + static_cast<int64_t>(ch0) * K + i * kVec, tmp);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) flat[i * kVec + e] = tmp[e];
+    }
+#pragma unroll
+    for (int c = 0; c < kVec; ++c)
+#pragma unroll
+      for (int j = 0; j < K; ++j) w[j][c] = flat[c * K + j];
+    if (bp) {
+      Vec8<T>::load(bp + ch0, b);
+    } else {
+#pragma unroll
+      for (int c = 0; c < kVec; ++c) b[c] = 0.f;
+    }
+  }
+
+  // win[0..K-2] = z rows preceding the current token (oldest first), cur = current token.
+  __device__ __forceinline__ void apply(const float (&win)[K - 1][kVec], const float (&cur)[kVec], bool silu,
+                                        float (&out)[kVec]) const {
+#pragma unroll
+    for (int c = 0; c < kVec; ++c) {
+      float acc = b[c];
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) acc = fmaf(w[j][c], win[j][c], acc);
+      acc = fmaf(w[K - 1][c], cur[c], acc);
+      if (silu) acc = acc / (1.0f + expf(-acc));
+      out[c] = acc;
+    }
+  }
+};
+
+template <typename T, int K>
+__global__ __launch_bounds__(kThreads) void conv_prefill_kernel(ConvArgs a) {
+  const int ch0 = (blockIdx.x * kThreads + threadIdx.x) * kVec;
+  if (ch0 >= a.channels) return;
+  const int C = a.channels;
+  const T* __restrict__ x = static_cast<const T*>(a.x);
+  const int* __restrict__ cu = a.cu_seqlens;
+  const int t0 = blockIdx.y * kStrip;
+  const int t1 = min(t0 + kStrip, a.total_tokens);
+
+  ConvTaps<T, K> taps;
+  taps.load(static_cast<const T*>(a.w), static_cast<const T*>(a.b), ch0);
+
+  // sequence holding t0: largest s with cu[s] <= t0 (cu[n] = total_tokens > t0)
+  int lo = 0, hi = a.n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t0) lo = mid; else hi = mid;
+  }
+  int s = lo;
+  int seq_start = cu[s];
+  int seq_end = cu[s + 1];
+
+  float win[K - 1][kVec];
+  bool reload = true;
+  for (int t = t0; t < t1; ++t) {
+    while (t >= seq_end) {  // next non-empty sequence starts at t
+      ++s;
+      seq_start = seq_end;
+      seq_end = cu[s + 1];
+      reload = true;
+    }
+    if (reload) {
+      const int p = t - seq_start;  // position of t in its sequence
+      const T* cs = reinterpret_cast<const T*>(a.state_ptrs[s]);
+#pragma unroll
+      for (int i = 0; i < K - 1; ++i) {
+        const int r = p + i;  // z row feeding tap i of token t
+        if (r < K - 1)
+          Vec8<T>::load(cs + static_cast<int64_t>(r) * C + ch0, win[i]);
+        else
+          Vec8<T>::load(x + static_cast<int64_t>(seq_start + r - (K - 1)) * a.x_stride + ch0, win[i]);
+      }
+      reload = false;
+    }
+    float cur[kVec], out[kVec];
+    Vec8<T>::load(x + static_cast<int64_t>(t) * a.x_stride + ch0, cur);
+    taps.apply(win, cur, a.silu != 0, out);
+    Vec8<float>::store(a.y + static_cast<int64_t>(t) * a.y_stride + ch0, out);
+#pragma unroll
+    for (int i = 0; i < K - 2; ++i)
+#pragma unroll
+      for (int c = 0; c < kVec; ++c) win[i][c] = win[i + 1][c];
+#pragma unroll
+    for (int c = 0; c < kVec; ++c) win[K - 2][c] = cur[c];
+  }
+}
+
+// After conv_prefill_kernel (stream order): each sequence's conv state becomes the last
+// K-1 rows of its z. A thread reads every row it needs before it writes any, and owns
+// its (sequence, channel group) column, so the in-place update cannot race.
+template <typename T, int K>
+__global__ __launch_bounds__(kThreads) void conv_commit_kernel(ConvArgs a) {
+  const int ch0 = (blockIdx.x * kThreads + threadIdx.x) * kVec;
+  if (ch0 >= a.channels) return;
+  const int s = blockIdx.y;
+  const int start = a.cu_seqlens[s];
+  const int L = a.cu_seqlens[s + 1] - start;
+  if (L <= 0) return;
+  const int C = a.channels;
+  const T* __restrict__ x = static_cast<const T*>(a.x);
+  T* cs = reinterpret_cast<T*>(a.state_ptrs[s]);
+  float nz[K - 1][kVec];
+#pragma unroll
+  for (int i = 0; i < K - 1; ++i) {
+    const int r = L + i;  // row of z that becomes new state row i
+    if (r < K - 1)
+      Vec8<T>::load(cs + static_cast<int64_t>(r) * C + ch0, nz[i]);
+    else
+      Vec8<T>::load(x + static_cast<int64_t>(start + r - (K - 1)) * a.x_stride + ch0, nz[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < K - 1; ++i) Vec8<T>::store(cs + static_cast<int64_t>(i) * C + ch0, nz[i]);
+}
+
+// Decode mode: token i belongs to slot i (sequence length 1); conv and state shift in one
+// pass, in place. A zero state pointer marks an inactive slot.
+template <typename T, int K>
+__global__ __launch_bounds__(kThreads) void conv_decode_kernel(ConvArgs a) {
+  const int ch0 = (blockIdx.x * kThreads + threadIdx.x) * kVec;
+  if (ch0 >= a.channels) return;
+  const int i = blockIdx.y;
+  const uint64_t sp = a.state_ptrs[i];
+  if (sp == 0) return;
+  const int C = a.channels;
+  T* cs = reinterpret_cast<T*>(sp);
+  ConvTaps<T, K> taps;
+  taps.load(static_cast<const T*>(a.w), static_cast<const T*>(a.b), ch0);
+  float win[K - 1][kVec], cur[kVec], out[kVec];
+#pragma unroll
+  for (int r = 0; r < K - 1; ++r) Vec8<T>::load(cs + static_cast<int64_t>(r) * C + ch0, win[r]);
+  Vec8<T>::load(static_cast<const T*>(a.x) + static_cast<int64_t>(i) * a.x_stride + ch0, cur);
+  taps.apply(win, cur, a.silu != 0, out);
+  Vec8<float>::store(a.y + static_cast<int64_t>(i) * a.y_stride + ch0, out);
+#pragma unroll
+  for (int r = 0; r < K - 2; ++r) Vec8<T>::store(cs + static_cast<int64_t>(r) * C + ch0, win[r + 1]);
+  Vec8<T>::store(cs + static_cast<int64_t>(K - 2) * C + ch0, cur);
+}
+
+template <typename T>
+hipError_t launch_all(const ConvArgs& a, hipStream_t s, bool decode) {
+  const unsigned gx = (a.channels / kVec + kThreads - 1) / kThreads;
+  if (decode) {
+    if (a.n == 0) return hipSuccess;
+    dim3 grid(gx, a.n);
+    switch (a.width) {
+      case 2: conv_decode_kernel<T, 2><<<grid, kThreads, 0, s>>>(a); break;
+      case 3: conv_decode_kernel<T, 3><<<grid, kThreads, 0, s>>>(a); break;
+      default: conv_decode_kernel<T, 4><<<grid, kThreads, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+  }
+  if (a.total_tokens > 0) {
+    dim3 grid(gx, (a.total_tokens + kStrip - 1) / kStrip);
+    switch (a.width) {
+      case 2: conv_prefill_kernel<T, 2><<<grid, kThreads, 0, s>>>(a); break;
+      case 3: conv_prefill_kernel<T, 3><<<grid, kThreads, 0, s>>>(a); break;
+      default: conv_prefill_kernel<T, 4><<<grid, kThreads, 0, s>>>(a); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.n == 0) return hipSuccess;
+  dim3 grid(gx, a.n);
+  switch (a.width) {
+    case 2: conv_commit_kernel<T, 2><<<grid, kThreads, 0, s>>>(a); break;
+    case 3: conv_commit_kernel<T, 3><<<grid, kThreads, 0, s>>>(a); break;
+    default: conv_commit_kernel<T, 4><<<grid, kThreads, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv_prefill(const ConvArgs& a, hipStream_t s) {
+  return a.bf16 ? launch_all<uint16_t>(a, s, false) : launch_all<float>(a, s, false);
+}
+
+hipError_t launch_conv_decode(const ConvArgs& a, hipStream_t s) {
+  return a.bf16 ? launch_all<uint16_t>(a, s, true) : launch_all<float>(a, s, true);
+}
+
+}  // namespace gdn

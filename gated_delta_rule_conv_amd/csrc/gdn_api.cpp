@@ -1,0 +1,205 @@
+// C-ABI entry points of libgdn: host-side argument checks, then kernel launches.
+// Every check is O(1) on host values; no device memory is read from the host and
+// nothing is launched when a check fails.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/gdn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+gdn_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return GDN_OK;
+  return fail(GDN_ERR_HIP, "%s: HIP error %d (%s)", what, static_cast<int>(e), hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by every entry point that takes dims.
+gdn_status check_dims(const gdn_dims* d, const char* fn) {
+  if (!d) return fail(GDN_ERR_NULL, "%s: dims is NULL", fn);
+  if (d->struct_size != static_cast<int32_t>(sizeof(gdn_dims)))
+    return fail(GDN_ERR_SHAPE, "%s: dims->struct_size is %d, expected %d", fn, d->struct_size,
+                static_cast<int>(sizeof(gdn_dims)));
+  if (d->num_k_heads < 1 || d->num_v_heads < 1)
+    return fail(GDN_ERR_SHAPE, "%s: head counts must be >= 1 (Hk=%d, Hv=%d)", fn, d->num_k_heads, d->num_v_heads);
+  if (d->num_v_heads % d->num_k_heads != 0)
+    return fail(GDN_ERR_SHAPE, "%s: num_v_heads (%d) must be a multiple of num_k_heads (%d)", fn, d->num_v_heads,
+                d->num_k_heads);
+  if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: head_dim %d not built (32, 64, 128)", fn, d->head_dim);
+  if (d->conv_width < 2 || d->conv_width > 4)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: conv_width %d not built (2, 3, 4)", fn, d->conv_width);
+  if (d->chunk_size != 16 && d->chunk_size != 32 && d->chunk_size != 64)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: chunk_size %d not built (16, 32, 64)", fn, d->chunk_size);
+  if (d->activation != GDN_ACT_NONE && d->activation != GDN_ACT_SILU)
+    return fail(GDN_ERR_DTYPE, "%s: unknown activation %d", fn, d->activation);
+  if (d->in_dtype != GDN_F32 && d->in_dtype != GDN_BF16)
+    return fail(GDN_ERR_DTYPE, "%s: unknown in_dtype %d", fn, d->in_dtype);
+  if (d->mma != GDN_MMA_AUTO && d->mma != GDN_MMA_FP32 && d->mma != GDN_MMA_BF16X3)
+    return fail(GDN_ERR_DTYPE, "%s: unknown mma policy %d", fn, d->mma);
+  if (!(d->l2_eps >= 0.0f) || !(d->l2_eps < 1e30f))
+    return fail(GDN_ERR_SHAPE, "%s: l2_eps must be finite and >= 0", fn);
+  if (!(d->scale == d->scale) || d->scale > 1e30f || d->scale < -1e30f)
+    return fail(GDN_ERR_SHAPE, "%s: scale must be finite", fn);
+  const int64_t C = static_cast<int64_t>(d->head_dim) * (2 * d->num_k_heads + d->num_v_heads);
+  if (C > (1 << 24)) return fail(GDN_ERR_SHAPE, "%s: channel count %lld too large", fn, static_cast<long long>(C));
+  return GDN_OK;
+}
+
+int64_t channels(const gdn_dims* d) {
+  return static_cast<int64_t>(d->head_dim) * (2 * d->num_k_heads + d->num_v_heads);
+}
+
+// q/k/v of the recurrence entry points.
+gdn_status check_qkv(const gdn_dims* d, const char* fn, const float* q, int64_t qs, const float* k, int64_t ks,
+                     const float* v, int64_t vs, const float* g, const float* beta, float* o, int32_t rows) {
+  if (!q || !k || !v || !g || !beta || !o) return fail(GDN_ERR_NULL, "%s: q, k, v, g, beta and o are required", fn);
+  const int64_t qk_w = static_cast<int64_t>(d->num_k_heads) * d->head_dim;
+  const int64_t v_w = static_cast<int64_t>(d->num_v_heads) * d->head_dim;
+  if (rows > 1 && (qs < qk_w || ks < qk_w || vs < v_w))
+    return fail(GDN_ERR_SHAPE, "%s: row strides (q %lld, k %lld, v %lld) below row widths (%lld, %lld)", fn,
+                static_cast<long long>(qs), static_cast<long long>(ks), static_cast<long long>(vs),
+                static_cast<long long>(qk_w), static_cast<long long>(v_w));
+  if (qs < 0 || ks < 0 || vs < 0) return fail(GDN_ERR_SHAPE, "%s: negative stride", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (qs % 4) || (ks % 4) || (vs % 4))
+    return fail(GDN_ERR_ALIGN, "%s: q, k, v must be 16-byte aligned with strides a multiple of 4 elements", fn);
+  return GDN_OK;
+}
+
+int resolve_mma(const gdn_dims* d) {
+  if (d->mma != GDN_MMA_AUTO) return d->mma;
+  return d->in_dtype == GDN_F32 ? GDN_MMA_FP32 : GDN_MMA_BF16X3;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+gdn_status gdn_conv_update(const gdn_dims* dims, const void* x, int64_t x_stride, float* y, int64_t y_stride,
+                           const void* conv_w, const void* conv_b, const int32_t* cu_seqlens,
+                           const uint64_t* conv_state_ptrs, int32_t n, int32_t total_tokens, void* stream) {
+  const char* fn = "gdn_conv_update";
+  if (gdn_status st = check_dims(dims, fn)) return st;
+  if (n < 0 || total_tokens < 0) return fail(GDN_ERR_SHAPE, "%s: negative n or total_tokens", fn);
+  const bool decode = cu_seqlens == nullptr;
+  if (decode && total_tokens != n)
+    return fail(GDN_ERR_SHAPE, "%s: decode mode (cu_seqlens NULL) needs total_tokens == n (%d vs %d)", fn,
+                total_tokens, n);
+  if (!decode && n == 0 && total_tokens != 0)
+    return fail(GDN_ERR_SHAPE, "%s: tokens without sequences", fn);
+  if (total_tokens == 0 && n == 0) return GDN_OK;
+  if (!x || !y || !conv_w || !conv_state_ptrs)
+    return fail(GDN_ERR_NULL, "%s: x, y, conv_w and conv_state_ptrs are required", fn);
+  const int64_t C = channels(dims);
+  const int64_t esz = dims->in_dtype == GDN_BF16 ? 2 : 4;
+  if (total_tokens > 1 && (x_stride < C || y_stride < C))
+    return fail(GDN_ERR_SHAPE, "%s: row strides (x %lld, y %lld) below channel count %lld", fn,
+                static_cast<long long>(x_stride), static_cast<long long>(y_stride), static_cast<long long>(C));
+  if (x_stride < 0 || y_stride < 0) return fail(GDN_ERR_SHAPE, "%s: negative stride", fn);
+  if (!aligned16(x) || !aligned16(y) || !aligned16(conv_w) || (conv_b && !aligned16(conv_b)) ||
+      (x_stride * esz) % 16 || (y_stride * 4) % 16)
+    return fail(GDN_ERR_ALIGN, "%s: x, y, conv_w, conv_b must be 16-byte aligned and row strides multiples of 16 bytes",
+                fn);
+  gdn::ConvArgs a{x, x_stride, y, y_stride, conv_w, conv_b, cu_seqlens, conv_state_ptrs, n, total_tokens,
+                  static_cast<int32_t>(C), dims->conv_width, dims->activation == GDN_ACT_SILU,
+                  dims->in_dtype == GDN_BF16};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(decode ? gdn::launch_conv_decode(a, s) : gdn::launch_conv_prefill(a, s), fn);
+}
+
+gdn_status gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, int32_t total_tokens, size_t* bytes) {
+  const char* fn = "gdn_prefill_workspace_size";
+  if (gdn_status st = check_dims(dims, fn)) return st;
+  if (!bytes) return fail(GDN_ERR_NULL, "%s: bytes is NULL", fn);
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_SHAPE, "%s: negative count", fn);
+  *bytes = gdn::prefill_workspace_bytes(dims->num_v_heads, dims->head_dim, dims->chunk_size, num_seqs, total_tokens);
+  return GDN_OK;
+}
+
+gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_stride, const float* k,
+                               int64_t k_stride, const float* v, int64_t v_stride, const float* g,
+                               const float* beta, float* o, const int32_t* cu_seqlens, int32_t num_seqs,
+                               int32_t total_tokens, const uint64_t* state_ptrs, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_prefill_chunked";
+  if (gdn_status st = check_dims(dims, fn)) return st;
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_SHAPE, "%s: negative count", fn);
+  if (num_seqs == 0) {
+    if (total_tokens != 0) return fail(GDN_ERR_SHAPE, "%s: tokens without sequences", fn);
+    return GDN_OK;
+  }
+  if (!cu_seqlens || !state_ptrs) return fail(GDN_ERR_NULL, "%s: cu_seqlens and state_ptrs are required", fn);
+  if (total_tokens > 0) {
+    if (gdn_status st = check_qkv(dims, fn, q, q_stride, k, k_stride, v, v_stride, g, beta, o, total_tokens))
+      return st;
+  }
+  const size_t need =
+      gdn::prefill_workspace_bytes(dims->num_v_heads, dims->head_dim, dims->chunk_size, num_seqs, total_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(GDN_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  gdn::PrefillArgs a{};
+  a.r = gdn::RecurArgs{q, q_stride, k, k_stride, v, v_stride, g, beta, o, state_ptrs, dims->num_k_heads,
+                       dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale};
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.chunk = dims->chunk_size;
+  a.mma = resolve_mma(dims);
+  a.workspace = workspace;
+  return hip_status(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_stride, const float* k,
+                              int64_t k_stride, const float* v, int64_t v_stride, const float* g,
+                              const float* beta, float* o, const uint64_t* state_ptrs, int32_t m, void* stream) {
+  const char* fn = "gdn_decode_batched";
+  if (gdn_status st = check_dims(dims, fn)) return st;
+  if (m < 0) return fail(GDN_ERR_SHAPE, "%s: negative m", fn);
+  if (m == 0) return GDN_OK;
+  if (m > 65535) return fail(GDN_ERR_SHAPE, "%s: m = %d above the grid limit 65535", fn, m);
+  if (!state_ptrs) return fail(GDN_ERR_NULL, "%s: state_ptrs is required", fn);
+  if (gdn_status st = check_qkv(dims, fn, q, q_stride, k, k_stride, v, v_stride, g, beta, o, m)) return st;
+  gdn::RecurArgs a{q, q_stride, k, k_stride, v, v_stride, g, beta, o, state_ptrs, dims->num_k_heads,
+                   dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale};
+  return hip_status(gdn::launch_decode(a, m, static_cast<hipStream_t>(stream)), fn);
+}
+
+gdn_status gdn_slot_pointers(uint64_t pool_base, int64_t slot_bytes, int32_t pool_slots, const int32_t* slot_idx,
+                             int32_t m, uint64_t* out_ptrs, void* stream) {
+  const char* fn = "gdn_slot_pointers";
+  if (m < 0 || pool_slots < 0 || slot_bytes <= 0) return fail(GDN_ERR_SHAPE, "%s: bad m, pool_slots or slot_bytes", fn);
+  if (m == 0) return GDN_OK;
+  if (!pool_base || !slot_idx || !out_ptrs) return fail(GDN_ERR_NULL, "%s: pool_base, slot_idx, out_ptrs required", fn);
+  if ((pool_base & 15u) || (slot_bytes & 15))
+    return fail(GDN_ERR_ALIGN, "%s: pool_base and slot_bytes must be multiples of 16", fn);
+  return hip_status(
+      gdn::launch_slot_pointers(pool_base, slot_bytes, pool_slots, slot_idx, m, out_ptrs, static_cast<hipStream_t>(stream)),
+      fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal launcher interface between the C-ABI layer (gdn_api.cpp) and the kernels.
+// Launchers assume their arguments were validated by the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct ConvArgs {
+  const void* x;
+  int64_t x_stride;
+  float* y;
+  int64_t y_stride;
+  const void* w;
+  const void* b;  // nullable
+  const int32_t* cu_seqlens;  // nullable (decode mode)
+  const uint64_t* state_ptrs;
+  int32_t n;
+  int32_t total_tokens;
+  int32_t channels;
+  int32_t width;  // K
+  int32_t silu;
+  int32_t bf16;  // in_dtype == BF16
+};
+
+hipError_t launch_conv_prefill(const ConvArgs& a, hipStream_t s);
+hipError_t launch_conv_decode(const ConvArgs& a, hipStream_t s);
+
+struct RecurArgs {
+  const float* q;
+  int64_t q_stride;
+  const float* k;
+  int64_t k_stride;
+  const float* v;
+  int64_t v_stride;
+  const float* g;
+  const float* beta;
+  float* o;
+  const uint64_t* state_ptrs;
+  int32_t hk;
+  int32_t hv;
+  int32_t d;
+  float eps;
+  float scale;
+};
+
+hipError_t launch_decode(const RecurArgs& a, int32_t m, hipStream_t s);
+
+struct PrefillArgs {
+  RecurArgs r;
+  const int32_t* cu_seqlens;
+  int32_t num_seqs;
+  int32_t total_tokens;
+  int32_t chunk;
+  int32_t mma;  // 1 = fp32, 2 = bf16x3 (resolved)
+  void* workspace;
+};
+
+size_t prefill_workspace_bytes(int32_t hv, int32_t d, int32_t chunk, int32_t num_seqs, int32_t total_tokens);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+hipError_t launch_slot_pointers(uint64_t base, int64_t slot_bytes, int32_t pool_slots, const int32_t* idx,
+                                int32_t m, uint64_t* out, hipStream_t s);
+
+}  // namespace gdn

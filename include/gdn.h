@@ -1,0 +1,202 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet layer core.
+ *
+ * The layer core, in order ("System Design" (project_6 SYSTEM_DESIGN.md),
+ * sections "Runtime Data Flow" and "GDN Kernel Dispatch Detail"):
+ *   1. a depthwise causal conv1d over the projected q|k|v channels, each sequence
+ *      continuing from its own conv state;
+ *   2. L2 normalisation of every q and k head vector;
+ *   3. the gated delta rule over a fixed-size fp32 state per sequence and v-head,
+ *        S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t,
+ *      run either as a chunked prefill over packed ragged sequences (the chunked
+ *      prefill kernel of that section takes (q, k, v, g, beta, state) and updates the
+ *      temporal state) or as a batched single-token decode.
+ * The decode batches over m slots, each reached through a device array of u64
+ * per-slot state pointers with the slot index on the grid ("serve: Qwen3.5 on CUDA
+ * never batches concurrent requests", aprender #5279, comment "Phase plan", phase
+ * P5); conv and delta-rule kernels carry a sequence dimension with per-sequence
+ * conv and SSM state (same issue, comment "Where concurrency is lost", item 3).
+ *
+ * Conventions for every entry point
+ *  - Every pointer argument except `dims`, `bytes` and `stream` is a DEVICE pointer
+ *    (HIP global memory) owned by the caller. The library allocates nothing, keeps
+ *    no device state, and never reads device memory from the host.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream). Calls on different streams are thread-safe.
+ *  - Argument checks are host-only and O(1); a failed check returns a status,
+ *    launches nothing and sets the thread-local text of gdn_last_error(). A failed
+ *    launch returns GDN_ERR_HIP with the HIP error text.
+ *  - Strides are in ELEMENTS of the pointed-to type.
+ *  - Unchecked preconditions (undefined behaviour when violated): device pointers
+ *    are valid for the stated extents; per-slot pointers within one call are
+ *    distinct; outputs alias no input; g <= 0 and finite; beta in [0, 1];
+ *    cu_seqlens is non-decreasing from 0 to total_tokens.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+  GDN_ERR_SHAPE = 2,       /* a count, size or stride is out of range or inconsistent */
+  GDN_ERR_DTYPE = 3,       /* unknown dtype / activation / precision-policy value */
+  GDN_ERR_ALIGN = 4,       /* a pointer or stride breaks the 16-byte alignment rule */
+  GDN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than gdn_prefill_workspace_size */
+  GDN_ERR_UNSUPPORTED = 6, /* valid but not built: head dim, chunk size or conv width */
+  GDN_ERR_HIP = 7          /* the HIP runtime failed the launch */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Activation applied to the conv output. The pages name the conv only as a depthwise
+ * causal Conv1d, so the default is the identity; SiLU is offered as an option. */
+typedef enum gdn_activation { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_activation;
+
+/* Matrix-core precision of the prefill contractions (decode is plain fp32 FMA).
+ *  AUTO   : FP32 when in_dtype is F32, BF16X3 when in_dtype is BF16.
+ *  FP32   : v_mfma_f32_16x16x4_f32, fp32 operands.
+ *  BF16X3 : every fp32 operand split as hi + lo (two bf16 values); each product is
+ *           hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16 with fp32 accumulation
+ *           ("bf16x3", Henry, Tang & Heinecke, ARITH 2019). */
+typedef enum gdn_mma { GDN_MMA_AUTO = 0, GDN_MMA_FP32 = 1, GDN_MMA_BF16X3 = 2 } gdn_mma;
+
+/* Layer dimensions and options, passed by pointer. struct_size must be
+ * sizeof(gdn_dims) as compiled by the caller (lets the struct grow later). */
+typedef struct gdn_dims {
+  int32_t struct_size;
+  int32_t num_k_heads; /* Hk >= 1 (q and k heads) */
+  int32_t num_v_heads; /* Hv >= 1 with Hv % Hk == 0; v-head j reads k-head j / (Hv / Hk) */
+  int32_t head_dim;    /* d = d_k = d_v; built for 32, 64 and 128 */
+  int32_t conv_width;  /* K; built for 2, 3 and 4 */
+  int32_t chunk_size;  /* prefill chunk length; built for 16, 32 and 64 */
+  int32_t activation;  /* gdn_activation */
+  int32_t in_dtype;    /* gdn_dtype of x, conv weight, conv bias and conv state */
+  int32_t mma;         /* gdn_mma */
+  float l2_eps;        /* k^ = k / sqrt(|k|^2 + l2_eps); q^ likewise, then times scale */
+  float scale;         /* multiplies q^ (1.0 = no scaling) */
+} gdn_dims;
+
+/* Conv channel count C = 2*Hk*d + Hv*d, channels ordered [q heads | k heads | v heads]. */
+
+/* ---------------------------------------------------------------------------------
+ * gdn_conv_update -- depthwise causal conv1d + conv-state update (both modes).
+ *
+ * For one sequence with conv state cs (K-1 rows, oldest first) and tokens x_0..x_{L-1},
+ * let z = [cs_0 .. cs_{K-2}, x_0 .. x_{L-1}]. Then per channel c
+ *     y_t[c] = act( b[c] + sum_{j<K} w[c][j] * z_{t+j}[c] ),     t = 0 .. L-1
+ * (w[c][K-1] multiplies the current token) and the new conv state is the last K-1
+ * rows of z. ("System Design", "GDN Kernel Dispatch Detail": Conv1d before the L2
+ * norm in prefill; conv state update first in the decode branch.)
+ *
+ *  x          [total_tokens][C] in_dtype, row stride x_stride (>= C).
+ *  y          [total_tokens][C] fp32 output, row stride y_stride (>= C). Feed q/k/v
+ *             views of y to gdn_prefill_chunked / gdn_decode_batched.
+ *  conv_w     [C][K] in_dtype, contiguous.   conv_b: [C] in_dtype, or NULL for no bias.
+ *  cu_seqlens prefill mode: device int32 [n+1], sequence s owns tokens
+ *             [cu_seqlens[s], cu_seqlens[s+1]); a zero-length sequence keeps its state.
+ *             NULL selects decode mode: token i belongs to slot i and total_tokens == n.
+ *  conv_state_ptrs  device u64 [n]; entry s points at sequence/slot s's conv state,
+ *             [K-1][C] in_dtype contiguous, 16-byte aligned, read and updated in place.
+ *             Decode mode only: an entry of 0 marks an inactive slot (its y row is left
+ *             untouched and nothing is read for it).
+ *  Prefill mode launches two kernels in stream order (outputs, then state commit), so
+ *  the in-place state update never races with a read of the old state.
+ *  Alignment: x, y 16-byte aligned; x_stride * elt_size and y_stride * 4 multiples of 16.
+ */
+gdn_status gdn_conv_update(const gdn_dims* dims, const void* x, int64_t x_stride, float* y,
+                           int64_t y_stride, const void* conv_w, const void* conv_b,
+                           const int32_t* cu_seqlens, const uint64_t* conv_state_ptrs, int32_t n,
+                           int32_t total_tokens, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * gdn_prefill_workspace_size -- bytes of device workspace gdn_prefill_chunked needs
+ * for at most num_seqs sequences and total_tokens tokens (written to *bytes).
+ */
+gdn_status gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, int32_t total_tokens,
+                                      size_t* bytes);
+
+/* ---------------------------------------------------------------------------------
+ * gdn_prefill_chunked -- L2 norm + gated delta rule over packed ragged sequences,
+ * chunked ("System Design", "GDN Kernel Dispatch Detail": the prefill branch runs a
+ * chunked gated-delta-rule kernel on (q, k, v, g, beta, state), then updates the
+ * temporal state).
+ *
+ * Chunks of chunk_size tokens start at each sequence's own first token, so the
+ * arithmetic of a sequence does not depend on what else is packed with it.
+ *
+ *  q, k       [total_tokens][Hk*d] fp32 (raw conv output; normalised inside), row
+ *             strides q_stride, k_stride.   v: [total_tokens][Hv*d] fp32, stride v_stride.
+ *  g, beta    [total_tokens][Hv] fp32 contiguous: log-decay (<= 0) and write strength.
+ *  o          [total_tokens][Hv][d] fp32 contiguous output.
+ *  cu_seqlens device int32 [num_seqs+1].
+ *  state_ptrs device u64 [num_seqs]; entry s points at sequence s's state, fp32
+ *             [Hv][d_v][d_k] (d_k contiguous), 16-byte aligned; read as the initial
+ *             state and overwritten with the final state. Zero-length sequences keep it.
+ *  workspace  device scratch of at least gdn_prefill_workspace_size(dims, num_seqs,
+ *             total_tokens) bytes, 256-byte aligned; contents on entry are ignored.
+ *  Alignment: q, k, v 16-byte aligned, strides multiples of 4 elements.
+ */
+gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_stride, const float* k,
+                               int64_t k_stride, const float* v, int64_t v_stride, const float* g,
+                               const float* beta, float* o, const int32_t* cu_seqlens, int32_t num_seqs,
+                               int32_t total_tokens, const uint64_t* state_ptrs, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * gdn_decode_batched -- one token for each of m slots: L2 norm + one step of the gated
+ * delta rule on each slot's state, in place ("System Design", "GDN Kernel Dispatch
+ * Detail", decode branch: decay the temporal state and write the delta, then
+ * multiply the query by the state; aprender #5279, "Phase plan", P5: slot index on
+ * the grid, device u64[m] array of per-slot state pointers).
+ *
+ * Each slot's result is the same bits whatever m is and whatever other slots are in
+ * the call: no reduction crosses slots and every reduction has a fixed order.
+ *
+ *  q, k       [m][Hk*d] fp32, row strides q_stride, k_stride (raw; normalised inside).
+ *  v          [m][Hv*d] fp32, row stride v_stride.
+ *  g, beta    [m][Hv] fp32 contiguous.
+ *  o          [m][Hv][d] fp32 contiguous output.
+ *  state_ptrs device u64 [m]; entry i points at slot i's fp32 [Hv][d_v][d_k] state
+ *             (16-byte aligned), updated in place. An entry of 0 marks an inactive
+ *             slot: nothing is read or written for it (its o rows are left untouched).
+ *  Alignment: q, k, v 16-byte aligned, strides multiples of 4 elements.
+ */
+gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_stride, const float* k,
+                              int64_t k_stride, const float* v, int64_t v_stride, const float* g,
+                              const float* beta, float* o, const uint64_t* state_ptrs, int32_t m,
+                              void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * gdn_slot_pointers -- build a device u64 pointer array from slot indices, on the
+ * device: out_ptrs[i] = pool_base + slot_idx[i] * slot_bytes, or 0 when slot_idx[i]
+ * is outside [0, pool_slots) (an inactive slot). The slot pool is one caller-owned
+ * allocation of pool_slots fixed-size blocks ("qLLM", section "What this is": a
+ * fixed-size recurrent-state / conv-buffer slot pool; aprender #5279, "Phase plan",
+ * P5: a device u64[m] array of per-layer state pointers).
+ *
+ *  pool_base  device address of slot 0 (16-byte aligned); slot_bytes: multiple of 16.
+ *  slot_idx   device int32 [m].   out_ptrs: device u64 [m].
+ */
+gdn_status gdn_slot_pointers(uint64_t pool_base, int64_t slot_bytes, int32_t pool_slots,
+                             const int32_t* slot_idx, int32_t m, uint64_t* out_ptrs, void* stream);
+
+/* Thread-local text describing the last non-OK status returned on this thread. */
+const char* gdn_last_error(void);
+
+/* GDN_ABI_VERSION of the built library. */
+int32_t gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,160 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+The library must load without a GPU, export every entry point include/gdn.h declares,
+and reject every invalid call with the documented status before any HIP call. Every
+call below carries at least one argument that fails a host check, so none of them
+can launch a kernel (the fake addresses are never dereferenced).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_conv_amd as gdn
+from gated_delta_rule_conv_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "gdn.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^(?:gdn_status|const char\*|int32_t)\s+(gdn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_symbols_are_exported():
+    syms = _declared_symbols()
+    assert set(syms) == set(_lib.EXPORTED)
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_abi_version_and_struct_size():
+    assert gdn.gdn_abi_version() == 1
+    assert ctypes.sizeof(_lib.gdn_dims) == 11 * 4
+
+
+def dims(**kw):
+    base = dict(num_k_heads=16, num_v_heads=32, head_dim=128, conv_width=4, chunk_size=64)
+    base.update(kw)
+    return gdn.make_dims(**base)
+
+
+def _status(fn, *args):
+    with pytest.raises(gdn.GDNError) as e:
+        fn(*args)
+    return e.value.status, str(e.value)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(conv_width=5), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(conv_width=1), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(chunk_size=128), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(num_k_heads=3, num_v_heads=32), _lib.GDN_ERR_SHAPE),
+    (dict(num_k_heads=0), _lib.GDN_ERR_SHAPE),
+    (dict(in_dtype=7), _lib.GDN_ERR_DTYPE),
+    (dict(activation=3), _lib.GDN_ERR_DTYPE),
+    (dict(mma=9), _lib.GDN_ERR_DTYPE),
+    (dict(l2_eps=-1.0), _lib.GDN_ERR_SHAPE),
+])
+def test_bad_dims_rejected_everywhere(kw, status):
+    d = dims(**kw)
+    st, _ = _status(gdn.gdn_prefill_workspace_size, d, 1, 10)
+    assert st == status
+    st, _ = _status(gdn.gdn_decode_batched, d, FAKE, 4096, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, 4, 0)
+    assert st == status
+    st, _ = _status(gdn.gdn_conv_update, d, FAKE, 8192, FAKE, 8192, FAKE, None, FAKE, FAKE, 1, 4, 0)
+    assert st == status
+
+
+def test_struct_size_checked():
+    d = dims()
+    d.struct_size = 12
+    st, msg = _status(gdn.gdn_prefill_workspace_size, d, 1, 10)
+    assert st == _lib.GDN_ERR_SHAPE and "struct_size" in msg
+
+
+def test_null_dims():
+    lib = _lib.lib()
+    size = ctypes.c_size_t()
+    assert lib.gdn_prefill_workspace_size(None, 1, 1, ctypes.byref(size)) == _lib.GDN_ERR_NULL
+    assert "dims" in gdn.gdn_last_error()
+
+
+def test_decode_argument_checks():
+    d = dims()
+    ok = (FAKE, 4096, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE)
+    # missing state pointer array
+    assert _status(gdn.gdn_decode_batched, d, *ok, None, 4, 0)[0] == _lib.GDN_ERR_NULL
+    # missing o
+    assert _status(gdn.gdn_decode_batched, d, FAKE, 4096, FAKE, 4096, FAKE, 4096, FAKE, FAKE, None, FAKE, 4,
+                   0)[0] == _lib.GDN_ERR_NULL
+    # misaligned q
+    assert _status(gdn.gdn_decode_batched, d, FAKE + 4, 4096, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, 4,
+                   0)[0] == _lib.GDN_ERR_ALIGN
+    # stride not a multiple of 4 elements
+    assert _status(gdn.gdn_decode_batched, d, FAKE, 4098, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, 4,
+                   0)[0] == _lib.GDN_ERR_ALIGN
+    # stride below the row width
+    assert _status(gdn.gdn_decode_batched, d, FAKE, 1024, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, 4,
+                   0)[0] == _lib.GDN_ERR_SHAPE
+    assert _status(gdn.gdn_decode_batched, d, *ok, FAKE, -1, 0)[0] == _lib.GDN_ERR_SHAPE
+    assert _status(gdn.gdn_decode_batched, d, *ok, FAKE, 70000, 0)[0] == _lib.GDN_ERR_SHAPE
+    # m = 0 is a no-op that launches nothing
+    gdn.gdn_decode_batched(d, *ok, FAKE, 0, 0)
+
+
+def test_conv_argument_checks():
+    d = dims()
+    C = 8192
+    # decode mode needs total_tokens == n
+    assert _status(gdn.gdn_conv_update, d, FAKE, C, FAKE, C, FAKE, None, None, FAKE, 4, 5, 0)[0] == _lib.GDN_ERR_SHAPE
+    # missing conv state pointers
+    assert _status(gdn.gdn_conv_update, d, FAKE, C, FAKE, C, FAKE, None, None, None, 4, 4, 0)[0] == _lib.GDN_ERR_NULL
+    # x row stride below C
+    assert _status(gdn.gdn_conv_update, d, FAKE, C - 8, FAKE, C, FAKE, None, FAKE, FAKE, 2, 9, 0)[0] == \
+        _lib.GDN_ERR_SHAPE
+    # misaligned bias
+    assert _status(gdn.gdn_conv_update, d, FAKE, C, FAKE, C, FAKE, FAKE + 2, FAKE, FAKE, 2, 9, 0)[0] == \
+        _lib.GDN_ERR_ALIGN
+    # bf16 x row stride of 4 elements = 8 bytes breaks the 16-byte rule
+    d1 = dims(num_k_heads=1, num_v_heads=1, head_dim=32)
+    assert _status(gdn.gdn_conv_update, d1, FAKE, 100, FAKE, 100, FAKE, None, FAKE, FAKE, 1, 2, 0)[0] == \
+        _lib.GDN_ERR_ALIGN
+    # tokens without sequences
+    assert _status(gdn.gdn_conv_update, d, FAKE, C, FAKE, C, FAKE, None, FAKE, FAKE, 0, 3, 0)[0] == _lib.GDN_ERR_SHAPE
+    # nothing at all is a no-op
+    gdn.gdn_conv_update(d, None, 0, None, 0, None, None, None, None, 0, 0, 0)
+
+
+def test_prefill_workspace_and_checks():
+    d = dims()
+    need = gdn.gdn_prefill_workspace_size(d, 8, 15717)
+    assert need > 0
+    # grows with tokens and sequences
+    assert gdn.gdn_prefill_workspace_size(d, 8, 30000) > need
+    assert gdn.gdn_prefill_workspace_size(d, 100, 15717) > need
+    qkv = (FAKE, 8192, FAKE, 8192, FAKE, 8192, FAKE, FAKE, FAKE)
+    st, msg = _status(gdn.gdn_prefill_chunked, d, *qkv, FAKE, 8, 15717, FAKE, FAKE, need - 1, 0)
+    assert st == _lib.GDN_ERR_WORKSPACE and str(need) in msg
+    assert _status(gdn.gdn_prefill_chunked, d, *qkv, FAKE, 8, 15717, FAKE, None, need, 0)[0] == \
+        _lib.GDN_ERR_WORKSPACE
+    assert _status(gdn.gdn_prefill_chunked, d, *qkv, FAKE, 8, 15717, FAKE, FAKE + 16, need, 0)[0] == \
+        _lib.GDN_ERR_ALIGN
+    assert _status(gdn.gdn_prefill_chunked, d, *qkv, None, 8, 15717, FAKE, FAKE, need, 0)[0] == _lib.GDN_ERR_NULL
+    assert _status(gdn.gdn_prefill_chunked, d, *qkv, FAKE, 0, 5, FAKE, FAKE, need, 0)[0] == _lib.GDN_ERR_SHAPE
+    # no sequences: no-op
+    gdn.gdn_prefill_chunked(d, *qkv, FAKE, 0, 0, FAKE, None, 0, 0)
+
+
+def test_slot_pointer_checks():
+    assert _status(gdn.gdn_slot_pointers, FAKE + 8, 256, 4, FAKE, 4, FAKE)[0] == _lib.GDN_ERR_ALIGN
+    assert _status(gdn.gdn_slot_pointers, FAKE, 1928, 4, FAKE, 4, FAKE)[0] == _lib.GDN_ERR_ALIGN
+    assert _status(gdn.gdn_slot_pointers, FAKE, 0, 4, FAKE, 4, FAKE)[0] == _lib.GDN_ERR_SHAPE
+    assert _status(gdn.gdn_slot_pointers, FAKE, 256, 4, None, 4, FAKE)[0] == _lib.GDN_ERR_NULL
+    gdn.gdn_slot_pointers(FAKE, 256, 4, FAKE, 0, FAKE)
