@@ -1,20 +1,595 @@
-// Chunked prefill of the gated delta rule (placeholder until the MFMA kernels land).
+// Chunked prefill of the gated delta rule over packed ragged sequences, gfx950.
+//
+// ("System Design" (project_6), "GDN Kernel Dispatch Detail": the prefill branch hands
+// (q, k, v, g, beta, state) to a chunked gated-delta-rule kernel and updates the
+// temporal state; aprender #5279, "Phase plan", P6: ragged lengths must give the
+// per-slot result.)
+//
+// Per sequence and v-head the rule S_t = exp(g_t) S_{t-1}(I - beta_t k_t k_t^T) +
+// beta_t v_t k_t^T, o_t = S_t q_t is rewritten over chunks of C tokens (chunks start at
+// each sequence's own first token). With gam = inclusive cumsum of g in the chunk and
+// S0 the state on entry:
+//   A[t,s] = beta_t e^{gam_t - gam_s} (k_t . k_s)  (s < t),   T = (I + A)^-1
+//   P[t,s] = e^{gam_t - gam_s} (q_t . k_s)          (s <= t)
+//   U = T (diag(beta) V - diag(beta e^gam) K S0^T)
+//   O = diag(e^gam) Q S0^T + P U
+//   S = e^{gam_n} S0 + U^T diag(e^{gam_n - gam}) K
+// Every decay factor is exp of gam_t - gam_s with t >= s (or gam alone, <= 0): nothing
+// can overflow, so no clamp is needed.
+//
+// Three launches, in stream order:
+//   chunk_table_kernel : cu_seqlens -> chunk table (sequence, start, length), per-sequence
+//                        chunk offsets and a longest-first sequence order, on the device.
+//   intra_chunk_kernel : one workgroup per (chunk, k-head), all chunks in parallel:
+//                        normalised K, Q in LDS; K K^T and Q K^T on MFMA; for each v-head
+//                        sharing the k-head: the decay mask, A, T by blocked (16x16)
+//                        forward substitution, and P. T and P go to the workspace.
+//   inter_chunk_kernel : one workgroup per (sequence, v-head, 16 state rows), walking the
+//                        chunks of its sequence in order with its 16 x d slice of the
+//                        state resident in registers/LDS; the contractions K S^T, Q S^T,
+//                        T R, P U and U^T K run on MFMA. The 16-row slices of one head are
+//                        mapped to one XCD so they share K, Q, T and P through its L2.
+
 #include "launch.h"
+#include "mma.h"
 
 namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kDVB = 16;  // state rows per inter-chunk workgroup
+constexpr int kMetaThreads = 1024;
+constexpr int kLptMaxSeqs = 256;  // longest-first ordering only up to this many sequences
+
+struct Workspace {
+  int* n_chunks;
+  int4* table;  // (sequence, first token, length, index in sequence)
+  int* chunk_off;
+  int* order;
+  float* T;  // [chunk][Hv][C][C]
+  float* P;  // [chunk][Hv][C][C]
+};
+
+inline size_t up256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+inline size_t max_chunks_of(int chunk, int num_seqs, int total_tokens) {
+  return static_cast<size_t>(total_tokens) / chunk + static_cast<size_t>(num_seqs);
+}
+
+Workspace carve(void* base, int hv, int chunk, int num_seqs, int total_tokens) {
+  char* p = static_cast<char*>(base);
+  const size_t mc = max_chunks_of(chunk, num_seqs, total_tokens);
+  const size_t mat = up256(mc * hv * chunk * chunk * sizeof(float));
+  Workspace w;
+  w.n_chunks = reinterpret_cast<int*>(p);
+  p += 256;
+  w.table = reinterpret_cast<int4*>(p);
+  p += up256(mc * sizeof(int4));
+  w.chunk_off = reinterpret_cast<int*>(p);
+  p += up256((static_cast<size_t>(num_seqs) + 1) * sizeof(int));
+  w.order = reinterpret_cast<int*>(p);
+  p += up256(static_cast<size_t>(num_seqs) * sizeof(int) + 4);
+  w.T = reinterpret_cast<float*>(p);
+  p += mat;
+  w.P = reinterpret_cast<float*>(p);
+  return w;
+}
+
+// ------------------------------------------------------------------------ chunk table
+__global__ __launch_bounds__(kMetaThreads) void chunk_table_kernel(const int* __restrict__ cu, int N, int C,
+                                                                  Workspace w) {
+  __shared__ int scan[kMetaThreads];
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int base = 0; base < N; base += kMetaThreads) {
+    const int s = base + tid;
+    const int nc = s < N ? (cu[s + 1] - cu[s] + C - 1) / C : 0;
+    scan[tid] = nc;
+    __syncthreads();
+    for (int off = 1; off < kMetaThreads; off <<= 1) {
+      const int add = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    if (s < N) w.chunk_off[s] = carry + scan[tid] - nc;
+    carry += scan[kMetaThreads - 1];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    w.chunk_off[N] = carry;
+    *w.n_chunks = carry;
+  }
+  for (int s = tid; s < N; s += kMetaThreads) {
+    const int start = cu[s];
+    const int len = cu[s + 1] - start;
+    const int off = w.chunk_off[s];  // written by this thread above
+    for (int c = 0; c * C < len; ++c) w.table[off + c] = make_int4(s, start + c * C, min(C, len - c * C), c);
+  }
+  // longest sequence first, so its long chain of chunks starts with the first wave of
+  // workgroups (ties by index)
+  for (int s = tid; s < N; s += kMetaThreads) {
+    if (N <= kLptMaxSeqs) {
+      const int ls = cu[s + 1] - cu[s];
+      int rank = 0;
+      for (int q = 0; q < N; ++q) {
+        const int lq = cu[q + 1] - cu[q];
+        rank += (lq > ls) || (lq == ls && q < s);
+      }
+      w.order[rank] = s;
+    } else {
+      w.order[s] = s;
+    }
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (fixed order).
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+// KPL contiguous values at row p, column k, zero where k >= limit (k is a multiple of 4).
+template <int KPL>
+__device__ __forceinline__ void load_k_guard(const float* p, int k, int limit, float* out) {
+  if (k < limit) {
+    load_k<KPL>(p + k, out);
+  } else {
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) out[e] = 0.f;
+  }
+}
+
+// ------------------------------------------------------------------------ intra-chunk
+template <int D, int C>
+struct IntraLayout {
+  static constexpr int KP = D + 4;  // padded row of K^/Q^
+  static constexpr int CP = C + 4;  // padded row of C x C matrices
+  static constexpr int R1_A = 2 * C * KP;
+  static constexpr int R1_B = 2 * C * CP + 3 * 16 * 20;
+  static constexpr int R1 = R1_A > R1_B ? R1_A : R1_B;  // K^, Q^  alias  A, T, W
+  static constexpr int OFF_G = R1;
+  static constexpr int OFF_QK = OFF_G + C * CP;
+  static constexpr int OFF_GAM = OFF_QK + C * CP;
+  static constexpr int OFF_BET = OFF_GAM + C;
+  static constexpr int TOTAL = OFF_BET + C;
+};
+
+template <int POL, int D, int C>
+__global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Workspace w) {
+  using M = Mma<POL>;
+  using Lo = IntraLayout<D, C>;
+  constexpr int NB = C / 16;
+  constexpr int KP = Lo::KP, CP = Lo::CP;
+  __shared__ __attribute__((aligned(16))) float smem[Lo::TOTAL];
+  float(*Kh)[KP] = reinterpret_cast<float(*)[KP]>(smem);
+  float(*Qh)[KP] = reinterpret_cast<float(*)[KP]>(smem + C * KP);
+  float(*Am)[CP] = reinterpret_cast<float(*)[CP]>(smem);
+  float(*Tm)[CP] = reinterpret_cast<float(*)[CP]>(smem + C * CP);
+  float(*Wm)[16][20] = reinterpret_cast<float(*)[16][20]>(smem + 2 * C * CP);
+  float(*Gm)[CP] = reinterpret_cast<float(*)[CP]>(smem + Lo::OFF_G);
+  float(*QKm)[CP] = reinterpret_cast<float(*)[CP]>(smem + Lo::OFF_QK);
+  float* gam = smem + Lo::OFF_GAM;
+  float* bet = smem + Lo::OFF_BET;
+
+  const int chunk = blockIdx.x;
+  if (chunk >= *w.n_chunks) return;
+  const int h = blockIdx.y;
+  const int4 ent = w.table[chunk];
+  const int t0 = ent.y, n = ent.z;
+  const RecurArgs& r = a.r;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int group = r.hv / r.hk;
+
+  // 1. normalised K and Q rows of the chunk into LDS; rows >= n are zero
+  constexpr int TPR = 4;
+  constexpr int EPT = D / TPR;
+  for (int row = tid / TPR; row < C; row += kThreads / TPR) {
+    const int part = tid % TPR;
+    float kv[EPT], qv[EPT];
+    const bool live = row < n;
+    if (live) {
+      load_k<EPT>(r.k + static_cast<int64_t>(t0 + row) * r.k_stride + h * D + part * EPT, kv);
+      load_k<EPT>(r.q + static_cast<int64_t>(t0 + row) * r.q_stride + h * D + part * EPT, qv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) kv[e] = qv[e] = 0.f;
+    }
+    float kk = 0.f, qq = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      kk = fmaf(kv[e], kv[e], kk);
+      qq = fmaf(qv[e], qv[e], qq);
+    }
+    kk = group_sum<4>(kk);
+    qq = group_sum<4>(qq);
+    const float rk = live ? 1.0f / sqrtf(kk + r.eps) : 0.f;
+    const float rq = live ? r.scale / sqrtf(qq + r.eps) : 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4) {
+      *reinterpret_cast<float4*>(&Kh[row][part * EPT + e]) =
+          make_float4(kv[e] * rk, kv[e + 1] * rk, kv[e + 2] * rk, kv[e + 3] * rk);
+      *reinterpret_cast<float4*>(&Qh[row][part * EPT + e]) =
+          make_float4(qv[e] * rq, qv[e + 1] * rq, qv[e + 2] * rq, qv[e + 3] * rq);
+    }
+  }
+  __syncthreads();
+
+  // 2. G = K^ K^T and QK = Q^ K^T on the lower-triangular 16x16 tiles
+  {
+    constexpr int NT = NB * (NB + 1) / 2;
+    const int l16 = lane & 15;
+    const int kl = M::KPL * (lane >> 4);
+    for (int item = wave; item < 2 * NT; item += kWaves) {
+      const bool isq = item >= NT;
+      const int it = isq ? item - NT : item;
+      int ti = 0;
+      while ((ti + 1) * (ti + 2) / 2 <= it) ++ti;
+      const int tj = it - ti * (ti + 1) / 2;
+      const float(*Aop)[KP] = isq ? Qh : Kh;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < D / M::KSTEP; ++v) {
+        float av[M::KPL], bv[M::KPL];
+        load_k<M::KPL>(&Aop[ti * 16 + l16][kl + v * M::KSTEP], av);
+        load_k<M::KPL>(&Kh[tj * 16 + l16][kl + v * M::KSTEP], bv);
+        M::step(acc, av, bv);
+      }
+      float(*Out)[CP] = isq ? QKm : Gm;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) Out[ti * 16 + 4 * (lane >> 4) + rr][tj * 16 + l16] = acc[rr];
+    }
+  }
+  __syncthreads();
+
+  // 3. per v-head of this k-head's group: decay mask, A, T = (I + A)^-1, P
+  for (int jj = 0; jj < group; ++jj) {
+    const int j = h * group + jj;
+    if (wave == 0) {
+      float gv = 0.f, bv = 0.f;
+      if (lane < n) {
+        gv = r.g[static_cast<int64_t>(t0 + lane) * r.hv + j];
+        bv = r.beta[static_cast<int64_t>(t0 + lane) * r.hv + j];
+      }
+      gv = wave_inclusive_scan(gv);
+      if (lane < C) {
+        gam[lane] = gv;
+        bet[lane] = bv;
+      }
+    }
+    __syncthreads();
+
+    float* Pg = w.P + (static_cast<int64_t>(chunk) * r.hv + j) * C * C;
+    for (int e = tid; e < C * C; e += kThreads) {
+      const int t = e / C, s = e % C;
+      float av = 0.f, pv = 0.f;
+      if (s <= t) {
+        const float dec = expf(gam[t] - gam[s]);
+        pv = dec * QKm[t][s];
+        if (s < t) av = bet[t] * dec * Gm[t][s];
+      }
+      Am[t][s] = av;
+      Pg[e] = pv;
+    }
+    __syncthreads();
+
+    // diagonal 16x16 blocks by forward substitution: lane c of wave b owns column c
+    for (int b = wave; b < NB; b += kWaves) {
+      if (lane < 16) {
+        const int c = lane;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float acc = (i == c) ? 1.f : 0.f;
+#pragma unroll
+          for (int k = 0; k < i; ++k) acc = fmaf(-Am[b * 16 + i][b * 16 + k], x[k], acc);
+          x[i] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Tm[b * 16 + i][b * 16 + c] = x[i];
+      }
+    }
+    __syncthreads();
+
+    // off-diagonal blocks by distance from the diagonal: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+    for (int dd = 1; dd < NB; ++dd) {
+      const int nblk = NB - dd;
+      for (int e = tid; e < nblk * 256; e += kThreads) {
+        const int jb = e / 256, rr = (e / 16) % 16, cc = e % 16;
+        const int ib = jb + dd;
+        float acc = 0.f;
+        for (int kb = jb; kb < ib; ++kb)
+#pragma unroll
+          for (int m = 0; m < 16; ++m) acc = fmaf(Am[ib * 16 + rr][kb * 16 + m], Tm[kb * 16 + m][jb * 16 + cc], acc);
+        Wm[jb][rr][cc] = acc;
+      }
+      __syncthreads();
+      for (int e = tid; e < nblk * 256; e += kThreads) {
+        const int jb = e / 256, rr = (e / 16) % 16, cc = e % 16;
+        const int ib = jb + dd;
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) acc = fmaf(Tm[ib * 16 + rr][ib * 16 + m], Wm[jb][m][cc], acc);
+        Tm[ib * 16 + rr][jb * 16 + cc] = -acc;
+      }
+      __syncthreads();
+    }
+
+    float* Tg = w.T + (static_cast<int64_t>(chunk) * r.hv + j) * C * C;
+    for (int e = tid; e < C * C; e += kThreads) {
+      const int t = e / C, s = e % C;
+      Tg[e] = (s <= t) ? Tm[t][s] : 0.f;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------ inter-chunk
+template <int D, int C>
+struct InterLayout {
+  static constexpr int SP = D + 4;
+  static constexpr int CP = C + 4;
+};
+
+template <int POL, int D, int C>
+__global__ __launch_bounds__(kThreads) void inter_chunk_kernel(PrefillArgs a, Workspace w) {
+  using M = Mma<POL>;
+  constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
+  constexpr int NBLK = D / kDVB;  // state-row blocks per head
+  constexpr int NT = C / 16;      // token tiles per chunk
+  constexpr int ST = D / 16;      // 16-column tiles of the state slice
+  constexpr int STW = (ST + kWaves - 1) / kWaves;
+  constexpr int NV = D / KSTEP;
+  constexpr int SP = InterLayout<D, C>::SP, CP = InterLayout<D, C>::CP;
+  __shared__ __attribute__((aligned(16))) float Sl[kDVB][SP];
+  __shared__ __attribute__((aligned(16))) float Rt[kDVB][CP];
+  __shared__ __attribute__((aligned(16))) float Ut[kDVB][CP];
+  __shared__ __attribute__((aligned(16))) float Us[kDVB][CP];
+  __shared__ __attribute__((aligned(16))) float Kt[D][CP];
+
+  const RecurArgs& r = a.r;
+  const int per_seq = NBLK * r.hv;
+  const int L = blockIdx.x;
+  const int zi = L / per_seq;
+  const int rem = L % per_seq;
+  // workgroups are dealt round-robin to the 8 XCDs: give the slices of one head
+  // consecutive virtual ids on one XCD so they share that XCD's L2
+  const int vid = (per_seq % 8 == 0) ? (rem % 8) * (per_seq / 8) + rem / 8 : rem;
+  const int j = vid / NBLK, blk = vid % NBLK;
+  const int s = w.order[zi];
+  const int start = a.cu_seqlens[s];
+  const int len = a.cu_seqlens[s + 1] - start;
+  if (len <= 0) return;
+  const uint64_t sptr = r.state_ptrs[s];
+  if (sptr == 0) return;
+  const int h = j / (r.hv / r.hk);
+  float* Sg = reinterpret_cast<float*>(sptr) + (static_cast<int64_t>(j) * D + blk * kDVB) * D;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int kl = KPL * lg;
+
+  f32x4 sacc[STW];
+#pragma unroll
+  for (int u = 0; u < STW; ++u) {
+    const int tile = wave * STW + u;
+    if (tile < ST) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float v = Sg[(4 * lg + rr) * D + tile * 16 + l16];
+        sacc[u][rr] = v;
+        Sl[4 * lg + rr][tile * 16 + l16] = v;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int nch = (len + C - 1) / C;
+  const int cbase = w.chunk_off[s];
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = start + c * C;
+    const int n = min(C, len - c * C);
+    const int64_t gch = static_cast<int64_t>(cbase + c) * r.hv + j;
+    const float* Tg = w.T + gch * C * C;
+    const float* Pg = w.P + gch * C * C;
+
+    float gv = 0.f, bv = 0.f;
+    if (lane < n) {
+      gv = r.g[static_cast<int64_t>(t0 + lane) * r.hv + j];
+      bv = r.beta[static_cast<int64_t>(t0 + lane) * r.hv + j];
+    }
+    gv = wave_inclusive_scan(gv);
+    const float gam_n = __shfl(gv, n - 1, 64);
+
+    const bool active = wave < NT;
+    f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+    float gam_t[4];
+    if (active) {
+      const int trow = wave * 16 + l16;
+      float kf[NV][KPL], qf[NV][KPL];
+      float kk = 0.f, qq = 0.f;
+      if (trow < n) {
+        const float* kp = r.k + static_cast<int64_t>(t0 + trow) * r.k_stride + h * D;
+        const float* qp = r.q + static_cast<int64_t>(t0 + trow) * r.q_stride + h * D;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          load_k<KPL>(kp + kl + v * KSTEP, kf[v]);
+          load_k<KPL>(qp + kl + v * KSTEP, qf[v]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+          for (int e = 0; e < KPL; ++e) kf[v][e] = qf[v][e] = 0.f;
+      }
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+          kk = fmaf(kf[v][e], kf[v][e], kk);
+          qq = fmaf(qf[v][e], qf[v][e], qq);
+        }
+      kk += __shfl_xor(kk, 16, 64);
+      kk += __shfl_xor(kk, 32, 64);
+      qq += __shfl_xor(qq, 16, 64);
+      qq += __shfl_xor(qq, 32, 64);
+      const float rk = trow < n ? 1.0f / sqrtf(kk + r.eps) : 0.f;
+      const float rq = trow < n ? r.scale / sqrtf(qq + r.eps) : 0.f;
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+          kf[v][e] *= rk;
+          qf[v][e] *= rq;
+          Kt[kl + v * KSTEP + e][trow] = kf[v][e];
+        }
+      // X = K^ S^T, Y = Q^ S^T for this wave's 16 tokens x the block's 16 state rows
+      f32x4 xacc = {0.f, 0.f, 0.f, 0.f}, yacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        float sb[KPL];
+        load_k<KPL>(&Sl[l16][kl + v * KSTEP], sb);
+        M::step(xacc, kf[v], sb);
+        M::step(yacc, qf[v], sb);
+      }
+      // R = beta V - beta e^gam X (stored transposed), O starts as e^gam Y
+      float rv[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int t = wave * 16 + 4 * lg + rr;
+        const float gt = __shfl(gv, t, 64);
+        const float bt = __shfl(bv, t, 64);
+        const float eg = expf(gt);
+        const float vt = t < n ? r.v[static_cast<int64_t>(t0 + t) * r.v_stride + j * D + blk * kDVB + l16] : 0.f;
+        rv[rr] = bt * (vt - eg * xacc[rr]);
+        oacc[rr] = eg * yacc[rr];
+        gam_t[rr] = gt;
+      }
+      *reinterpret_cast<float4*>(&Rt[l16][wave * 16 + 4 * lg]) = make_float4(rv[0], rv[1], rv[2], rv[3]);
+    }
+    __syncthreads();
+
+    // U = T R (T lower triangular: only token columns below this tile's end)
+    if (active) {
+      const int trow = wave * 16 + l16;
+      f32x4 uacc = {0.f, 0.f, 0.f, 0.f};
+      const int kend = wave * 16 + 16;
+      for (int k0 = 0; k0 < kend; k0 += KSTEP) {
+        float ta[KPL], rb[KPL];
+        load_k_guard<KPL>(Tg + static_cast<int64_t>(trow) * C, k0 + kl, C, ta);
+        load_k_guard<KPL>(&Rt[l16][0], k0 + kl, C, rb);
+        M::step(uacc, ta, rb);
+      }
+      float us[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) us[rr] = expf(gam_n - gam_t[rr]) * uacc[rr];
+      *reinterpret_cast<float4*>(&Ut[l16][wave * 16 + 4 * lg]) = make_float4(uacc[0], uacc[1], uacc[2], uacc[3]);
+      *reinterpret_cast<float4*>(&Us[l16][wave * 16 + 4 * lg]) = make_float4(us[0], us[1], us[2], us[3]);
+    }
+    __syncthreads();
+
+    // O = e^gam Y + P U
+    if (active) {
+      const int trow = wave * 16 + l16;
+      const int kend = wave * 16 + 16;
+      for (int k0 = 0; k0 < kend; k0 += KSTEP) {
+        float pa[KPL], ub[KPL];
+        load_k_guard<KPL>(Pg + static_cast<int64_t>(trow) * C, k0 + kl, C, pa);
+        load_k_guard<KPL>(&Ut[l16][0], k0 + kl, C, ub);
+        M::step(oacc, pa, ub);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int t = wave * 16 + 4 * lg + rr;
+        if (t < n) r.o[(static_cast<int64_t>(t0 + t) * r.hv + j) * D + blk * kDVB + l16] = oacc[rr];
+      }
+    }
+
+    // S <- e^{gam_n} S + Us^T K^   (this wave's 16-column tiles of the slice)
+    const float egn = expf(gam_n);
+#pragma unroll
+    for (int u = 0; u < STW; ++u) {
+      const int tile = wave * STW + u;
+      if (tile < ST) {
+        f32x4 acc;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[rr] = sacc[u][rr] * egn;
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += KSTEP) {
+          float ua[KPL], kb[KPL];
+          load_k_guard<KPL>(&Us[l16][0], k0 + kl, C, ua);
+          load_k_guard<KPL>(&Kt[tile * 16 + l16][0], k0 + kl, C, kb);
+          M::step(acc, ua, kb);
+        }
+        sacc[u] = acc;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) Sl[4 * lg + rr][tile * 16 + l16] = acc[rr];
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int u = 0; u < STW; ++u) {
+    const int tile = wave * STW + u;
+    if (tile < ST) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) Sg[(4 * lg + rr) * D + tile * 16 + l16] = sacc[u][rr];
+    }
+  }
+}
+
+template <int POL, int D, int C>
+hipError_t launch_chunked(const PrefillArgs& a, const Workspace& w, hipStream_t s) {
+  const size_t mc = max_chunks_of(C, a.num_seqs, a.total_tokens);
+  intra_chunk_kernel<POL, D, C><<<dim3(static_cast<unsigned>(mc), a.r.hk), kThreads, 0, s>>>(a, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned blocks = static_cast<unsigned>((D / kDVB) * a.r.hv * a.num_seqs);
+  inter_chunk_kernel<POL, D, C><<<blocks, kThreads, 0, s>>>(a, w);
+  return hipGetLastError();
+}
+
+template <int POL, int D>
+hipError_t by_chunk(const PrefillArgs& a, const Workspace& w, hipStream_t s) {
+  switch (a.chunk) {
+    case 16: return launch_chunked<POL, D, 16>(a, w, s);
+    case 32: return launch_chunked<POL, D, 32>(a, w, s);
+    default: return launch_chunked<POL, D, 64>(a, w, s);
+  }
+}
+
+template <int POL>
+hipError_t by_dim(const PrefillArgs& a, const Workspace& w, hipStream_t s) {
+  switch (a.r.d) {
+    case 32: return by_chunk<POL, 32>(a, w, s);
+    case 64: return by_chunk<POL, 64>(a, w, s);
+    default: return by_chunk<POL, 128>(a, w, s);
+  }
+}
+
+}  // namespace
 
 size_t prefill_workspace_bytes(int32_t hv, int32_t d, int32_t chunk, int32_t num_seqs, int32_t total_tokens) {
   (void)d;
-  const size_t max_chunks = static_cast<size_t>(total_tokens) / chunk + static_cast<size_t>(num_seqs);
-  auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
-  return up(max_chunks * 16) + up((static_cast<size_t>(num_seqs) + 1) * 4) + 256 +
-         2 * up(max_chunks * hv * chunk * chunk * 4);
+  const size_t mc = max_chunks_of(chunk, num_seqs, total_tokens);
+  return 256 + up256(mc * sizeof(int4)) + up256((static_cast<size_t>(num_seqs) + 1) * sizeof(int)) +
+         up256(static_cast<size_t>(num_seqs) * sizeof(int) + 4) +
+         2 * up256(mc * static_cast<size_t>(hv) * chunk * chunk * sizeof(float));
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  (void)a;
-  (void)s;
-  return hipErrorNotSupported;
+  if (a.num_seqs == 0 || a.total_tokens == 0) return hipSuccess;
+  const Workspace w = carve(a.workspace, a.r.hv, a.chunk, a.num_seqs, a.total_tokens);
+  chunk_table_kernel<<<1, kMetaThreads, 0, s>>>(a.cu_seqlens, a.num_seqs, a.chunk, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return a.mma == kPolFP32 ? by_dim<kPolFP32>(a, w, s) : by_dim<kPolBF16X3>(a, w, s);
 }
 
 }  // namespace gdn
