@@ -134,7 +134,8 @@ gdn_status gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, in
   if (gdn_status st = check_dims(dims, fn)) return st;
   if (!bytes) return fail(GDN_ERR_NULL, "%s: bytes is NULL", fn);
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_SHAPE, "%s: negative count", fn);
-  *bytes = gdn::prefill_workspace_bytes(dims->num_v_heads, dims->head_dim, dims->chunk_size, num_seqs, total_tokens);
+  *bytes = gdn::prefill_workspace_bytes(dims->num_k_heads, dims->num_v_heads, dims->head_dim, dims->chunk_size, num_seqs,
+                                      total_tokens);
   return GDN_OK;
 }
 
@@ -156,7 +157,8 @@ gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_s
       return st;
   }
   const size_t need =
-      gdn::prefill_workspace_bytes(dims->num_v_heads, dims->head_dim, dims->chunk_size, num_seqs, total_tokens);
+      gdn::prefill_workspace_bytes(dims->num_k_heads, dims->num_v_heads, dims->head_dim, dims->chunk_size, num_seqs,
+                                      total_tokens);
   if (!workspace || workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, need, workspace_bytes,
                 workspace ? "" : " (NULL)");

@@ -58,7 +58,8 @@ struct PrefillArgs {
   void* workspace;
 };
 
-size_t prefill_workspace_bytes(int32_t hv, int32_t d, int32_t chunk, int32_t num_seqs, int32_t total_tokens);
+size_t prefill_workspace_bytes(int32_t hk, int32_t hv, int32_t d, int32_t chunk, int32_t num_seqs,
+                               int32_t total_tokens);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 hipError_t launch_slot_pointers(uint64_t base, int64_t slot_bytes, int32_t pool_slots, const int32_t* idx,

@@ -30,9 +30,22 @@ template <>
 struct Mma<kPolFP32> {
   static constexpr int KPL = 4;
   static constexpr int KSTEP = 16;
-  __device__ __forceinline__ static void step(f32x4& acc, const float* a, const float* b) {
+  // an operand fragment: the lane's KPL values of one step
+  struct Frag {
+    float v[4];
+  };
+  __device__ __forceinline__ static Frag frag(const float* x) {
+    Frag f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+    for (int e = 0; e < 4; ++e) f.v[e] = x[e];
+    return f;
+  }
+  __device__ __forceinline__ static void mma(f32x4& acc, const Frag& a, const Frag& b) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+  }
+  __device__ __forceinline__ static void step(f32x4& acc, const float* a, const float* b) {
+    mma(acc, frag(a), frag(b));
   }
 };
 
@@ -48,13 +61,101 @@ struct Mma<kPolBF16X3> {
       lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
     }
   }
+  struct Frag {
+    bf16x8 hi, lo;
+  };
+  __device__ __forceinline__ static Frag frag(const float* x) {
+    Frag f;
+    split(x, f.hi, f.lo);
+    return f;
+  }
+  __device__ __forceinline__ static void mma(f32x4& acc, const Frag& a, const Frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+  }
   __device__ __forceinline__ static void step(f32x4& acc, const float* a, const float* b) {
-    bf16x8 ah, al, bh, bl;
-    split(a, ah, al);
-    split(b, bh, bl);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+    mma(acc, frag(a), frag(b));
+  }
+};
+
+// Operand matrices stored "pre-split": for BF16X3 an R x Cc matrix is two bf16 planes
+// (hi, then lo), for FP32 one fp32 plane; both take R*Cc*4 bytes. A fragment is the
+// lane's KPL values starting at (row, col); col is a multiple of KPL.
+template <int POL>
+struct Split;
+
+template <>
+struct Split<kPolFP32> {
+  using M = Mma<kPolFP32>;
+  __device__ __forceinline__ static M::Frag load(const void* base, int rows, int cols, int row, int col) {
+    (void)rows;
+    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + (int64_t)row * cols + col);
+    M::Frag f;
+    f.v[0] = v.x; f.v[1] = v.y; f.v[2] = v.z; f.v[3] = v.w;
+    return f;
+  }
+  __device__ __forceinline__ static M::Frag zero() {
+    M::Frag f;
+    f.v[0] = f.v[1] = f.v[2] = f.v[3] = 0.f;
+    return f;
+  }
+  // store n (<= 8, multiple of 4) consecutive values of one row
+  __device__ __forceinline__ static void store(void* base, int rows, int cols, int row, int col, const float* x, int n) {
+    (void)rows;
+    float* p = static_cast<float*>(base) + (int64_t)row * cols + col;
+    for (int i = 0; i < n; i += 4) *reinterpret_cast<float4*>(p + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+  }
+  __device__ __forceinline__ static void store1(void* base, int rows, int cols, int row, int col, float x) {
+    (void)rows;
+    static_cast<float*>(base)[(int64_t)row * cols + col] = x;
+  }
+};
+
+template <>
+struct Split<kPolBF16X3> {
+  using M = Mma<kPolBF16X3>;
+  __device__ __forceinline__ static M::Frag load(const void* base, int rows, int cols, int row, int col) {
+    const __bf16* hi = static_cast<const __bf16*>(base) + (int64_t)row * cols + col;
+    const __bf16* lo = hi + (int64_t)rows * cols;
+    M::Frag f;
+    f.hi = *reinterpret_cast<const bf16x8*>(hi);
+    f.lo = *reinterpret_cast<const bf16x8*>(lo);
+    return f;
+  }
+  __device__ __forceinline__ static M::Frag zero() {
+    M::Frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.hi[e] = f.lo[e] = static_cast<__bf16>(0.f);
+    return f;
+  }
+  // store n (4 or 8) consecutive values of one row (8 or 16 bytes per plane)
+  __device__ __forceinline__ static void store(void* base, int rows, int cols, int row, int col, const float* x, int n) {
+    __bf16* hi = static_cast<__bf16*>(base) + (int64_t)row * cols + col;
+    __bf16* lo = hi + (int64_t)rows * cols;
+    if (n == 8) {
+      bf16x8 h, l;
+      M::split(x, h, l);
+      *reinterpret_cast<bf16x8*>(hi) = h;
+      *reinterpret_cast<bf16x8*>(lo) = l;
+    } else {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 h, l;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 t = static_cast<__bf16>(x[e]);
+        h[e] = t;
+        l[e] = static_cast<__bf16>(x[e] - static_cast<float>(t));
+      }
+      *reinterpret_cast<bf16x4*>(hi) = h;
+      *reinterpret_cast<bf16x4*>(lo) = l;
+    }
+  }
+  __device__ __forceinline__ static void store1(void* base, int rows, int cols, int row, int col, float x) {
+    __bf16* hi = static_cast<__bf16*>(base) + (int64_t)row * cols + col;
+    const __bf16 t = static_cast<__bf16>(x);
+    hi[0] = t;
+    hi[(int64_t)rows * cols] = static_cast<__bf16>(x - static_cast<float>(t));
   }
 };
 

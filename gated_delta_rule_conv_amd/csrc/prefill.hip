@@ -36,19 +36,25 @@
 namespace gdn {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;      // intra-chunk workgroup
 constexpr int kWaves = 4;
-constexpr int kDVB = 16;  // state rows per inter-chunk workgroup
+constexpr int kInterThreads = 512; // inter-chunk workgroup: 8 waves
+constexpr int kDVB = 16;           // state rows per inter-chunk workgroup
 constexpr int kMetaThreads = 1024;
-constexpr int kLptMaxSeqs = 256;  // longest-first ordering only up to this many sequences
+constexpr int kLptMaxSeqs = 256;   // longest-first ordering only up to this many sequences
 
+// Per-chunk operands the intra-chunk kernel hands to the inter-chunk kernel, stored
+// pre-split for the MFMA policy (see Split<> in mma.h):
+//   per (chunk, k-head): K^ [C][D], Q^ [C][D] (q already scaled), K^T [D][C]
+//   per (chunk, v-head): T [C][C], P [C][C], gam [C] (fp32, padded with gam_{n-1}),
+//                        beta [C] (fp32, padded with 0)
 struct Workspace {
   int* n_chunks;
   int4* table;  // (sequence, first token, length, index in sequence)
   int* chunk_off;
   int* order;
-  float* T;  // [chunk][Hv][C][C]
-  float* P;  // [chunk][Hv][C][C]
+  char* kq;
+  char* tp;
 };
 
 inline size_t up256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
@@ -57,10 +63,19 @@ inline size_t max_chunks_of(int chunk, int num_seqs, int total_tokens) {
   return static_cast<size_t>(total_tokens) / chunk + static_cast<size_t>(num_seqs);
 }
 
-Workspace carve(void* base, int hv, int chunk, int num_seqs, int total_tokens) {
+__host__ __device__ constexpr size_t kq_bytes(int D, int C) { return 3ull * C * D * 4; }
+__host__ __device__ constexpr size_t tp_bytes(int C) { return 2ull * C * C * 4 + 2ull * C * 4; }
+
+size_t workspace_bytes(int hk, int hv, int d, int chunk, int num_seqs, int total_tokens) {
+  const size_t mc = max_chunks_of(chunk, num_seqs, total_tokens);
+  return 256 + up256(mc * sizeof(int4)) + up256((static_cast<size_t>(num_seqs) + 1) * sizeof(int)) +
+         up256(static_cast<size_t>(num_seqs) * sizeof(int) + 4) + up256(mc * hk * kq_bytes(d, chunk)) +
+         up256(mc * hv * tp_bytes(chunk));
+}
+
+Workspace carve(void* base, int hk, int hv, int d, int chunk, int num_seqs, int total_tokens) {
   char* p = static_cast<char*>(base);
   const size_t mc = max_chunks_of(chunk, num_seqs, total_tokens);
-  const size_t mat = up256(mc * hv * chunk * chunk * sizeof(float));
   Workspace w;
   w.n_chunks = reinterpret_cast<int*>(p);
   p += 256;
@@ -70,9 +85,9 @@ Workspace carve(void* base, int hv, int chunk, int num_seqs, int total_tokens) {
   p += up256((static_cast<size_t>(num_seqs) + 1) * sizeof(int));
   w.order = reinterpret_cast<int*>(p);
   p += up256(static_cast<size_t>(num_seqs) * sizeof(int) + 4);
-  w.T = reinterpret_cast<float*>(p);
-  p += mat;
-  w.P = reinterpret_cast<float*>(p);
+  w.kq = p;
+  p += up256(mc * hk * kq_bytes(d, chunk));
+  w.tp = p;
   return w;
 }
 
@@ -135,17 +150,6 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
   return v;
 }
 
-// KPL contiguous values at row p, column k, zero where k >= limit (k is a multiple of 4).
-template <int KPL>
-__device__ __forceinline__ void load_k_guard(const float* p, int k, int limit, float* out) {
-  if (k < limit) {
-    load_k<KPL>(p + k, out);
-  } else {
-#pragma unroll
-    for (int e = 0; e < KPL; ++e) out[e] = 0.f;
-  }
-}
-
 // ------------------------------------------------------------------------ intra-chunk
 template <int D, int C>
 struct IntraLayout {
@@ -164,6 +168,7 @@ struct IntraLayout {
 template <int POL, int D, int C>
 __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Workspace w) {
   using M = Mma<POL>;
+  using SP = Split<POL>;
   using Lo = IntraLayout<D, C>;
   constexpr int NB = C / 16;
   constexpr int KP = Lo::KP, CP = Lo::CP;
@@ -221,6 +226,29 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   }
   __syncthreads();
 
+  // 1b. export K^, Q^ (token rows) and K^T (head-dim rows), pre-split
+  {
+    char* kq = w.kq + (static_cast<int64_t>(chunk) * r.hk + h) * kq_bytes(D, C);
+    for (int e = tid; e < C * D / 8; e += kThreads) {
+      const int t = e / (D / 8), d0 = (e % (D / 8)) * 8;
+      float kx[8], qx[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kx[i] = Kh[t][d0 + i];
+        qx[i] = Qh[t][d0 + i];
+      }
+      SP::store(kq, C, D, t, d0, kx, 8);
+      SP::store(kq + static_cast<size_t>(C) * D * 4, C, D, t, d0, qx, 8);
+    }
+    for (int e = tid; e < D * C / 8; e += kThreads) {
+      const int dk = e / (C / 8), s0 = (e % (C / 8)) * 8;
+      float kx[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kx[i] = Kh[s0 + i][dk];
+      SP::store(kq + 2 * static_cast<size_t>(C) * D * 4, D, C, dk, s0, kx, 8);
+    }
+  }
+
   // 2. G = K^ K^T and QK = Q^ K^T on the lower-triangular 16x16 tiles
   {
     constexpr int NT = NB * (NB + 1) / 2;
@@ -251,6 +279,8 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   // 3. per v-head of this k-head's group: decay mask, A, T = (I + A)^-1, P
   for (int jj = 0; jj < group; ++jj) {
     const int j = h * group + jj;
+    char* tp = w.tp + (static_cast<int64_t>(chunk) * r.hv + j) * tp_bytes(C);
+    float* gam_out = reinterpret_cast<float*>(tp + 2 * static_cast<size_t>(C) * C * 4);
     if (wave == 0) {
       float gv = 0.f, bv = 0.f;
       if (lane < n) {
@@ -261,21 +291,29 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
       if (lane < C) {
         gam[lane] = gv;
         bet[lane] = bv;
+        gam_out[lane] = gv;
+        gam_out[C + lane] = bv;
       }
     }
     __syncthreads();
 
-    float* Pg = w.P + (static_cast<int64_t>(chunk) * r.hv + j) * C * C;
-    for (int e = tid; e < C * C; e += kThreads) {
-      const int t = e / C, s = e % C;
-      float av = 0.f, pv = 0.f;
-      if (s <= t) {
-        const float dec = expf(gam[t] - gam[s]);
-        pv = dec * QKm[t][s];
-        if (s < t) av = bet[t] * dec * Gm[t][s];
+    // A (strictly lower) into LDS, P (lower incl. diagonal) to the workspace
+    for (int e = tid; e < C * C / 8; e += kThreads) {
+      const int t = e / (C / 8), s0 = (e % (C / 8)) * 8;
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int s = s0 + i;
+        float av = 0.f;
+        pv[i] = 0.f;
+        if (s <= t) {
+          const float dec = expf(gam[t] - gam[s]);
+          pv[i] = dec * QKm[t][s];
+          if (s < t) av = bet[t] * dec * Gm[t][s];
+        }
+        Am[t][s] = av;
       }
-      Am[t][s] = av;
-      Pg[e] = pv;
+      SP::store(tp + static_cast<size_t>(C) * C * 4, C, C, t, s0, pv, 8);
     }
     __syncthreads();
 
@@ -321,37 +359,57 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
       __syncthreads();
     }
 
-    float* Tg = w.T + (static_cast<int64_t>(chunk) * r.hv + j) * C * C;
-    for (int e = tid; e < C * C; e += kThreads) {
-      const int t = e / C, s = e % C;
-      Tg[e] = (s <= t) ? Tm[t][s] : 0.f;
+    for (int e = tid; e < C * C / 8; e += kThreads) {
+      const int t = e / (C / 8), s0 = (e % (C / 8)) * 8;
+      float tv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tv[i] = (s0 + i <= t) ? Tm[t][s0 + i] : 0.f;
+      SP::store(tp, C, C, t, s0, tv, 8);
     }
     __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------------ inter-chunk
-template <int D, int C>
-struct InterLayout {
-  static constexpr int SP = D + 4;
-  static constexpr int CP = C + 4;
+// Everything one wave reads from global memory for one chunk; loaded one chunk ahead so
+// the loads overlap the previous chunk's arithmetic. Waves 0-3 ("K side") hold K^ rows
+// and T rows, waves 4-7 ("Q side") hold Q^ rows and P rows, of token tile wave % 4.
+template <int POL, int D, int C>
+struct ChunkIn {
+  using F = typename Mma<POL>::Frag;
+  static constexpr int KSTEP = Mma<POL>::KSTEP;
+  static constexpr int NV = D / KSTEP;                // k-steps over the head dim
+  static constexpr int NK = (C + KSTEP - 1) / KSTEP;  // k-steps over the chunk's tokens
+  F af[NV];     // K^ (or Q^) row of token 16*tt + l16
+  F mf[NK];     // T (or P) row of token 16*tt + l16
+  F kt[NK];     // K^T row 16*wave + l16 (this wave's state tile)
+  float vv[4];  // v at the 4 output rows this lane holds (K side)
+  float gt[4], bt[4];
+  float gn;     // gam of the chunk's last token
+  int n;        // tokens in the chunk
 };
 
 template <int POL, int D, int C>
-__global__ __launch_bounds__(kThreads) void inter_chunk_kernel(PrefillArgs a, Workspace w) {
+__global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs a, Workspace w) {
   using M = Mma<POL>;
+  using SP = Split<POL>;
+  using F = typename M::Frag;
+  using In = ChunkIn<POL, D, C>;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
   constexpr int NBLK = D / kDVB;  // state-row blocks per head
   constexpr int NT = C / 16;      // token tiles per chunk
-  constexpr int ST = D / 16;      // 16-column tiles of the state slice
-  constexpr int STW = (ST + kWaves - 1) / kWaves;
-  constexpr int NV = D / KSTEP;
-  constexpr int SP = InterLayout<D, C>::SP, CP = InterLayout<D, C>::CP;
-  __shared__ __attribute__((aligned(16))) float Sl[kDVB][SP];
-  __shared__ __attribute__((aligned(16))) float Rt[kDVB][CP];
-  __shared__ __attribute__((aligned(16))) float Ut[kDVB][CP];
-  __shared__ __attribute__((aligned(16))) float Us[kDVB][CP];
-  __shared__ __attribute__((aligned(16))) float Kt[D][CP];
+  constexpr int ST = D / 16;      // 16-column tiles of the state slice (one per wave)
+  constexpr int NV = In::NV, NK = In::NK;
+  constexpr int PADE = POL == kPolBF16X3 ? 8 : 4;  // row padding in elements
+  constexpr int SLD = D + PADE;                     // LDS row strides
+  constexpr int RLD = C + PADE;
+  constexpr int S_BYTES = kDVB * SLD * 4;
+  constexpr int R_BYTES = kDVB * RLD * 4;
+  __shared__ __attribute__((aligned(16))) char lds[S_BYTES + 3 * R_BYTES];
+  char* Sl = lds;                     // state slice  [16][D]   B operand of K^S^T, Q^S^T
+  char* Rt = lds + S_BYTES;           // R^T          [16][C]   B operand of T R
+  char* Ut = Rt + R_BYTES;            // U^T          [16][C]   B operand of P U
+  char* Us = Ut + R_BYTES;            // (e^{gam_n-gam} U)^T    A operand of the update
 
   const RecurArgs& r = a.r;
   const int per_seq = NBLK * r.hv;
@@ -373,174 +431,142 @@ __global__ __launch_bounds__(kThreads) void inter_chunk_kernel(PrefillArgs a, Wo
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int kl = KPL * lg;
-
-  f32x4 sacc[STW];
-#pragma unroll
-  for (int u = 0; u < STW; ++u) {
-    const int tile = wave * STW + u;
-    if (tile < ST) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float v = Sg[(4 * lg + rr) * D + tile * 16 + l16];
-        sacc[u][rr] = v;
-        Sl[4 * lg + rr][tile * 16 + l16] = v;
-      }
-    }
-  }
-  __syncthreads();
-
+  const bool qside = wave >= 4;
+  const int tt = wave & 3;            // token tile
+  const bool active = tt < NT;
+  const bool has_tile = wave < ST;    // this wave updates state tile `wave`
   const int nch = (len + C - 1) / C;
   const int cbase = w.chunk_off[s];
-  for (int c = 0; c < nch; ++c) {
-    const int t0 = start + c * C;
-    const int n = min(C, len - c * C);
-    const int64_t gch = static_cast<int64_t>(cbase + c) * r.hv + j;
-    const float* Tg = w.T + gch * C * C;
-    const float* Pg = w.P + gch * C * C;
 
-    float gv = 0.f, bv = 0.f;
-    if (lane < n) {
-      gv = r.g[static_cast<int64_t>(t0 + lane) * r.hv + j];
-      bv = r.beta[static_cast<int64_t>(t0 + lane) * r.hv + j];
+  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+  if (has_tile) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float v = Sg[(4 * lg + rr) * D + wave * 16 + l16];
+      sacc[rr] = v;
+      SP::store1(Sl, kDVB, SLD, 4 * lg + rr, wave * 16 + l16, v);
     }
-    gv = wave_inclusive_scan(gv);
-    const float gam_n = __shfl(gv, n - 1, 64);
-
-    const bool active = wave < NT;
-    f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
-    float gam_t[4];
-    if (active) {
-      const int trow = wave * 16 + l16;
-      float kf[NV][KPL], qf[NV][KPL];
-      float kk = 0.f, qq = 0.f;
-      if (trow < n) {
-        const float* kp = r.k + static_cast<int64_t>(t0 + trow) * r.k_stride + h * D;
-        const float* qp = r.q + static_cast<int64_t>(t0 + trow) * r.q_stride + h * D;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          load_k<KPL>(kp + kl + v * KSTEP, kf[v]);
-          load_k<KPL>(qp + kl + v * KSTEP, qf[v]);
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < NV; ++v)
-#pragma unroll
-          for (int e = 0; e < KPL; ++e) kf[v][e] = qf[v][e] = 0.f;
-      }
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-          kk = fmaf(kf[v][e], kf[v][e], kk);
-          qq = fmaf(qf[v][e], qf[v][e], qq);
-        }
-      kk += __shfl_xor(kk, 16, 64);
-      kk += __shfl_xor(kk, 32, 64);
-      qq += __shfl_xor(qq, 16, 64);
-      qq += __shfl_xor(qq, 32, 64);
-      const float rk = trow < n ? 1.0f / sqrtf(kk + r.eps) : 0.f;
-      const float rq = trow < n ? r.scale / sqrtf(qq + r.eps) : 0.f;
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-          kf[v][e] *= rk;
-          qf[v][e] *= rq;
-          Kt[kl + v * KSTEP + e][trow] = kf[v][e];
-        }
-      // X = K^ S^T, Y = Q^ S^T for this wave's 16 tokens x the block's 16 state rows
-      f32x4 xacc = {0.f, 0.f, 0.f, 0.f}, yacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        float sb[KPL];
-        load_k<KPL>(&Sl[l16][kl + v * KSTEP], sb);
-        M::step(xacc, kf[v], sb);
-        M::step(yacc, qf[v], sb);
-      }
-      // R = beta V - beta e^gam X (stored transposed), O starts as e^gam Y
-      float rv[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int t = wave * 16 + 4 * lg + rr;
-        const float gt = __shfl(gv, t, 64);
-        const float bt = __shfl(bv, t, 64);
-        const float eg = expf(gt);
-        const float vt = t < n ? r.v[static_cast<int64_t>(t0 + t) * r.v_stride + j * D + blk * kDVB + l16] : 0.f;
-        rv[rr] = bt * (vt - eg * xacc[rr]);
-        oacc[rr] = eg * yacc[rr];
-        gam_t[rr] = gt;
-      }
-      *reinterpret_cast<float4*>(&Rt[l16][wave * 16 + 4 * lg]) = make_float4(rv[0], rv[1], rv[2], rv[3]);
-    }
-    __syncthreads();
-
-    // U = T R (T lower triangular: only token columns below this tile's end)
-    if (active) {
-      const int trow = wave * 16 + l16;
-      f32x4 uacc = {0.f, 0.f, 0.f, 0.f};
-      const int kend = wave * 16 + 16;
-      for (int k0 = 0; k0 < kend; k0 += KSTEP) {
-        float ta[KPL], rb[KPL];
-        load_k_guard<KPL>(Tg + static_cast<int64_t>(trow) * C, k0 + kl, C, ta);
-        load_k_guard<KPL>(&Rt[l16][0], k0 + kl, C, rb);
-        M::step(uacc, ta, rb);
-      }
-      float us[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) us[rr] = expf(gam_n - gam_t[rr]) * uacc[rr];
-      *reinterpret_cast<float4*>(&Ut[l16][wave * 16 + 4 * lg]) = make_float4(uacc[0], uacc[1], uacc[2], uacc[3]);
-      *reinterpret_cast<float4*>(&Us[l16][wave * 16 + 4 * lg]) = make_float4(us[0], us[1], us[2], us[3]);
-    }
-    __syncthreads();
-
-    // O = e^gam Y + P U
-    if (active) {
-      const int trow = wave * 16 + l16;
-      const int kend = wave * 16 + 16;
-      for (int k0 = 0; k0 < kend; k0 += KSTEP) {
-        float pa[KPL], ub[KPL];
-        load_k_guard<KPL>(Pg + static_cast<int64_t>(trow) * C, k0 + kl, C, pa);
-        load_k_guard<KPL>(&Ut[l16][0], k0 + kl, C, ub);
-        M::step(oacc, pa, ub);
-      }
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int t = wave * 16 + 4 * lg + rr;
-        if (t < n) r.o[(static_cast<int64_t>(t0 + t) * r.hv + j) * D + blk * kDVB + l16] = oacc[rr];
-      }
-    }
-
-    // S <- e^{gam_n} S + Us^T K^   (this wave's 16-column tiles of the slice)
-    const float egn = expf(gam_n);
-#pragma unroll
-    for (int u = 0; u < STW; ++u) {
-      const int tile = wave * STW + u;
-      if (tile < ST) {
-        f32x4 acc;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) acc[rr] = sacc[u][rr] * egn;
-#pragma unroll
-        for (int k0 = 0; k0 < C; k0 += KSTEP) {
-          float ua[KPL], kb[KPL];
-          load_k_guard<KPL>(&Us[l16][0], k0 + kl, C, ua);
-          load_k_guard<KPL>(&Kt[tile * 16 + l16][0], k0 + kl, C, kb);
-          M::step(acc, ua, kb);
-        }
-        sacc[u] = acc;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) Sl[4 * lg + rr][tile * 16 + l16] = acc[rr];
-      }
-    }
-    __syncthreads();
   }
 
+  auto load = [&](int c, In& in) {
+    const int t0 = start + c * C;
+    in.n = min(C, len - c * C);
+    const int64_t gc = cbase + c;
+    const char* kq = w.kq + (gc * r.hk + h) * kq_bytes(D, C);
+    const char* tp = w.tp + (gc * r.hv + j) * tp_bytes(C);
+    const float* gb = reinterpret_cast<const float*>(tp + 2 * static_cast<size_t>(C) * C * 4);
+    in.gn = gb[C - 1];
+    if (active) {
+      const char* arows = kq + (qside ? static_cast<size_t>(C) * D * 4 : 0);
+      const char* mrows = tp + (qside ? static_cast<size_t>(C) * C * 4 : 0);
 #pragma unroll
-  for (int u = 0; u < STW; ++u) {
-    const int tile = wave * STW + u;
-    if (tile < ST) {
+      for (int v = 0; v < NV; ++v) in.af[v] = SP::load(arows, C, D, tt * 16 + l16, kl + v * KSTEP);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) Sg[(4 * lg + rr) * D + tile * 16 + l16] = sacc[u][rr];
+      for (int kk = 0; kk < NK; ++kk)
+        in.mf[kk] = (kk * KSTEP + kl < C) ? SP::load(mrows, C, C, tt * 16 + l16, kk * KSTEP + kl) : SP::zero();
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int t = tt * 16 + 4 * lg + rr;
+        in.gt[rr] = gb[t];
+        in.bt[rr] = gb[C + t];
+        in.vv[rr] = (!qside && t < in.n)
+                        ? r.v[static_cast<int64_t>(t0 + t) * r.v_stride + j * D + blk * kDVB + l16]
+                        : 0.f;
+      }
     }
+    if (has_tile) {
+      const char* ktp = kq + 2 * static_cast<size_t>(C) * D * 4;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        in.kt[kk] = (kk * KSTEP + kl < C) ? SP::load(ktp, D, C, wave * 16 + l16, kk * KSTEP + kl) : SP::zero();
+    }
+  };
+
+  auto process = [&](int c, In& in) {
+    const int t0 = start + c * C;
+    f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+    // phase 1: X = K^ S^T (K side) or Y = Q^ S^T (Q side)
+    if (active) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < NV; ++v) M::mma(acc, in.af[v], SP::load(Sl, kDVB, SLD, l16, kl + v * KSTEP));
+      if (!qside) {
+        float rv[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) rv[rr] = in.bt[rr] * (in.vv[rr] - expf(in.gt[rr]) * acc[rr]);
+        SP::store(Rt, kDVB, RLD, l16, tt * 16 + 4 * lg, rv, 4);
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) oacc[rr] = expf(in.gt[rr]) * acc[rr];
+      }
+    }
+    __syncthreads();
+    // phase 2 (K side): U = T R, T lower triangular
+    if (active && !qside) {
+      f32x4 uacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        if (kk * KSTEP < tt * 16 + 16) {
+          const F rf = (kk * KSTEP + kl < C) ? SP::load(Rt, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+          M::mma(uacc, in.mf[kk], rf);
+        }
+      }
+      float ut[4], us[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        ut[rr] = uacc[rr];
+        us[rr] = expf(in.gn - in.gt[rr]) * uacc[rr];
+      }
+      SP::store(Ut, kDVB, RLD, l16, tt * 16 + 4 * lg, ut, 4);
+      SP::store(Us, kDVB, RLD, l16, tt * 16 + 4 * lg, us, 4);
+    }
+    __syncthreads();
+    // phase 3: O = e^gam Y + P U (Q side); S <- e^{gam_n} S + Us^T K^ (state tiles)
+    if (active && qside) {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        if (kk * KSTEP < tt * 16 + 16) {
+          const F uf = (kk * KSTEP + kl < C) ? SP::load(Ut, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+          M::mma(oacc, in.mf[kk], uf);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int t = tt * 16 + 4 * lg + rr;
+        if (t < in.n) r.o[(static_cast<int64_t>(t0 + t) * r.hv + j) * D + blk * kDVB + l16] = oacc[rr];
+      }
+    }
+    if (has_tile) {
+      const float egn = expf(in.gn);
+      f32x4 acc;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) acc[rr] = sacc[rr] * egn;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const F ua = (kk * KSTEP + kl < C) ? SP::load(Us, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+        M::mma(acc, ua, in.kt[kk]);
+      }
+      sacc = acc;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) SP::store1(Sl, kDVB, SLD, 4 * lg + rr, wave * 16 + l16, acc[rr]);
+    }
+    __syncthreads();
+  };
+
+  In in0, in1;
+  load(0, in0);
+  __syncthreads();  // Sl filled
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) load(c + 1, in1);
+    process(c, in0);
+    if (c + 1 >= nch) break;
+    if (c + 2 < nch) load(c + 2, in0);
+    process(c + 1, in1);
+  }
+
+  if (has_tile) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) Sg[(4 * lg + rr) * D + wave * 16 + l16] = sacc[rr];
   }
 }
 
@@ -551,7 +577,7 @@ hipError_t launch_chunked(const PrefillArgs& a, const Workspace& w, hipStream_t 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned blocks = static_cast<unsigned>((D / kDVB) * a.r.hv * a.num_seqs);
-  inter_chunk_kernel<POL, D, C><<<blocks, kThreads, 0, s>>>(a, w);
+  inter_chunk_kernel<POL, D, C><<<blocks, kInterThreads, 0, s>>>(a, w);
   return hipGetLastError();
 }
 
@@ -575,17 +601,14 @@ hipError_t by_dim(const PrefillArgs& a, const Workspace& w, hipStream_t s) {
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int32_t hv, int32_t d, int32_t chunk, int32_t num_seqs, int32_t total_tokens) {
-  (void)d;
-  const size_t mc = max_chunks_of(chunk, num_seqs, total_tokens);
-  return 256 + up256(mc * sizeof(int4)) + up256((static_cast<size_t>(num_seqs) + 1) * sizeof(int)) +
-         up256(static_cast<size_t>(num_seqs) * sizeof(int) + 4) +
-         2 * up256(mc * static_cast<size_t>(hv) * chunk * chunk * sizeof(float));
+size_t prefill_workspace_bytes(int32_t hk, int32_t hv, int32_t d, int32_t chunk, int32_t num_seqs,
+                               int32_t total_tokens) {
+  return workspace_bytes(hk, hv, d, chunk, num_seqs, total_tokens);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (a.num_seqs == 0 || a.total_tokens == 0) return hipSuccess;
-  const Workspace w = carve(a.workspace, a.r.hv, a.chunk, a.num_seqs, a.total_tokens);
+  const Workspace w = carve(a.workspace, a.r.hk, a.r.hv, a.r.d, a.chunk, a.num_seqs, a.total_tokens);
   chunk_table_kernel<<<1, kMetaThreads, 0, s>>>(a.cu_seqlens, a.num_seqs, a.chunk, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
