@@ -55,11 +55,30 @@ class GDNError(RuntimeError):
         self.status = status
 
 
+def _hip_runtimes() -> set:
+    """Distinct HIP runtime files mapped into this process (Linux)."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {ln.split()[-1] for ln in f if "libamdhip64.so" in ln}
+    except OSError:  # pragma: no cover
+        return set()
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with gated_delta_rule_conv_amd/build_lib.py "
                           "(or __graft_entry__.build()); there is no fallback path")
+    # The library takes device pointers and hipStream_t handles made by torch, so it has
+    # to run on the HIP runtime torch already loaded. Both runtimes carry the soname
+    # libamdhip64.so.7: importing torch first makes the loader reuse torch's copy for
+    # libgdn.so instead of mapping a second, independent runtime.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are mapped into this process ({sorted(runtimes)}); libgdn.so must "
+                          "share torch's runtime")
     P, I32, I64, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
     D = ctypes.POINTER(gdn_dims)
     lib.gdn_conv_update.argtypes = [D, P, I64, P, I64, P, P, P, P, I32, I32, P]

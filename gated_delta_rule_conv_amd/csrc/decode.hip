@@ -13,12 +13,23 @@
 //     S_r <- alpha S_r + u_r k^,        o_r = alpha p_r + u_r (k^ . q^)
 // so the state is streamed once from HBM and written once, rows in any order.
 //
-// Mapping (d = 128): a block is one (slot, v-head) = 64 KiB of state, 4 waves x 32 rows.
-// Eight lanes share a row; lane c of the eight holds floats [4c + 32u, 4c + 32u + 4),
-// u = 0..3, so each load instruction of a wave covers 8 rows x 128 contiguous bytes.
-// Each lane issues its 16 float4 loads before any arithmetic. The two row dots are
-// reduced over the eight lanes with a fixed DPP butterfly, so the bits of a slot's
-// result do not depend on m, on the grid, or on which other slots are in the call.
+// Work unit = one wave over P passes of RPP rows of one (slot, v-head). D/16 lanes
+// share a row; lane c of a row group holds floats [4c + 4*LPR*u, +4), u = 0..3, so
+// every load instruction of a wave covers RPP whole rows (RPP * D * 4 = 4 KiB
+// contiguous). Units are dealt to waves in (slot, head, row) order, four waves per
+// workgroup, so the grid sweeps each 2 MiB slot state front to back.
+//
+// What the memory system wants here (measured on MI355X at 30 layers x 64 slots):
+//  * small units (one 4 KiB pass per wave at large m) beat long-lived waves that hold
+//    16 KiB of state: reads and writes of many short waves interleave like a plain
+//    streaming copy;
+//  * state loads and stores go through the global (not flat) address space and carry
+//    the nontemporal hint; the slot pointer, g and beta are wave-uniform scalar loads;
+//  * every load of a unit is issued before any arithmetic, and nothing waits on a
+//    store (v is read up front).
+// The two row dots are reduced over the row's lanes with a fixed DPP butterfly, so the
+// bits of a slot's result depend neither on m, nor on the unit size, nor on which
+// other slots are in the call.
 
 #include "device_common.h"
 #include "launch.h"
@@ -26,60 +37,77 @@
 namespace gdn {
 namespace {
 
-template <int D>
+typedef __attribute__((address_space(1))) f32x4 gf32x4;
+typedef __attribute__((address_space(1))) float gfloat;
+typedef __attribute__((address_space(1))) const float cgfloat;
+typedef __attribute__((address_space(4))) const uint64_t cu64;
+typedef __attribute__((address_space(4))) const float cfloat;
+// (Generic -> global/constant pointer conversions are address-space casts, which C++
+// spells only as C-style casts.)
+
+constexpr int kDecodeWaves = 4;  // waves per workgroup
+
+template <int D, int P>
 struct DecodeCfg {
-  static constexpr int kLanesPerRow = D / 16;          // 16 floats per lane per row
-  static constexpr int kRowsPerPass = kWave / kLanesPerRow;
-  static constexpr int kPasses = (D * D / 4096) > 0 ? (D * D / 4096) : 1;
-  static constexpr int kRowsPerWave = kRowsPerPass * kPasses;
-  static constexpr int kWaves = D / kRowsPerWave;
-  static constexpr int kThreads = kWaves * kWave;
-  static_assert(kWaves * kRowsPerWave == D, "rows must tile the head");
+  static constexpr int LPR = D / 16;          // lanes per row (16 floats per lane)
+  static constexpr int RPP = kWave / LPR;     // rows per pass
+  static constexpr int ROWS = RPP * P;        // rows per unit
+  static constexpr int NPART = D / ROWS;      // units per (slot, head)
+  static_assert(NPART * ROWS == D, "units must tile the head");
 };
 
-template <int D>
-__global__ __launch_bounds__(DecodeCfg<D>::kThreads) void decode_kernel(RecurArgs a) {
-  using Cfg = DecodeCfg<D>;
-  constexpr int LPR = Cfg::kLanesPerRow;
-  constexpr int P = Cfg::kPasses;
-  const int j = blockIdx.x;  // v-head
-  const int i = blockIdx.y;  // slot
-  const uint64_t sp = a.state_ptrs[i];
+template <int D, int P, bool SCHED_FENCE>
+__global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(RecurArgs a, int32_t total_units) {
+  using Cfg = DecodeCfg<D, P>;
+  constexpr int LPR = Cfg::LPR, RPP = Cfg::RPP, NPART = Cfg::NPART;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int u = blockIdx.x * kDecodeWaves + w;
+  if (u >= total_units) return;
+  const int part = u % NPART;
+  const int j = (u / NPART) % a.hv;
+  const int i = (u / NPART) / a.hv;
+  const uint64_t sp = ((cu64*)a.state_ptrs)[i];
   if (sp == 0) return;  // inactive slot
   const int h = j / (a.hv / a.hk);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int c = lane % LPR;           // column group inside the row
-  const int rlocal = lane / LPR;      // row inside a pass
+  const int c = lane % LPR;   // column group inside the row
+  const int rl = lane / LPR;  // row inside a pass
+  const int row0 = part * Cfg::ROWS + rl;
 
-  float* S = reinterpret_cast<float*>(sp) + static_cast<int64_t>(j) * D * D;
-  const int row0 = wave * Cfg::kRowsPerWave + rlocal;
+  gf32x4* S = (gf32x4*)(reinterpret_cast<float*>(sp) + static_cast<int64_t>(j) * D * D);
 
-  // state rows: issue every load first
+  // every load of the unit first: state rows, k, q, v, g, beta
   f32x4 s[P][4];
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const f32x4* rowp = reinterpret_cast<const f32x4*>(S + static_cast<int64_t>(row0 + p * Cfg::kRowsPerPass) * D);
+  for (int p = 0; p < P; ++p)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) s[p][u] = __builtin_nontemporal_load(rowp + c + LPR * u);
+    for (int e = 0; e < 4; ++e)
+      s[p][e] = __builtin_nontemporal_load(S + static_cast<int64_t>(row0 + p * RPP) * (D / 4) + c + LPR * e);
+  const gf32x4* kp = (const gf32x4*)(a.k + static_cast<int64_t>(i) * a.k_stride + h * D);
+  const gf32x4* qp = (const gf32x4*)(a.q + static_cast<int64_t>(i) * a.q_stride + h * D);
+  f32x4 kv[4], qv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    kv[e] = kp[c + LPR * e];
+    qv[e] = qp[c + LPR * e];
   }
+  const cgfloat* vrow = (const cgfloat*)(a.v + static_cast<int64_t>(i) * a.v_stride + static_cast<int64_t>(j) * D);
+  float vr[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) vr[p] = vrow[row0 + p * RPP];
+  const int64_t gi = static_cast<int64_t>(i) * a.hv + j;
+  const float gval = ((cfloat*)a.g)[gi];
+  const float beta = ((cfloat*)a.beta)[gi];
+  if constexpr (SCHED_FENCE) __builtin_amdgcn_sched_barrier(0);
 
-  // k^ and q^ at this lane's 16 columns
-  const float4* kp = reinterpret_cast<const float4*>(a.k + static_cast<int64_t>(i) * a.k_stride + h * D);
-  const float4* qp = reinterpret_cast<const float4*>(a.q + static_cast<int64_t>(i) * a.q_stride + h * D);
-  float4 kv[4], qv[4];
+  // k^ and q^ at this lane's 16 columns, and k^ . q^
   float kk = 0.f, qq = 0.f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    kv[u] = kp[c + LPR * u];
-    qv[u] = qp[c + LPR * u];
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    kk = fmaf(kv[u].x, kv[u].x, kk); kk = fmaf(kv[u].y, kv[u].y, kk);
-    kk = fmaf(kv[u].z, kv[u].z, kk); kk = fmaf(kv[u].w, kv[u].w, kk);
-    qq = fmaf(qv[u].x, qv[u].x, qq); qq = fmaf(qv[u].y, qv[u].y, qq);
-    qq = fmaf(qv[u].z, qv[u].z, qq); qq = fmaf(qv[u].w, qv[u].w, qq);
+  for (int e = 0; e < 4; ++e) {
+    kk = fmaf(kv[e].x, kv[e].x, kk); kk = fmaf(kv[e].y, kv[e].y, kk);
+    kk = fmaf(kv[e].z, kv[e].z, kk); kk = fmaf(kv[e].w, kv[e].w, kk);
+    qq = fmaf(qv[e].x, qv[e].x, qq); qq = fmaf(qv[e].y, qv[e].y, qq);
+    qq = fmaf(qv[e].z, qv[e].z, qq); qq = fmaf(qv[e].w, qv[e].w, qq);
   }
   kk = group_sum<LPR>(kk);
   qq = group_sum<LPR>(qq);
@@ -87,59 +115,65 @@ __global__ __launch_bounds__(DecodeCfg<D>::kThreads) void decode_kernel(RecurArg
   const float rq = a.scale / sqrtf(qq + a.eps);
   float kq = 0.f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    kv[u].x *= rk; kv[u].y *= rk; kv[u].z *= rk; kv[u].w *= rk;
-    qv[u].x *= rq; qv[u].y *= rq; qv[u].z *= rq; qv[u].w *= rq;
-    kq = fmaf(kv[u].x, qv[u].x, kq); kq = fmaf(kv[u].y, qv[u].y, kq);
-    kq = fmaf(kv[u].z, qv[u].z, kq); kq = fmaf(kv[u].w, qv[u].w, kq);
+  for (int e = 0; e < 4; ++e) {
+    kv[e].x *= rk; kv[e].y *= rk; kv[e].z *= rk; kv[e].w *= rk;
+    qv[e].x *= rq; qv[e].y *= rq; qv[e].z *= rq; qv[e].w *= rq;
+    kq = fmaf(kv[e].x, qv[e].x, kq); kq = fmaf(kv[e].y, qv[e].y, kq);
+    kq = fmaf(kv[e].z, qv[e].z, kq); kq = fmaf(kv[e].w, qv[e].w, kq);
   }
   kq = group_sum<LPR>(kq);
-
-  const int64_t gi = static_cast<int64_t>(i) * a.hv + j;
-  const float alpha = expf(a.g[gi]);
-  const float beta = a.beta[gi];
-  const float* vrow = a.v + static_cast<int64_t>(i) * a.v_stride + static_cast<int64_t>(j) * D;
-  float* orow = a.o + gi * D;
+  const float alpha = expf(gval);
+  gfloat* orow = (gfloat*)(a.o + gi * D);
 
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    const int r = row0 + p * Cfg::kRowsPerPass;
+    const int r = row0 + p * RPP;
     float sk = 0.f, sq = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      sk = fmaf(s[p][u].x, kv[u].x, sk); sk = fmaf(s[p][u].y, kv[u].y, sk);
-      sk = fmaf(s[p][u].z, kv[u].z, sk); sk = fmaf(s[p][u].w, kv[u].w, sk);
-      sq = fmaf(s[p][u].x, qv[u].x, sq); sq = fmaf(s[p][u].y, qv[u].y, sq);
-      sq = fmaf(s[p][u].z, qv[u].z, sq); sq = fmaf(s[p][u].w, qv[u].w, sq);
+    for (int e = 0; e < 4; ++e) {
+      sk = fmaf(s[p][e].x, kv[e].x, sk); sk = fmaf(s[p][e].y, kv[e].y, sk);
+      sk = fmaf(s[p][e].z, kv[e].z, sk); sk = fmaf(s[p][e].w, kv[e].w, sk);
+      sq = fmaf(s[p][e].x, qv[e].x, sq); sq = fmaf(s[p][e].y, qv[e].y, sq);
+      sq = fmaf(s[p][e].z, qv[e].z, sq); sq = fmaf(s[p][e].w, qv[e].w, sq);
     }
     sk = group_sum<LPR>(sk);
     sq = group_sum<LPR>(sq);
-    const float ur = beta * (vrow[r] - alpha * sk);
-    f32x4* rowp = reinterpret_cast<f32x4*>(S + static_cast<int64_t>(r) * D);
+    const float ur = beta * (vr[p] - alpha * sk);
+    gf32x4* rowp = S + static_cast<int64_t>(r) * (D / 4);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int e = 0; e < 4; ++e) {
       f32x4 n;
-      n.x = fmaf(ur, kv[u].x, alpha * s[p][u].x);
-      n.y = fmaf(ur, kv[u].y, alpha * s[p][u].y);
-      n.z = fmaf(ur, kv[u].z, alpha * s[p][u].z);
-      n.w = fmaf(ur, kv[u].w, alpha * s[p][u].w);
-      __builtin_nontemporal_store(n, rowp + c + LPR * u);
+      n.x = fmaf(ur, kv[e].x, alpha * s[p][e].x);
+      n.y = fmaf(ur, kv[e].y, alpha * s[p][e].y);
+      n.z = fmaf(ur, kv[e].z, alpha * s[p][e].z);
+      n.w = fmaf(ur, kv[e].w, alpha * s[p][e].w);
+      __builtin_nontemporal_store(n, rowp + c + LPR * e);
     }
     if (c == 0) orow[r] = fmaf(ur, kq, alpha * sq);
   }
 }
 
+template <int D, int P, bool F>
+hipError_t launch_units(const RecurArgs& a, int32_t m, hipStream_t s) {
+  const int64_t units = static_cast<int64_t>(m) * a.hv * DecodeCfg<D, P>::NPART;
+  const unsigned blocks = static_cast<unsigned>((units + kDecodeWaves - 1) / kDecodeWaves);
+  decode_kernel<D, P, F><<<blocks, kDecodeWaves * kWave, 0, s>>>(a, static_cast<int32_t>(units));
+  return hipGetLastError();
+}
+
 }  // namespace
 
+// Unit size by batch: one pass per wave once the call has thousands of (slot, head)
+// pairs (m * Hv >= 1024), two passes below that, where fewer, longer waves hide the
+// launch ramp better. Either choice gives the same bits.
 hipError_t launch_decode(const RecurArgs& a, int32_t m, hipStream_t s) {
   if (m == 0) return hipSuccess;
-  dim3 grid(a.hv, m);
+  const bool big = static_cast<int64_t>(m) * a.hv >= 1024;
   switch (a.d) {
-    case 32: decode_kernel<32><<<grid, DecodeCfg<32>::kThreads, 0, s>>>(a); break;
-    case 64: decode_kernel<64><<<grid, DecodeCfg<64>::kThreads, 0, s>>>(a); break;
-    default: decode_kernel<128><<<grid, DecodeCfg<128>::kThreads, 0, s>>>(a); break;
+    case 32: return launch_units<32, 1, false>(a, m, s);
+    case 64: return big ? launch_units<64, 1, false>(a, m, s) : launch_units<64, 2, true>(a, m, s);
+    default: return big ? launch_units<128, 1, false>(a, m, s) : launch_units<128, 2, true>(a, m, s);
   }
-  return hipGetLastError();
 }
 
 namespace {

@@ -158,3 +158,13 @@ def test_slot_pointer_checks():
     assert _status(gdn.gdn_slot_pointers, FAKE, 0, 4, FAKE, 4, FAKE)[0] == _lib.GDN_ERR_SHAPE
     assert _status(gdn.gdn_slot_pointers, FAKE, 256, 4, None, 4, FAKE)[0] == _lib.GDN_ERR_NULL
     gdn.gdn_slot_pointers(FAKE, 256, 4, FAKE, 0, FAKE)
+
+
+def test_library_shares_torchs_hip_runtime():
+    """libgdn.so receives torch's device pointers and stream handles, so exactly one HIP
+    runtime (torch's) may be mapped into the process, whatever was imported first."""
+    runtimes = _lib._hip_runtimes()
+    assert len(runtimes) == 1, runtimes
+    import torch
+
+    assert os.path.dirname(next(iter(runtimes))) == os.path.join(os.path.dirname(torch.__file__), "lib")

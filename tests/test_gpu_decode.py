@@ -200,3 +200,106 @@ def test_inactive_slot_pointers_are_skipped_and_run_twice_is_deterministic():
         outs.append((bits_of(o), bits_of(pool.state), bits_of(pool.conv_state)))
     for a, b in zip(outs[0], outs[1]):
         np.testing.assert_array_equal(a, b)
+
+
+def test_large_batch_unit_size_is_bit_exact_against_m1():
+    """At m * Hv >= 1024 the decode launch uses one-pass units (8 state rows per wave),
+    below it two-pass units; a slot's bits must not depend on which one ran. m = 40 in one
+    call == the same slots one at a time (m = 1)."""
+    import torch
+
+    import gated_delta_rule_conv_amd as gdn
+
+    announce("decode bit-exact m=40 (one-pass units) vs m=1 (two-pass units)")
+    shape = LayerShape(16, 32, 128, in_dtype="bf16")
+    dims = _dims(shape)
+    base = make_decode_pool(2, pool=48, shape=shape)
+    slots = [int(s) for s in base["perm"][:40]]
+    inp = make_decode_step(2, 5, 40, shape=shape)
+    conv_w = to_dev(base["conv_w"], "bf16")
+    x, g, beta = to_dev(inp["x"], "bf16"), to_dev(inp["g"], "f32"), to_dev(inp["beta"], "f32")
+
+    def fresh_pool():
+        return gdn.SlotPool(dims, 48, state=to_dev(base["S"], "f32"), conv_state=to_dev(base["conv_state"], "bf16"))
+
+    pa = fresh_pool()
+    sp, cp = pa.pointers(torch.tensor(slots, dtype=torch.int32, device="cuda"))
+    ya = torch.empty((40, shape.channels), dtype=torch.float32, device="cuda")
+    oa = torch.empty((40, 32, 128), dtype=torch.float32, device="cuda")
+    gdn.conv_update(dims, x, ya, conv_w, None, cp)
+    gdn.decode(dims, ya, g, beta, oa, sp)
+    pb = fresh_pool()
+    ob = torch.empty_like(oa)
+    for i, s in enumerate(slots):
+        sp1, cp1 = pb.pointers(torch.tensor([s], dtype=torch.int32, device="cuda"))
+        y1 = torch.empty((1, shape.channels), dtype=torch.float32, device="cuda")
+        o1 = torch.empty((1, 32, 128), dtype=torch.float32, device="cuda")
+        gdn.conv_update(dims, x[i:i + 1], y1, conv_w, None, cp1)
+        gdn.decode(dims, y1, g[i:i + 1], beta[i:i + 1], o1, sp1)
+        ob[i] = o1[0]
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits_of(oa), bits_of(ob))
+    np.testing.assert_array_equal(bits_of(pa.state), bits_of(pb.state))
+    np.testing.assert_array_equal(bits_of(pa.conv_state), bits_of(pb.conv_state))
+    # and the one-pass result matches the oracle
+    ref = decode_layer(inp["x"], base["conv_w"], base["conv_state"][slots], base["S"][slots], inp["g"],
+                       inp["beta"], 16, 32, 128, in_dtype="bf16")
+    S_gpu = pa.state[slots].cpu().numpy()
+    err_S = max_block_err_S(S_gpu, ref["S"])
+    err_o = max(normwise_err(oa[i, j].cpu().numpy(), ref["o"][i, j]) for i in range(40) for j in range(32))
+    print(f"m=40 one-pass units: max normwise err o={err_o:.3e} S={err_S:.3e}")
+    assert err_S <= TOL_BF16 and err_o <= TOL_BF16
+
+
+def test_graph_replay_matches_eager_every_replay():
+    """A two-layer decode step captured in a HIP graph, replayed three times with eager
+    work in between: every replay equals the same step run eagerly, bit for bit."""
+    import torch
+
+    import gated_delta_rule_conv_amd as gdn
+
+    announce("decode graph replay vs eager")
+    shape = LayerShape(16, 32, 128, in_dtype="bf16")
+    dims = _dims(shape)
+    layers, pool_slots, m = 2, 24, 20
+    base = [make_decode_pool(2, pool=pool_slots, shape=shape) for _ in range(layers)]
+    slots = [int(s) for s in base[0]["perm"][:m]]
+    idx = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    inp = make_decode_step(2, 7, m, shape=shape)
+    x, g, beta = to_dev(inp["x"], "bf16"), to_dev(inp["g"], "f32"), to_dev(inp["beta"], "f32")
+
+    def rig():
+        pools = [gdn.SlotPool(dims, pool_slots, state=to_dev(b["S"], "f32"),
+                              conv_state=to_dev(b["conv_state"], "bf16")) for b in base]
+        ptrs = [p.pointers(idx) for p in pools]
+        ws = [to_dev(b["conv_w"], "bf16") for b in base]
+        y = torch.empty((m, shape.channels), dtype=torch.float32, device="cuda")
+        o = torch.empty((layers, m, 32, 128), dtype=torch.float32, device="cuda")
+
+        def step():
+            for layer in range(layers):
+                sp, cp = ptrs[layer]
+                gdn.conv_update(dims, x, y, ws[layer], None, cp)
+                gdn.decode(dims, y, g, beta, o[layer], sp)
+        return pools, o, step
+
+    pools_g, o_g, step_g = rig()
+    pools_e, o_e, step_e = rig()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step_g()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        graph.replay()
+        step_e()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits_of(o_g), bits_of(o_e), err_msg=f"replay {rep}: o")
+        for pg, pe in zip(pools_g, pools_e):
+            np.testing.assert_array_equal(bits_of(pg.state), bits_of(pe.state), err_msg=f"replay {rep}: state")
+            np.testing.assert_array_equal(bits_of(pg.conv_state), bits_of(pe.conv_state),
+                                          err_msg=f"replay {rep}: conv state")
