@@ -20,6 +20,7 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kDecThreads = 64;  // decode: one wave per workgroup
 constexpr int kVec = 8;
 constexpr int kStrip = 16;  // tokens per block in prefill mode
 
@@ -50,6 +51,29 @@ struct ConvTaps {
     }
   }
 
+  // the same from raw (unconverted) tap and bias vectors
+  __device__ __forceinline__ void from_raw(const typename Vec8<T>::Raw (&wr)[K], const typename Vec8<T>::Raw& br,
+                                           bool has_b) {
+    float flat[K * kVec];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      float tmp[kVec];
+      Vec8<T>::convert(wr[i], tmp);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) flat[i * kVec + e] = tmp[e];
+    }
+#pragma unroll
+    for (int c = 0; c < kVec; ++c)
+#pragma unroll
+      for (int j = 0; j < K; ++j) w[j][c] = flat[c * K + j];
+    if (has_b) {
+      Vec8<T>::convert(br, b);
+    } else {
+#pragma unroll
+      for (int c = 0; c < kVec; ++c) b[c] = 0.f;
+    }
+  }
+
   // win[0..K-2] = z rows preceding the current token (oldest first), cur = current token.
   __device__ __forceinline__ void apply(const float (&win)[K - 1][kVec], const float (&cur)[kVec], bool silu,
                                         float (&out)[kVec]) const {
@@ -73,7 +97,13 @@ __global__ __launch_bounds__(kThreads) void conv_prefill_kernel(ConvArgs a) {
   const T* __restrict__ x = static_cast<const T*>(a.x);
   const int* __restrict__ cu = a.cu_seqlens;
   const int t0 = blockIdx.y * kStrip;
-  const int t1 = min(t0 + kStrip, a.total_tokens);
+  const int nt = min(kStrip, a.total_tokens - t0);
+
+  // every x row of the strip is loaded up front (rows past the end repeat the last one),
+  // so the strip's loads are all in flight together
+  typename Vec8<T>::Raw xr[kStrip];
+#pragma unroll
+  for (int u = 0; u < kStrip; ++u) xr[u] = Vec8<T>::load_raw(x + static_cast<int64_t>(t0 + min(u, nt - 1)) * a.x_stride + ch0);
 
   ConvTaps<T, K> taps;
   taps.load(static_cast<const T*>(a.w), static_cast<const T*>(a.b), ch0);
@@ -90,36 +120,40 @@ __global__ __launch_bounds__(kThreads) void conv_prefill_kernel(ConvArgs a) {
 
   float win[K - 1][kVec];
   bool reload = true;
-  for (int t = t0; t < t1; ++t) {
-    while (t >= seq_end) {  // next non-empty sequence starts at t
-      ++s;
-      seq_start = seq_end;
-      seq_end = cu[s + 1];
-      reload = true;
-    }
-    if (reload) {
-      const int p = t - seq_start;  // position of t in its sequence
-      const T* cs = reinterpret_cast<const T*>(a.state_ptrs[s]);
 #pragma unroll
-      for (int i = 0; i < K - 1; ++i) {
-        const int r = p + i;  // z row feeding tap i of token t
-        if (r < K - 1)
-          Vec8<T>::load(cs + static_cast<int64_t>(r) * C + ch0, win[i]);
-        else
-          Vec8<T>::load(x + static_cast<int64_t>(seq_start + r - (K - 1)) * a.x_stride + ch0, win[i]);
+  for (int u = 0; u < kStrip; ++u) {
+    if (u < nt) {  // (a guard, not a break: the loop must unroll fully to keep xr in registers)
+      const int t = t0 + u;
+      while (t >= seq_end) {  // next non-empty sequence starts at t
+        ++s;
+        seq_start = seq_end;
+        seq_end = cu[s + 1];
+        reload = true;
       }
-      reload = false;
+      if (reload) {
+        const int p = t - seq_start;  // position of t in its sequence
+        const T* cs = reinterpret_cast<const T*>(a.state_ptrs[s]);
+#pragma unroll
+        for (int i = 0; i < K - 1; ++i) {
+          const int r = p + i;  // z row feeding tap i of token t
+          if (r < K - 1)
+            Vec8<T>::load(cs + static_cast<int64_t>(r) * C + ch0, win[i]);
+          else
+            Vec8<T>::load(x + static_cast<int64_t>(seq_start + r - (K - 1)) * a.x_stride + ch0, win[i]);
+        }
+        reload = false;
+      }
+      float cur[kVec], out[kVec];
+      Vec8<T>::convert(xr[u], cur);
+      taps.apply(win, cur, a.silu != 0, out);
+      Vec8<float>::store(a.y + static_cast<int64_t>(t) * a.y_stride + ch0, out);
+#pragma unroll
+      for (int i = 0; i < K - 2; ++i)
+#pragma unroll
+        for (int c = 0; c < kVec; ++c) win[i][c] = win[i + 1][c];
+#pragma unroll
+      for (int c = 0; c < kVec; ++c) win[K - 2][c] = cur[c];
     }
-    float cur[kVec], out[kVec];
-    Vec8<T>::load(x + static_cast<int64_t>(t) * a.x_stride + ch0, cur);
-    taps.apply(win, cur, a.silu != 0, out);
-    Vec8<float>::store(a.y + static_cast<int64_t>(t) * a.y_stride + ch0, out);
-#pragma unroll
-    for (int i = 0; i < K - 2; ++i)
-#pragma unroll
-      for (int c = 0; c < kVec; ++c) win[i][c] = win[i + 1][c];
-#pragma unroll
-    for (int c = 0; c < kVec; ++c) win[K - 2][c] = cur[c];
   }
 }
 
@@ -151,27 +185,40 @@ __global__ __launch_bounds__(kThreads) void conv_commit_kernel(ConvArgs a) {
 }
 
 // Decode mode: token i belongs to slot i (sequence length 1); conv and state shift in one
-// pass, in place. A zero state pointer marks an inactive slot.
+// pass, in place. A zero state pointer marks an inactive slot. The slot pointer is a
+// scalar load; the taps, the K-1 state rows and the token are all loaded before any of
+// them is used (one memory round trip), and the state goes through global-address-space
+// accesses. Small workgroups spread a slot over many CUs.
 template <typename T, int K>
-__global__ __launch_bounds__(kThreads) void conv_decode_kernel(ConvArgs a) {
-  const int ch0 = (blockIdx.x * kThreads + threadIdx.x) * kVec;
+__global__ __launch_bounds__(kDecThreads) void conv_decode_kernel(ConvArgs a) {
+  typedef __attribute__((address_space(4))) const uint64_t cu64;
+  const int ch0 = (blockIdx.x * kDecThreads + threadIdx.x) * kVec;
   if (ch0 >= a.channels) return;
   const int i = blockIdx.y;
-  const uint64_t sp = a.state_ptrs[i];
+  const uint64_t sp = ((cu64*)a.state_ptrs)[i];
   if (sp == 0) return;
   const int C = a.channels;
-  T* cs = reinterpret_cast<T*>(sp);
+  using GT = __attribute__((address_space(1))) T;
+  GT* cs = (GT*)reinterpret_cast<T*>(sp);
+  typename Vec8<T>::Raw wr[K], sr[K - 1], xr, br;
+#pragma unroll
+  for (int j = 0; j < K; ++j) wr[j] = Vec8<T>::load_raw(static_cast<const T*>(a.w) + static_cast<int64_t>(ch0) * K + j * kVec);
+#pragma unroll
+  for (int r = 0; r < K - 1; ++r) sr[r] = Vec8<T>::load_raw_g(cs + static_cast<int64_t>(r) * C + ch0);
+  xr = Vec8<T>::load_raw(static_cast<const T*>(a.x) + static_cast<int64_t>(i) * a.x_stride + ch0);
+  const bool has_b = a.b != nullptr;
+  br = Vec8<T>::load_raw(static_cast<const T*>(has_b ? a.b : a.w) + ch0);  // (taps as a stand-in when no bias)
   ConvTaps<T, K> taps;
-  taps.load(static_cast<const T*>(a.w), static_cast<const T*>(a.b), ch0);
+  taps.from_raw(wr, br, has_b);
   float win[K - 1][kVec], cur[kVec], out[kVec];
 #pragma unroll
-  for (int r = 0; r < K - 1; ++r) Vec8<T>::load(cs + static_cast<int64_t>(r) * C + ch0, win[r]);
-  Vec8<T>::load(static_cast<const T*>(a.x) + static_cast<int64_t>(i) * a.x_stride + ch0, cur);
+  for (int r = 0; r < K - 1; ++r) Vec8<T>::convert(sr[r], win[r]);
+  Vec8<T>::convert(xr, cur);
   taps.apply(win, cur, a.silu != 0, out);
   Vec8<float>::store(a.y + static_cast<int64_t>(i) * a.y_stride + ch0, out);
 #pragma unroll
-  for (int r = 0; r < K - 2; ++r) Vec8<T>::store(cs + static_cast<int64_t>(r) * C + ch0, win[r + 1]);
-  Vec8<T>::store(cs + static_cast<int64_t>(K - 2) * C + ch0, cur);
+  for (int r = 0; r < K - 2; ++r) Vec8<T>::store_raw_g(cs + static_cast<int64_t>(r) * C + ch0, sr[r + 1]);
+  Vec8<T>::store_raw_g(cs + static_cast<int64_t>(K - 2) * C + ch0, xr);
 }
 
 template <typename T>
@@ -179,11 +226,11 @@ hipError_t launch_all(const ConvArgs& a, hipStream_t s, bool decode) {
   const unsigned gx = (a.channels / kVec + kThreads - 1) / kThreads;
   if (decode) {
     if (a.n == 0) return hipSuccess;
-    dim3 grid(gx, a.n);
+    dim3 grid((a.channels / kVec + kDecThreads - 1) / kDecThreads, a.n);
     switch (a.width) {
-      case 2: conv_decode_kernel<T, 2><<<grid, kThreads, 0, s>>>(a); break;
-      case 3: conv_decode_kernel<T, 3><<<grid, kThreads, 0, s>>>(a); break;
-      default: conv_decode_kernel<T, 4><<<grid, kThreads, 0, s>>>(a); break;
+      case 2: conv_decode_kernel<T, 2><<<grid, kDecThreads, 0, s>>>(a); break;
+      case 3: conv_decode_kernel<T, 3><<<grid, kDecThreads, 0, s>>>(a); break;
+      default: conv_decode_kernel<T, 4><<<grid, kDecThreads, 0, s>>>(a); break;
     }
     return hipGetLastError();
   }

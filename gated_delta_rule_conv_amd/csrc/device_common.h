@@ -30,6 +30,27 @@ struct Vec8;
 
 template <>
 struct Vec8<float> {
+  // raw = the 8 values as loaded (two 16-byte vectors), converted later
+  struct Raw {
+    f32x4 a, b;
+  };
+  typedef __attribute__((address_space(1))) float GT;
+  __device__ __forceinline__ static Raw load_raw(const float* p) {
+    return Raw{reinterpret_cast<const f32x4*>(p)[0], reinterpret_cast<const f32x4*>(p)[1]};
+  }
+  __device__ __forceinline__ static Raw load_raw_g(const GT* p) {
+    typedef __attribute__((address_space(1))) const f32x4 G4;
+    return Raw{((G4*)p)[0], ((G4*)p)[1]};
+  }
+  __device__ __forceinline__ static void store_raw_g(GT* p, const Raw& r) {
+    typedef __attribute__((address_space(1))) f32x4 G4;
+    ((G4*)p)[0] = r.a;
+    ((G4*)p)[1] = r.b;
+  }
+  __device__ __forceinline__ static void convert(const Raw& r, float (&v)[8]) {
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+  }
   __device__ __forceinline__ static void load(const float* p, float (&v)[8]) {
     const float4 a = reinterpret_cast<const float4*>(p)[0];
     const float4 b = reinterpret_cast<const float4*>(p)[1];
@@ -44,6 +65,24 @@ struct Vec8<float> {
 
 template <>
 struct Vec8<uint16_t> {
+  typedef uint32_t Raw __attribute__((ext_vector_type(4)));  // 8 bf16 as loaded
+  typedef __attribute__((address_space(1))) uint16_t GT;
+  __device__ __forceinline__ static Raw load_raw(const uint16_t* p) { return *reinterpret_cast<const Raw*>(p); }
+  __device__ __forceinline__ static Raw load_raw_g(const GT* p) {
+    typedef __attribute__((address_space(1))) const Raw G4;
+    return *(G4*)p;
+  }
+  __device__ __forceinline__ static void store_raw_g(GT* p, const Raw& r) {
+    typedef __attribute__((address_space(1))) Raw G4;
+    *(G4*)p = r;
+  }
+  __device__ __forceinline__ static void convert(const Raw& a, float (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(a[i] << 16);
+      v[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+    }
+  }
   __device__ __forceinline__ static void load(const uint16_t* p, float (&v)[8]) {
     const uint4 a = *reinterpret_cast<const uint4*>(p);
     const uint32_t w[4] = {a.x, a.y, a.z, a.w};

@@ -383,7 +383,7 @@ struct ChunkIn {
   F af[NV];     // K^ (or Q^) row of token 16*tt + l16
   F mf[NK];     // T (or P) row of token 16*tt + l16
   F kt[NK];     // K^T row 16*wave + l16 (this wave's state tile)
-  float vv[4];  // v at the 4 output rows this lane holds (K side)
+  float vv[4];  // v at the 4 output rows this lane holds (K side; rows >= n masked at use)
   float gt[4], bt[4];
   float gn;     // gam of the chunk's last token
   int n;        // tokens in the chunk
@@ -433,8 +433,11 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
   const int kl = KPL * lg;
   const bool qside = wave >= 4;
   const int tt = wave & 3;            // token tile
-  const bool active = tt < NT;
-  const bool has_tile = wave < ST;    // this wave updates state tile `wave`
+  // (both are always true at C = 64, D = 128; writing them so lets the compiler see
+  // straight-line loads, which keeps its wait counts exact and the prefetch alive)
+  const bool active = NT >= 4 || tt < NT;
+  const bool has_tile = ST >= 8 || wave < ST;  // this wave updates state tile `wave`
+  constexpr bool kFullK = C % KSTEP == 0;      // every lane's k-slice of a chunk row is in range
   const int nch = (len + C - 1) / C;
   const int cbase = w.chunk_off[s];
 
@@ -463,22 +466,26 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
       for (int v = 0; v < NV; ++v) in.af[v] = SP::load(arows, C, D, tt * 16 + l16, kl + v * KSTEP);
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        in.mf[kk] = (kk * KSTEP + kl < C) ? SP::load(mrows, C, C, tt * 16 + l16, kk * KSTEP + kl) : SP::zero();
+        in.mf[kk] = (kFullK || kk * KSTEP + kl < C) ? SP::load(mrows, C, C, tt * 16 + l16, kk * KSTEP + kl)
+                                                    : SP::zero();
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int t = tt * 16 + 4 * lg + rr;
         in.gt[rr] = gb[t];
         in.bt[rr] = gb[C + t];
-        in.vv[rr] = (!qside && t < in.n)
-                        ? r.v[static_cast<int64_t>(t0 + t) * r.v_stride + j * D + blk * kDVB + l16]
-                        : 0.f;
+        // a valid row of this sequence, read unconditionally; rows past the chunk's end
+        // are masked where the value is used (using a load in the step that issues it
+        // would wait for every load before it, the prefetch included)
+        const int tc = min(t, in.n - 1);
+        in.vv[rr] = r.v[static_cast<int64_t>(t0 + tc) * r.v_stride + j * D + blk * kDVB + l16];
       }
     }
     if (has_tile) {
       const char* ktp = kq + 2 * static_cast<size_t>(C) * D * 4;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        in.kt[kk] = (kk * KSTEP + kl < C) ? SP::load(ktp, D, C, wave * 16 + l16, kk * KSTEP + kl) : SP::zero();
+        in.kt[kk] = (kFullK || kk * KSTEP + kl < C) ? SP::load(ktp, D, C, wave * 16 + l16, kk * KSTEP + kl)
+                                                    : SP::zero();
     }
   };
 
@@ -493,7 +500,10 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
       if (!qside) {
         float rv[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) rv[rr] = in.bt[rr] * (in.vv[rr] - expf(in.gt[rr]) * acc[rr]);
+        for (int rr = 0; rr < 4; ++rr) {
+          const float vt = (tt * 16 + 4 * lg + rr < in.n) ? in.vv[rr] : 0.f;
+          rv[rr] = in.bt[rr] * (vt - expf(in.gt[rr]) * acc[rr]);
+        }
         SP::store(Rt, kDVB, RLD, l16, tt * 16 + 4 * lg, rv, 4);
       } else {
 #pragma unroll
@@ -507,7 +517,7 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         if (kk * KSTEP < tt * 16 + 16) {
-          const F rf = (kk * KSTEP + kl < C) ? SP::load(Rt, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+          const F rf = (kFullK || kk * KSTEP + kl < C) ? SP::load(Rt, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
           M::mma(uacc, in.mf[kk], rf);
         }
       }
@@ -526,7 +536,7 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         if (kk * KSTEP < tt * 16 + 16) {
-          const F uf = (kk * KSTEP + kl < C) ? SP::load(Ut, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+          const F uf = (kFullK || kk * KSTEP + kl < C) ? SP::load(Ut, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
           M::mma(oacc, in.mf[kk], uf);
         }
       }
@@ -543,7 +553,7 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
       for (int rr = 0; rr < 4; ++rr) acc[rr] = sacc[rr] * egn;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const F ua = (kk * KSTEP + kl < C) ? SP::load(Us, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+        const F ua = (kFullK || kk * KSTEP + kl < C) ? SP::load(Us, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
         M::mma(acc, ua, in.kt[kk]);
       }
       sacc = acc;
@@ -553,14 +563,16 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
     __syncthreads();
   };
 
+  // Two operand buffers, one chunk ahead. The prefetch index is clamped rather than
+  // guarded (the last chunk is simply read twice), so no load sits under a branch.
   In in0, in1;
   load(0, in0);
   __syncthreads();  // Sl filled
   for (int c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) load(c + 1, in1);
+    load(min(c + 1, nch - 1), in1);
     process(c, in0);
     if (c + 1 >= nch) break;
-    if (c + 2 < nch) load(c + 2, in0);
+    load(min(c + 2, nch - 1), in0);
     process(c + 1, in1);
   }
 
