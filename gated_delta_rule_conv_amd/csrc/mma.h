@@ -47,6 +47,13 @@ struct Mma<kPolFP32> {
   __device__ __forceinline__ static void step(f32x4& acc, const float* a, const float* b) {
     mma(acc, frag(a), frag(b));
   }
+  // three independent accumulator chains (summed by total()) instead of one dependent chain
+  __device__ __forceinline__ static void mma3(f32x4 (&acc)[3], const Frag& a, const Frag& b) {
+    acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[0], b.v[0], acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[1], b.v[1], acc[1], 0, 0, 0);
+    acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[2], b.v[2], acc[2], 0, 0, 0);
+    acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[3], b.v[3], acc[0], 0, 0, 0);
+  }
 };
 
 template <>
@@ -77,7 +84,20 @@ struct Mma<kPolBF16X3> {
   __device__ __forceinline__ static void step(f32x4& acc, const float* a, const float* b) {
     mma(acc, frag(a), frag(b));
   }
+  // the three products on three independent accumulator chains (summed by total())
+  __device__ __forceinline__ static void mma3(f32x4 (&acc)[3], const Frag& a, const Frag& b) {
+    acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc[1], 0, 0, 0);
+    acc[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc[2], 0, 0, 0);
+  }
 };
+
+__device__ __forceinline__ void zero3(f32x4 (&acc)[3]) {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+// acc[0] + (acc[1] + acc[2]): the main products plus the two correction chains
+__device__ __forceinline__ f32x4 total(const f32x4 (&acc)[3]) { return acc[0] + (acc[1] + acc[2]); }
 
 // Operand matrices stored "pre-split": for BF16X3 an R x Cc matrix is two bf16 planes
 // (hi, then lo), for FP32 one fp32 plane; both take R*Cc*4 bytes. A fragment is the
@@ -158,6 +178,57 @@ struct Split<kPolBF16X3> {
     hi[(int64_t)rows * cols] = static_cast<__bf16>(x - static_cast<float>(t));
   }
 };
+
+// Operands in fragment order (global workspace). An R x K operand (row r, contraction
+// index k) is cut into 16 x KSTEP fragments; fragment (rt, ks) is a block of BYTES bytes at
+// block index rt * nks + ks. Inside a block, lane l's KPL values (row 16 rt + l % 16, k from
+// ks * KSTEP + KPL * (l / 16)) are 16 contiguous bytes at l * 16 -- for bf16x3 the hi values,
+// with the lo values 1 KiB further on. One load instruction of a wave is then one
+// contiguous KiB, which the gfx950 load path moves about twice as fast as the same bytes
+// gathered as 16 half cache lines.
+template <int POL>
+struct FragIO;
+
+template <>
+struct FragIO<kPolFP32> {
+  using M = Mma<kPolFP32>;
+  static constexpr int BYTES = 1024;
+  __device__ __forceinline__ static M::Frag load(const char* blk, int lane) {
+    const float4 v = *reinterpret_cast<const float4*>(blk + lane * 16);
+    M::Frag f;
+    f.v[0] = v.x; f.v[1] = v.y; f.v[2] = v.z; f.v[3] = v.w;
+    return f;
+  }
+  __device__ __forceinline__ static void store(char* blk, int lane, const float* x) {
+    *reinterpret_cast<float4*>(blk + lane * 16) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+};
+
+template <>
+struct FragIO<kPolBF16X3> {
+  using M = Mma<kPolBF16X3>;
+  static constexpr int BYTES = 2048;
+  __device__ __forceinline__ static M::Frag load(const char* blk, int lane) {
+    M::Frag f;
+    f.hi = *reinterpret_cast<const bf16x8*>(blk + lane * 16);
+    f.lo = *reinterpret_cast<const bf16x8*>(blk + 1024 + lane * 16);
+    return f;
+  }
+  __device__ __forceinline__ static void store(char* blk, int lane, const float* x) {
+    bf16x8 h, l;
+    M::split(x, h, l);
+    *reinterpret_cast<bf16x8*>(blk + lane * 16) = h;
+    *reinterpret_cast<bf16x8*>(blk + 1024 + lane * 16) = l;
+  }
+};
+
+// Block index and lane of the fragment slot holding (row r, k0), k0 a multiple of KPL.
+template <int POL>
+__device__ __forceinline__ void frag_slot(int r, int k0, int nks, int& blk, int& lane) {
+  using M = Mma<POL>;
+  blk = (r / 16) * nks + k0 / M::KSTEP;
+  lane = r % 16 + 16 * ((k0 % M::KSTEP) / M::KPL);
+}
 
 // KPL contiguous floats from p (16-byte aligned): global or LDS.
 template <int KPL>

@@ -43,11 +43,13 @@ constexpr int kDVB = 16;           // state rows per inter-chunk workgroup
 constexpr int kMetaThreads = 1024;
 constexpr int kLptMaxSeqs = 256;   // longest-first ordering only up to this many sequences
 
-// Per-chunk operands the intra-chunk kernel hands to the inter-chunk kernel, stored
-// pre-split for the MFMA policy (see Split<> in mma.h):
-//   per (chunk, k-head): K^ [C][D], Q^ [C][D] (q already scaled), K^T [D][C]
-//   per (chunk, v-head): T [C][C], P [C][C], gam [C] (fp32, padded with gam_{n-1}),
-//                        beta [C] (fp32, padded with 0)
+// Per-chunk operands the intra-chunk kernel hands to the inter-chunk kernel, stored in
+// fragment order for the MFMA policy (FragIO<> in mma.h), zero-padded past the chunk:
+//   per (chunk, k-head): K^ and Q^ (q already scaled) as A operands (rows = tokens,
+//                        k = head dim), then K^ as the B operand of the state update
+//                        (rows = head dim, k = tokens)
+//   per (chunk, v-head): T, then P, as A operands (rows and k = tokens); then gam [C]
+//                        (fp32, padded with gam_{n-1}) and beta [C] (fp32, padded with 0)
 struct Workspace {
   int* n_chunks;
   int4* table;  // (sequence, first token, length, index in sequence)
@@ -55,6 +57,8 @@ struct Workspace {
   int* order;
   char* kq;
   char* tp;
+  int64_t kq_stride;  // bytes per (chunk, k-head)
+  int64_t tp_stride;  // bytes per (chunk, v-head)
 };
 
 inline size_t up256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
@@ -63,14 +67,34 @@ inline size_t max_chunks_of(int chunk, int num_seqs, int total_tokens) {
   return static_cast<size_t>(total_tokens) / chunk + static_cast<size_t>(num_seqs);
 }
 
-__host__ __device__ constexpr size_t kq_bytes(int D, int C) { return 3ull * C * D * 4; }
-__host__ __device__ constexpr size_t tp_bytes(int C) { return 2ull * C * C * 4 + 2ull * C * 4; }
+// fragment counts: NT token tiles, NV k-steps over the head dim, ST head-dim tiles,
+// NK k-steps over the chunk's tokens (padded up to a whole k-step)
+template <int POL>
+struct FragCount {
+  static constexpr int KSTEP = Mma<POL>::KSTEP;
+  static constexpr int BYTES = FragIO<POL>::BYTES;
+  __host__ __device__ static constexpr int nk(int C) { return (C + KSTEP - 1) / KSTEP; }
+  __host__ __device__ static constexpr size_t kq(int D, int C) {
+    return (2ull * (C / 16) * (D / KSTEP) + static_cast<size_t>(D / 16) * nk(C)) * BYTES;
+  }
+  __host__ __device__ static constexpr size_t tp(int C) { return 2ull * (C / 16) * nk(C) * BYTES + 2ull * C * 4; }
+};
+
+// per-chunk strides of the two operand regions: the larger of the two policies' sizes
+inline size_t kq_stride(int D, int C) {
+  const size_t a = FragCount<kPolFP32>::kq(D, C), b = FragCount<kPolBF16X3>::kq(D, C);
+  return a > b ? a : b;
+}
+inline size_t tp_stride(int C) {
+  const size_t a = FragCount<kPolFP32>::tp(C), b = FragCount<kPolBF16X3>::tp(C);
+  return a > b ? a : b;
+}
 
 size_t workspace_bytes(int hk, int hv, int d, int chunk, int num_seqs, int total_tokens) {
   const size_t mc = max_chunks_of(chunk, num_seqs, total_tokens);
   return 256 + up256(mc * sizeof(int4)) + up256((static_cast<size_t>(num_seqs) + 1) * sizeof(int)) +
-         up256(static_cast<size_t>(num_seqs) * sizeof(int) + 4) + up256(mc * hk * kq_bytes(d, chunk)) +
-         up256(mc * hv * tp_bytes(chunk));
+         up256(static_cast<size_t>(num_seqs) * sizeof(int) + 4) + up256(mc * hk * kq_stride(d, chunk)) +
+         up256(mc * hv * tp_stride(chunk));
 }
 
 Workspace carve(void* base, int hk, int hv, int d, int chunk, int num_seqs, int total_tokens) {
@@ -86,8 +110,10 @@ Workspace carve(void* base, int hk, int hv, int d, int chunk, int num_seqs, int 
   w.order = reinterpret_cast<int*>(p);
   p += up256(static_cast<size_t>(num_seqs) * sizeof(int) + 4);
   w.kq = p;
-  p += up256(mc * hk * kq_bytes(d, chunk));
+  p += up256(mc * hk * kq_stride(d, chunk));
   w.tp = p;
+  w.kq_stride = static_cast<int64_t>(kq_stride(d, chunk));
+  w.tp_stride = static_cast<int64_t>(tp_stride(chunk));
   return w;
 }
 
@@ -168,7 +194,6 @@ struct IntraLayout {
 template <int POL, int D, int C>
 __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Workspace w) {
   using M = Mma<POL>;
-  using SP = Split<POL>;
   using Lo = IntraLayout<D, C>;
   constexpr int NB = C / 16;
   constexpr int KP = Lo::KP, CP = Lo::CP;
@@ -226,26 +251,35 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   }
   __syncthreads();
 
-  // 1b. export K^, Q^ (token rows) and K^T (head-dim rows), pre-split
+  // 1b. export K^, Q^ (A operands) and K^ as the update's B operand, in fragment order
   {
-    char* kq = w.kq + (static_cast<int64_t>(chunk) * r.hk + h) * kq_bytes(D, C);
-    for (int e = tid; e < C * D / 8; e += kThreads) {
-      const int t = e / (D / 8), d0 = (e % (D / 8)) * 8;
-      float kx[8], qx[8];
+    using FIO = FragIO<POL>;
+    using FC = FragCount<POL>;
+    constexpr int KPL = M::KPL, NVF = D / M::KSTEP, NKF = FC::nk(C), KPAD = NKF * M::KSTEP;
+    char* kq = w.kq + (static_cast<int64_t>(chunk) * r.hk + h) * w.kq_stride;
+    char* qq = kq + static_cast<size_t>(C / 16) * NVF * FIO::BYTES;
+    char* kt = qq + static_cast<size_t>(C / 16) * NVF * FIO::BYTES;
+    for (int e = tid; e < C * D / KPL; e += kThreads) {
+      const int t = e / (D / KPL), d0 = (e % (D / KPL)) * KPL;
+      float kx[KPL], qx[KPL];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < KPL; ++i) {
         kx[i] = Kh[t][d0 + i];
         qx[i] = Qh[t][d0 + i];
       }
-      SP::store(kq, C, D, t, d0, kx, 8);
-      SP::store(kq + static_cast<size_t>(C) * D * 4, C, D, t, d0, qx, 8);
+      int blk, ln;
+      frag_slot<POL>(t, d0, NVF, blk, ln);
+      FIO::store(kq + static_cast<size_t>(blk) * FIO::BYTES, ln, kx);
+      FIO::store(qq + static_cast<size_t>(blk) * FIO::BYTES, ln, qx);
     }
-    for (int e = tid; e < D * C / 8; e += kThreads) {
-      const int dk = e / (C / 8), s0 = (e % (C / 8)) * 8;
-      float kx[8];
+    for (int e = tid; e < D * KPAD / KPL; e += kThreads) {
+      const int dk = e / (KPAD / KPL), s0 = (e % (KPAD / KPL)) * KPL;
+      float kx[KPL];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kx[i] = Kh[s0 + i][dk];
-      SP::store(kq + 2 * static_cast<size_t>(C) * D * 4, D, C, dk, s0, kx, 8);
+      for (int i = 0; i < KPL; ++i) kx[i] = (s0 + i < C) ? Kh[s0 + i][dk] : 0.f;
+      int blk, ln;
+      frag_slot<POL>(dk, s0, NKF, blk, ln);
+      FIO::store(kt + static_cast<size_t>(blk) * FIO::BYTES, ln, kx);
     }
   }
 
@@ -261,14 +295,16 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
       while ((ti + 1) * (ti + 2) / 2 <= it) ++ti;
       const int tj = it - ti * (ti + 1) / 2;
       const float(*Aop)[KP] = isq ? Qh : Kh;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 a3[3];
+      zero3(a3);
 #pragma unroll
       for (int v = 0; v < D / M::KSTEP; ++v) {
         float av[M::KPL], bv[M::KPL];
         load_k<M::KPL>(&Aop[ti * 16 + l16][kl + v * M::KSTEP], av);
         load_k<M::KPL>(&Kh[tj * 16 + l16][kl + v * M::KSTEP], bv);
-        M::step(acc, av, bv);
+        M::mma3(a3, M::frag(av), M::frag(bv));
       }
+      const f32x4 acc = total(a3);
       float(*Out)[CP] = isq ? QKm : Gm;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) Out[ti * 16 + 4 * (lane >> 4) + rr][tj * 16 + l16] = acc[rr];
@@ -279,8 +315,11 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   // 3. per v-head of this k-head's group: decay mask, A, T = (I + A)^-1, P
   for (int jj = 0; jj < group; ++jj) {
     const int j = h * group + jj;
-    char* tp = w.tp + (static_cast<int64_t>(chunk) * r.hv + j) * tp_bytes(C);
-    float* gam_out = reinterpret_cast<float*>(tp + 2 * static_cast<size_t>(C) * C * 4);
+    using FIO = FragIO<POL>;
+    constexpr int NKF = FragCount<POL>::nk(C), KPAD = NKF * M::KSTEP;
+    char* tp = w.tp + (static_cast<int64_t>(chunk) * r.hv + j) * w.tp_stride;
+    char* pp = tp + static_cast<size_t>(C / 16) * NKF * FIO::BYTES;
+    float* gam_out = reinterpret_cast<float*>(pp + static_cast<size_t>(C / 16) * NKF * FIO::BYTES);
     if (wave == 0) {
       float gv = 0.f, bv = 0.f;
       if (lane < n) {
@@ -297,9 +336,10 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     }
     __syncthreads();
 
-    // A (strictly lower) into LDS, P (lower incl. diagonal) to the workspace
-    for (int e = tid; e < C * C / 8; e += kThreads) {
-      const int t = e / (C / 8), s0 = (e % (C / 8)) * 8;
+    // A (strictly lower) into LDS, P (lower incl. diagonal) to the workspace; the k range
+    // runs to the padded KPAD so the zero padding of the P fragments is written too
+    for (int e = tid; e < C * KPAD / 8; e += kThreads) {
+      const int t = e / (KPAD / 8), s0 = (e % (KPAD / 8)) * 8;
       float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -311,9 +351,14 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
           pv[i] = dec * QKm[t][s];
           if (s < t) av = bet[t] * dec * Gm[t][s];
         }
-        Am[t][s] = av;
+        if (s < C) Am[t][s] = av;
       }
-      SP::store(tp + static_cast<size_t>(C) * C * 4, C, C, t, s0, pv, 8);
+#pragma unroll
+      for (int q = 0; q < 8; q += M::KPL) {
+        int blk, ln;
+        frag_slot<POL>(t, s0 + q, NKF, blk, ln);
+        FIO::store(pp + static_cast<size_t>(blk) * FIO::BYTES, ln, pv + q);
+      }
     }
     __syncthreads();
 
@@ -359,12 +404,17 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
       __syncthreads();
     }
 
-    for (int e = tid; e < C * C / 8; e += kThreads) {
-      const int t = e / (C / 8), s0 = (e % (C / 8)) * 8;
+    for (int e = tid; e < C * KPAD / 8; e += kThreads) {
+      const int t = e / (KPAD / 8), s0 = (e % (KPAD / 8)) * 8;
       float tv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) tv[i] = (s0 + i <= t) ? Tm[t][s0 + i] : 0.f;
-      SP::store(tp, C, C, t, s0, tv, 8);
+#pragma unroll
+      for (int q = 0; q < 8; q += M::KPL) {
+        int blk, ln;
+        frag_slot<POL>(t, s0 + q, NKF, blk, ln);
+        FIO::store(tp + static_cast<size_t>(blk) * FIO::BYTES, ln, tv + q);
+      }
     }
     __syncthreads();
   }
@@ -395,6 +445,7 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
   using SP = Split<POL>;
   using F = typename M::Frag;
   using In = ChunkIn<POL, D, C>;
+  using FIO = FragIO<POL>;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
   constexpr int NBLK = D / kDVB;  // state-row blocks per head
   constexpr int NT = C / 16;      // token tiles per chunk
@@ -455,24 +506,27 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
     const int t0 = start + c * C;
     in.n = min(C, len - c * C);
     const int64_t gc = cbase + c;
-    const char* kq = w.kq + (gc * r.hk + h) * kq_bytes(D, C);
-    const char* tp = w.tp + (gc * r.hv + j) * tp_bytes(C);
-    const float* gb = reinterpret_cast<const float*>(tp + 2 * static_cast<size_t>(C) * C * 4);
+    // every operand fragment is one contiguous KiB per plane (fragment order, zero-padded)
+    const char* kq = w.kq + (gc * r.hk + h) * w.kq_stride;
+    const char* tp = w.tp + (gc * r.hv + j) * w.tp_stride;
+    const float* gb = reinterpret_cast<const float*>(tp + 2 * static_cast<size_t>(NT) * NK * FIO::BYTES);
     in.gn = gb[C - 1];
     if (active) {
-      const char* arows = kq + (qside ? static_cast<size_t>(C) * D * 4 : 0);
-      const char* mrows = tp + (qside ? static_cast<size_t>(C) * C * 4 : 0);
+      const char* arows = kq + (qside ? static_cast<size_t>(NT) * NV * FIO::BYTES : 0);
+      const char* mrows = tp + (qside ? static_cast<size_t>(NT) * NK * FIO::BYTES : 0);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) in.af[v] = SP::load(arows, C, D, tt * 16 + l16, kl + v * KSTEP);
+      for (int v = 0; v < NV; ++v) in.af[v] = FIO::load(arows + static_cast<size_t>(tt * NV + v) * FIO::BYTES, lane);
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        in.mf[kk] = (kFullK || kk * KSTEP + kl < C) ? SP::load(mrows, C, C, tt * 16 + l16, kk * KSTEP + kl)
-                                                    : SP::zero();
+        in.mf[kk] = FIO::load(mrows + static_cast<size_t>(tt * NK + kk) * FIO::BYTES, lane);
+      // gam and beta of this lane's 4 output rows are 4 consecutive floats
+      const float4 g4 = *reinterpret_cast<const float4*>(gb + tt * 16 + 4 * lg);
+      const float4 b4 = *reinterpret_cast<const float4*>(gb + C + tt * 16 + 4 * lg);
+      in.gt[0] = g4.x; in.gt[1] = g4.y; in.gt[2] = g4.z; in.gt[3] = g4.w;
+      in.bt[0] = b4.x; in.bt[1] = b4.y; in.bt[2] = b4.z; in.bt[3] = b4.w;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int t = tt * 16 + 4 * lg + rr;
-        in.gt[rr] = gb[t];
-        in.bt[rr] = gb[C + t];
         // a valid row of this sequence, read unconditionally; rows past the chunk's end
         // are masked where the value is used (using a load in the step that issues it
         // would wait for every load before it, the prefetch included)
@@ -481,11 +535,10 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
       }
     }
     if (has_tile) {
-      const char* ktp = kq + 2 * static_cast<size_t>(C) * D * 4;
+      const char* ktp = kq + 2 * static_cast<size_t>(NT) * NV * FIO::BYTES;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        in.kt[kk] = (kFullK || kk * KSTEP + kl < C) ? SP::load(ktp, D, C, wave * 16 + l16, kk * KSTEP + kl)
-                                                    : SP::zero();
+        in.kt[kk] = FIO::load(ktp + static_cast<size_t>(wave * NK + kk) * FIO::BYTES, lane);
     }
   };
 
@@ -494,9 +547,11 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
     f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
     // phase 1: X = K^ S^T (K side) or Y = Q^ S^T (Q side)
     if (active) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 a3[3];
+      zero3(a3);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) M::mma(acc, in.af[v], SP::load(Sl, kDVB, SLD, l16, kl + v * KSTEP));
+      for (int v = 0; v < NV; ++v) M::mma3(a3, in.af[v], SP::load(Sl, kDVB, SLD, l16, kl + v * KSTEP));
+      const f32x4 acc = total(a3);
       if (!qside) {
         float rv[4];
 #pragma unroll
@@ -513,14 +568,16 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
     __syncthreads();
     // phase 2 (K side): U = T R, T lower triangular
     if (active && !qside) {
-      f32x4 uacc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 u3[3];
+      zero3(u3);
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         if (kk * KSTEP < tt * 16 + 16) {
           const F rf = (kFullK || kk * KSTEP + kl < C) ? SP::load(Rt, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
-          M::mma(uacc, in.mf[kk], rf);
+          M::mma3(u3, in.mf[kk], rf);
         }
       }
+      const f32x4 uacc = total(u3);
       float ut[4], us[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -533,13 +590,16 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
     __syncthreads();
     // phase 3: O = e^gam Y + P U (Q side); S <- e^{gam_n} S + Us^T K^ (state tiles)
     if (active && qside) {
+      f32x4 o3[3];
+      zero3(o3);
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         if (kk * KSTEP < tt * 16 + 16) {
           const F uf = (kFullK || kk * KSTEP + kl < C) ? SP::load(Ut, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
-          M::mma(oacc, in.mf[kk], uf);
+          M::mma3(o3, in.mf[kk], uf);
         }
       }
+      oacc += total(o3);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int t = tt * 16 + 4 * lg + rr;
@@ -548,14 +608,17 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
     }
     if (has_tile) {
       const float egn = expf(in.gn);
-      f32x4 acc;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) acc[rr] = sacc[rr] * egn;
+      f32x4 s3[3];
+      zero3(s3);
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         const F ua = (kFullK || kk * KSTEP + kl < C) ? SP::load(Us, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
-        M::mma(acc, ua, in.kt[kk]);
+        M::mma3(s3, ua, in.kt[kk]);
       }
+      const f32x4 upd = total(s3);
+      f32x4 acc;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sacc[rr], egn, upd[rr]);
       sacc = acc;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) SP::store1(Sl, kDVB, SLD, 4 * lg + rr, wave * 16 + l16, acc[rr]);
