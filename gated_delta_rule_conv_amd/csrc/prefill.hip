@@ -36,8 +36,8 @@
 namespace gdn {
 namespace {
 
-constexpr int kThreads = 256;      // intra-chunk workgroup
-constexpr int kWaves = 4;
+constexpr int kThreads = 512;      // intra-chunk workgroup: 8 waves
+constexpr int kWaves = 8;
 constexpr int kInterThreads = 512; // inter-chunk workgroup: 8 waves
 constexpr int kDVB = 16;           // state rows per inter-chunk workgroup
 constexpr int kMetaThreads = 1024;
@@ -194,15 +194,19 @@ struct IntraLayout {
 template <int POL, int D, int C>
 __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Workspace w) {
   using M = Mma<POL>;
+  using FIO = FragIO<POL>;
   using Lo = IntraLayout<D, C>;
+  using F32 = Mma<kPolFP32>;
   constexpr int NB = C / 16;
   constexpr int KP = Lo::KP, CP = Lo::CP;
+  constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
+  constexpr int NVF = D / KSTEP;              // k-steps over the head dim
+  constexpr int NKF = FragCount<POL>::nk(C);  // k-steps over the chunk (padded)
   __shared__ __attribute__((aligned(16))) float smem[Lo::TOTAL];
   float(*Kh)[KP] = reinterpret_cast<float(*)[KP]>(smem);
   float(*Qh)[KP] = reinterpret_cast<float(*)[KP]>(smem + C * KP);
   float(*Am)[CP] = reinterpret_cast<float(*)[CP]>(smem);
   float(*Tm)[CP] = reinterpret_cast<float(*)[CP]>(smem + C * CP);
-  float(*Wm)[16][20] = reinterpret_cast<float(*)[16][20]>(smem + 2 * C * CP);
   float(*Gm)[CP] = reinterpret_cast<float(*)[CP]>(smem + Lo::OFF_G);
   float(*QKm)[CP] = reinterpret_cast<float(*)[CP]>(smem + Lo::OFF_QK);
   float* gam = smem + Lo::OFF_GAM;
@@ -215,10 +219,11 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   const int t0 = ent.y, n = ent.z;
   const RecurArgs& r = a.r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
   const int group = r.hv / r.hk;
 
   // 1. normalised K and Q rows of the chunk into LDS; rows >= n are zero
-  constexpr int TPR = 4;
+  constexpr int TPR = 8;
   constexpr int EPT = D / TPR;
   for (int row = tid / TPR; row < C; row += kThreads / TPR) {
     const int part = tid % TPR;
@@ -237,8 +242,8 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
       kk = fmaf(kv[e], kv[e], kk);
       qq = fmaf(qv[e], qv[e], qq);
     }
-    kk = group_sum<4>(kk);
-    qq = group_sum<4>(qq);
+    kk = group_sum<TPR>(kk);
+    qq = group_sum<TPR>(qq);
     const float rk = live ? 1.0f / sqrtf(kk + r.eps) : 0.f;
     const float rq = live ? r.scale / sqrtf(qq + r.eps) : 0.f;
 #pragma unroll
@@ -251,34 +256,31 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   }
   __syncthreads();
 
-  // 1b. export K^, Q^ (A operands) and K^ as the update's B operand, in fragment order
+  // 1b. export K^, Q^ (A operands) and K^ as the update's B operand, in fragment order.
+  // Thread e writes lane e % 64 of fragment block e / 64, so each wave stores whole
+  // contiguous KiBs.
   {
-    using FIO = FragIO<POL>;
-    using FC = FragCount<POL>;
-    constexpr int KPL = M::KPL, NVF = D / M::KSTEP, NKF = FC::nk(C), KPAD = NKF * M::KSTEP;
     char* kq = w.kq + (static_cast<int64_t>(chunk) * r.hk + h) * w.kq_stride;
     char* qq = kq + static_cast<size_t>(C / 16) * NVF * FIO::BYTES;
     char* kt = qq + static_cast<size_t>(C / 16) * NVF * FIO::BYTES;
-    for (int e = tid; e < C * D / KPL; e += kThreads) {
-      const int t = e / (D / KPL), d0 = (e % (D / KPL)) * KPL;
+    for (int e = tid; e < (C / 16) * NVF * 64; e += kThreads) {
+      const int blk = e / 64, ln = e % 64;
+      const int t = (blk / NVF) * 16 + ln % 16, d0 = (blk % NVF) * KSTEP + KPL * (ln / 16);
       float kx[KPL], qx[KPL];
 #pragma unroll
       for (int i = 0; i < KPL; ++i) {
         kx[i] = Kh[t][d0 + i];
         qx[i] = Qh[t][d0 + i];
       }
-      int blk, ln;
-      frag_slot<POL>(t, d0, NVF, blk, ln);
       FIO::store(kq + static_cast<size_t>(blk) * FIO::BYTES, ln, kx);
       FIO::store(qq + static_cast<size_t>(blk) * FIO::BYTES, ln, qx);
     }
-    for (int e = tid; e < D * KPAD / KPL; e += kThreads) {
-      const int dk = e / (KPAD / KPL), s0 = (e % (KPAD / KPL)) * KPL;
+    for (int e = tid; e < (D / 16) * NKF * 64; e += kThreads) {
+      const int blk = e / 64, ln = e % 64;
+      const int dk = (blk / NKF) * 16 + ln % 16, s0 = (blk % NKF) * KSTEP + KPL * (ln / 16);
       float kx[KPL];
 #pragma unroll
       for (int i = 0; i < KPL; ++i) kx[i] = (s0 + i < C) ? Kh[s0 + i][dk] : 0.f;
-      int blk, ln;
-      frag_slot<POL>(dk, s0, NKF, blk, ln);
       FIO::store(kt + static_cast<size_t>(blk) * FIO::BYTES, ln, kx);
     }
   }
@@ -286,8 +288,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   // 2. G = K^ K^T and QK = Q^ K^T on the lower-triangular 16x16 tiles
   {
     constexpr int NT = NB * (NB + 1) / 2;
-    const int l16 = lane & 15;
-    const int kl = M::KPL * (lane >> 4);
+    const int kl = KPL * lg;
     for (int item = wave; item < 2 * NT; item += kWaves) {
       const bool isq = item >= NT;
       const int it = isq ? item - NT : item;
@@ -298,16 +299,16 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
       f32x4 a3[3];
       zero3(a3);
 #pragma unroll
-      for (int v = 0; v < D / M::KSTEP; ++v) {
-        float av[M::KPL], bv[M::KPL];
-        load_k<M::KPL>(&Aop[ti * 16 + l16][kl + v * M::KSTEP], av);
-        load_k<M::KPL>(&Kh[tj * 16 + l16][kl + v * M::KSTEP], bv);
+      for (int v = 0; v < NVF; ++v) {
+        float av[KPL], bv[KPL];
+        load_k<KPL>(&Aop[ti * 16 + l16][kl + v * KSTEP], av);
+        load_k<KPL>(&Kh[tj * 16 + l16][kl + v * KSTEP], bv);
         M::mma3(a3, M::frag(av), M::frag(bv));
       }
       const f32x4 acc = total(a3);
       float(*Out)[CP] = isq ? QKm : Gm;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) Out[ti * 16 + 4 * (lane >> 4) + rr][tj * 16 + l16] = acc[rr];
+      for (int rr = 0; rr < 4; ++rr) Out[ti * 16 + 4 * lg + rr][tj * 16 + l16] = acc[rr];
     }
   }
   __syncthreads();
@@ -315,8 +316,6 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   // 3. per v-head of this k-head's group: decay mask, A, T = (I + A)^-1, P
   for (int jj = 0; jj < group; ++jj) {
     const int j = h * group + jj;
-    using FIO = FragIO<POL>;
-    constexpr int NKF = FragCount<POL>::nk(C), KPAD = NKF * M::KSTEP;
     char* tp = w.tp + (static_cast<int64_t>(chunk) * r.hv + j) * w.tp_stride;
     char* pp = tp + static_cast<size_t>(C / 16) * NKF * FIO::BYTES;
     float* gam_out = reinterpret_cast<float*>(pp + static_cast<size_t>(C / 16) * NKF * FIO::BYTES);
@@ -336,13 +335,15 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     }
     __syncthreads();
 
-    // A (strictly lower) into LDS, P (lower incl. diagonal) to the workspace; the k range
-    // runs to the padded KPAD so the zero padding of the P fragments is written too
-    for (int e = tid; e < C * KPAD / 8; e += kThreads) {
-      const int t = e / (KPAD / 8), s0 = (e % (KPAD / 8)) * 8;
-      float pv[8];
+    // A (strictly lower) into LDS and P (lower incl. diagonal) to the workspace, one
+    // fragment lane per thread; the k range runs to the padded NKF * KSTEP so the zero
+    // padding of the P fragments is written too
+    for (int e = tid; e < (C / 16) * NKF * 64; e += kThreads) {
+      const int blk = e / 64, ln = e % 64;
+      const int t = (blk / NKF) * 16 + ln % 16, s0 = (blk % NKF) * KSTEP + KPL * (ln / 16);
+      float pv[KPL];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < KPL; ++i) {
         const int s = s0 + i;
         float av = 0.f;
         pv[i] = 0.f;
@@ -353,12 +354,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
         }
         if (s < C) Am[t][s] = av;
       }
-#pragma unroll
-      for (int q = 0; q < 8; q += M::KPL) {
-        int blk, ln;
-        frag_slot<POL>(t, s0 + q, NKF, blk, ln);
-        FIO::store(pp + static_cast<size_t>(blk) * FIO::BYTES, ln, pv + q);
-      }
+      FIO::store(pp + static_cast<size_t>(blk) * FIO::BYTES, ln, pv);
     }
     __syncthreads();
 
@@ -380,41 +376,43 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     }
     __syncthreads();
 
-    // off-diagonal blocks by distance from the diagonal: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+    // off-diagonal blocks by distance from the diagonal, one wave per block, on fp32 MFMA:
+    //   Wb = sum_{k=jb}^{ib-1} A_{ib,k} T_{k,jb},   T_{ib,jb} = -T_{ib,ib} Wb.
+    // Wb's accumulator layout (lane l: rows 4(l/16)+r, column l%16) is exactly the B
+    // operand layout of the second product, so it feeds it without a round trip.
     for (int dd = 1; dd < NB; ++dd) {
-      const int nblk = NB - dd;
-      for (int e = tid; e < nblk * 256; e += kThreads) {
-        const int jb = e / 256, rr = (e / 16) % 16, cc = e % 16;
+      for (int jb = wave; jb < NB - dd; jb += kWaves) {
         const int ib = jb + dd;
-        float acc = 0.f;
-        for (int kb = jb; kb < ib; ++kb)
+        f32x4 wacc = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = jb; kb < ib; ++kb) {
+          // one 16-deep step: lane l supplies k = 4(l/16) + e, e = 0..3
+          F32::Frag fa, fb;
+          const float4 av = *reinterpret_cast<const float4*>(&Am[ib * 16 + l16][kb * 16 + 4 * lg]);
+          fa.v[0] = av.x; fa.v[1] = av.y; fa.v[2] = av.z; fa.v[3] = av.w;
 #pragma unroll
-          for (int m = 0; m < 16; ++m) acc = fmaf(Am[ib * 16 + rr][kb * 16 + m], Tm[kb * 16 + m][jb * 16 + cc], acc);
-        Wm[jb][rr][cc] = acc;
-      }
-      __syncthreads();
-      for (int e = tid; e < nblk * 256; e += kThreads) {
-        const int jb = e / 256, rr = (e / 16) % 16, cc = e % 16;
-        const int ib = jb + dd;
-        float acc = 0.f;
+          for (int e2 = 0; e2 < 4; ++e2) fb.v[e2] = Tm[kb * 16 + 4 * lg + e2][jb * 16 + l16];
+          F32::mma(wacc, fa, fb);
+        }
+        F32::Frag ta, tb;
+        const float4 tv = *reinterpret_cast<const float4*>(&Tm[ib * 16 + l16][ib * 16 + 4 * lg]);
+        ta.v[0] = tv.x; ta.v[1] = tv.y; ta.v[2] = tv.z; ta.v[3] = tv.w;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) acc = fmaf(Tm[ib * 16 + rr][ib * 16 + m], Wm[jb][m][cc], acc);
-        Tm[ib * 16 + rr][jb * 16 + cc] = -acc;
+        for (int e2 = 0; e2 < 4; ++e2) tb.v[e2] = wacc[e2];
+        f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
+        F32::mma(tacc, ta, tb);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) Tm[ib * 16 + 4 * lg + rr][jb * 16 + l16] = -tacc[rr];
       }
       __syncthreads();
     }
 
-    for (int e = tid; e < C * KPAD / 8; e += kThreads) {
-      const int t = e / (KPAD / 8), s0 = (e % (KPAD / 8)) * 8;
-      float tv[8];
+    for (int e = tid; e < (C / 16) * NKF * 64; e += kThreads) {
+      const int blk = e / 64, ln = e % 64;
+      const int t = (blk / NKF) * 16 + ln % 16, s0 = (blk % NKF) * KSTEP + KPL * (ln / 16);
+      float tv[KPL];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) tv[i] = (s0 + i <= t) ? Tm[t][s0 + i] : 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; q += M::KPL) {
-        int blk, ln;
-        frag_slot<POL>(t, s0 + q, NKF, blk, ln);
-        FIO::store(tp + static_cast<size_t>(blk) * FIO::BYTES, ln, tv + q);
-      }
+      for (int i = 0; i < KPL; ++i) tv[i] = (s0 + i <= t) ? Tm[t][s0 + i] : 0.f;
+      FIO::store(tp + static_cast<size_t>(blk) * FIO::BYTES, ln, tv);
     }
     __syncthreads();
   }
