@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     gdn_last_error,
     gdn_prefill_chunked,
     gdn_prefill_workspace_size,
+    gdn_slot_copy,
     gdn_slot_pointers,
     make_dims,
 )

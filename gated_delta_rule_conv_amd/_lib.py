@@ -23,7 +23,7 @@ GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 GDN_MMA_AUTO, GDN_MMA_FP32, GDN_MMA_BF16X3 = 0, 1, 2
 
 EXPORTED = ("gdn_conv_update", "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_decode_batched",
-            "gdn_slot_pointers", "gdn_last_error", "gdn_abi_version")
+            "gdn_slot_copy", "gdn_slot_pointers", "gdn_last_error", "gdn_abi_version")
 
 
 class gdn_dims(ctypes.Structure):
@@ -85,9 +85,10 @@ def _load() -> ctypes.CDLL:
     lib.gdn_prefill_workspace_size.argtypes = [D, I32, I32, ctypes.POINTER(SZ)]
     lib.gdn_prefill_chunked.argtypes = [D, P, I64, P, I64, P, I64, P, P, P, P, I32, I32, P, P, SZ, P]
     lib.gdn_decode_batched.argtypes = [D, P, I64, P, I64, P, I64, P, P, P, P, I32, P]
+    lib.gdn_slot_copy.argtypes = [D, P, P, P, P, I32, P]
     lib.gdn_slot_pointers.argtypes = [U64, I64, I32, P, I32, P, P]
     for fn in ("gdn_conv_update", "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_decode_batched",
-               "gdn_slot_pointers"):
+               "gdn_slot_copy", "gdn_slot_pointers"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.gdn_last_error.argtypes = []
     lib.gdn_last_error.restype = ctypes.c_char_p
@@ -166,6 +167,14 @@ def gdn_decode_batched(dims: gdn_dims, q, q_stride: int, k, k_stride: int, v, v_
     st = _LIB.gdn_decode_batched(ctypes.byref(dims), _ptr(q), q_stride, _ptr(k), k_stride, _ptr(v), v_stride,
                                  _ptr(g), _ptr(beta), _ptr(o), _ptr(state_ptrs), m, _stream(stream, q, o, state_ptrs))
     _check("gdn_decode_batched", st)
+
+
+def gdn_slot_copy(dims: gdn_dims, src_state_ptrs, dst_state_ptrs, src_conv_ptrs, dst_conv_ptrs, n: int,
+                  stream=None) -> None:
+    st = _LIB.gdn_slot_copy(ctypes.byref(dims), _ptr(src_state_ptrs), _ptr(dst_state_ptrs), _ptr(src_conv_ptrs),
+                            _ptr(dst_conv_ptrs), n,
+                            _stream(stream, src_state_ptrs, dst_state_ptrs, src_conv_ptrs, dst_conv_ptrs))
+    _check("gdn_slot_copy", st)
 
 
 def gdn_slot_pointers(pool_base: int, slot_bytes: int, pool_slots: int, slot_idx, m: int, out_ptrs,

@@ -186,6 +186,43 @@ __global__ void slot_pointers_kernel(uint64_t base, int64_t slot_bytes, int32_t 
 }
 }  // namespace
 
+// Slot copy: blockIdx.y = slot pair, each workgroup streams 16 KiB (256 threads x 4 x 16 B)
+// of the slot's bytes with nontemporal 16-byte loads and stores.
+namespace {
+constexpr int kCopyThreads = 256;
+constexpr int kCopyVecs = 4;  // 16-byte vectors per thread
+__global__ __launch_bounds__(kCopyThreads) void slot_copy_kernel(const uint64_t* src, const uint64_t* dst,
+                                                                 int64_t vecs) {
+  const int i = blockIdx.y;
+  const uint64_t sp = ((cu64*)src)[i];
+  const uint64_t dp = ((cu64*)dst)[i];
+  if (sp == 0 || dp == 0) return;
+  const gf32x4* a = (const gf32x4*)reinterpret_cast<const float*>(sp);
+  gf32x4* b = (gf32x4*)reinterpret_cast<float*>(dp);
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyThreads * kCopyVecs + threadIdx.x;
+  f32x4 v[kCopyVecs];
+#pragma unroll
+  for (int e = 0; e < kCopyVecs; ++e) {
+    const int64_t k = base + e * kCopyThreads;
+    if (k < vecs) v[e] = __builtin_nontemporal_load(a + k);
+  }
+#pragma unroll
+  for (int e = 0; e < kCopyVecs; ++e) {
+    const int64_t k = base + e * kCopyThreads;
+    if (k < vecs) __builtin_nontemporal_store(v[e], b + k);
+  }
+}
+}  // namespace
+
+hipError_t launch_slot_copy(const uint64_t* src, const uint64_t* dst, int64_t bytes, int32_t n, hipStream_t s) {
+  if (n == 0 || bytes == 0) return hipSuccess;
+  const int64_t vecs = bytes / 16;
+  const int64_t per_block = static_cast<int64_t>(kCopyThreads) * kCopyVecs;
+  const dim3 grid(static_cast<unsigned>((vecs + per_block - 1) / per_block), static_cast<unsigned>(n));
+  slot_copy_kernel<<<grid, kCopyThreads, 0, s>>>(src, dst, vecs);
+  return hipGetLastError();
+}
+
 hipError_t launch_slot_pointers(uint64_t base, int64_t slot_bytes, int32_t pool_slots, const int32_t* idx,
                                 int32_t m, uint64_t* out, hipStream_t s) {
   if (m == 0) return hipSuccess;

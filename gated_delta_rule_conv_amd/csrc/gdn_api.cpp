@@ -191,6 +191,30 @@ gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_st
   return hip_status(gdn::launch_decode(a, m, static_cast<hipStream_t>(stream)), fn);
 }
 
+gdn_status gdn_slot_copy(const gdn_dims* dims, const uint64_t* src_state_ptrs, const uint64_t* dst_state_ptrs,
+                         const uint64_t* src_conv_ptrs, const uint64_t* dst_conv_ptrs, int32_t n, void* stream) {
+  const char* fn = "gdn_slot_copy";
+  if (gdn_status st = check_dims(dims, fn)) return st;
+  if (n < 0) return fail(GDN_ERR_SHAPE, "%s: negative n", fn);
+  if ((src_state_ptrs == nullptr) != (dst_state_ptrs == nullptr) ||
+      (src_conv_ptrs == nullptr) != (dst_conv_ptrs == nullptr))
+    return fail(GDN_ERR_NULL, "%s: source and destination pointer arrays come in pairs (both or neither)", fn);
+  if (n == 0) return GDN_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t d = dims->head_dim;
+  const int64_t channels = d * (2 * static_cast<int64_t>(dims->num_k_heads) + dims->num_v_heads);
+  if (src_state_ptrs) {
+    const int64_t bytes = static_cast<int64_t>(dims->num_v_heads) * d * d * 4;
+    if (gdn_status st = hip_status(gdn::launch_slot_copy(src_state_ptrs, dst_state_ptrs, bytes, n, s), fn)) return st;
+  }
+  if (src_conv_ptrs) {
+    const int64_t elt = dims->in_dtype == GDN_BF16 ? 2 : 4;
+    const int64_t bytes = (dims->conv_width - 1) * channels * elt;
+    if (gdn_status st = hip_status(gdn::launch_slot_copy(src_conv_ptrs, dst_conv_ptrs, bytes, n, s), fn)) return st;
+  }
+  return GDN_OK;
+}
+
 gdn_status gdn_slot_pointers(uint64_t pool_base, int64_t slot_bytes, int32_t pool_slots, const int32_t* slot_idx,
                              int32_t m, uint64_t* out_ptrs, void* stream) {
   const char* fn = "gdn_slot_pointers";

@@ -62,6 +62,8 @@ size_t prefill_workspace_bytes(int32_t hk, int32_t hv, int32_t d, int32_t chunk,
                                int32_t total_tokens);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
+hipError_t launch_slot_copy(const uint64_t* src, const uint64_t* dst, int64_t bytes, int32_t n, hipStream_t s);
+
 hipError_t launch_slot_pointers(uint64_t base, int64_t slot_bytes, int32_t pool_slots, const int32_t* idx,
                                 int32_t m, uint64_t* out, hipStream_t s);
 

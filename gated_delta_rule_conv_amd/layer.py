@@ -61,6 +61,19 @@ class SlotPool:
         return sp, cp
 
 
+    def copy_slots(self, src_idx: torch.Tensor, dst_idx: torch.Tensor, state: bool = True,
+                   conv_state: bool = True, stream=None) -> None:
+        """Snapshot / fork: slot dst_idx[i] takes the state and conv state of slot src_idx[i]
+        (int32 device index tensors of equal length; destinations distinct from each other
+        and from every source)."""
+        assert src_idx.numel() == dst_idx.numel()
+        n = src_idx.numel()
+        ss, sc = self.pointers(src_idx)
+        ds, dc = self.pointers(dst_idx)
+        _lib.gdn_slot_copy(self.dims, ss if state else None, ds if state else None, sc if conv_state else None,
+                           dc if conv_state else None, n, stream)
+
+
 def qkv_views(dims: gdn_dims, y: torch.Tensor):
     """q, k, v views of the conv output y [T, C] (channels [q | k | v])."""
     hk = dims.num_k_heads * dims.head_dim

@@ -189,6 +189,25 @@ gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_st
 gdn_status gdn_slot_pointers(uint64_t pool_base, int64_t slot_bytes, int32_t pool_slots,
                              const int32_t* slot_idx, int32_t m, uint64_t* out_ptrs, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * gdn_slot_copy -- snapshot / fork of slots: for i < n, copy the recurrent state at
+ * src_state_ptrs[i] to dst_state_ptrs[i] (Hv*d*d fp32 each) and the conv state at
+ * src_conv_ptrs[i] to dst_conv_ptrs[i] ((K-1)*C in_dtype each), in one launch per kind.
+ * A sequence prefix run once can then seed any number of slots, and a slot can be
+ * checkpointed and restored, since the fixed-size state is all the history the layer
+ * keeps ("qLLM", "What's still open": prefix caching is off because recurrent state
+ * cannot be rebuilt from a cached prefix; aprender #5279, "Where concurrency is lost",
+ * item 6, and "Phase plan", P7: per-slot prefix reuse and checkpoints).
+ *
+ *  src_state_ptrs, dst_state_ptrs  device u64 [n], or both NULL (no state copied).
+ *  src_conv_ptrs,  dst_conv_ptrs   device u64 [n], or both NULL (no conv state copied).
+ *  An entry whose source or destination is 0 is skipped. All addresses 16-byte aligned.
+ *  Unchecked precondition: destination slots are distinct from one another and from
+ *  every source (one source may feed several destinations).
+ */
+gdn_status gdn_slot_copy(const gdn_dims* dims, const uint64_t* src_state_ptrs, const uint64_t* dst_state_ptrs,
+                         const uint64_t* src_conv_ptrs, const uint64_t* dst_conv_ptrs, int32_t n, void* stream);
+
 /* Thread-local text describing the last non-OK status returned on this thread. */
 const char* gdn_last_error(void);
 

@@ -168,3 +168,14 @@ def test_library_shares_torchs_hip_runtime():
     import torch
 
     assert os.path.dirname(next(iter(runtimes))) == os.path.join(os.path.dirname(torch.__file__), "lib")
+
+
+def test_slot_copy_checks():
+    dims = gdn.make_dims(16, 32, 128)
+    # pointer arrays come in (source, destination) pairs
+    assert _status(gdn.gdn_slot_copy, dims, FAKE, None, None, None, 4)[0] == _lib.GDN_ERR_NULL
+    assert _status(gdn.gdn_slot_copy, dims, None, None, None, FAKE, 4)[0] == _lib.GDN_ERR_NULL
+    assert _status(gdn.gdn_slot_copy, dims, FAKE, FAKE, None, None, -1)[0] == _lib.GDN_ERR_SHAPE
+    bad = gdn.make_dims(16, 30, 128)  # Hv % Hk != 0
+    assert _status(gdn.gdn_slot_copy, bad, FAKE, FAKE, None, None, 4)[0] == _lib.GDN_ERR_SHAPE
+    gdn.gdn_slot_copy(dims, FAKE, FAKE, FAKE, FAKE, 0)  # n = 0: nothing to do, nothing launched
