@@ -177,16 +177,21 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
 }
 
 // ------------------------------------------------------------------------ intra-chunk
+// LDS of the intra-chunk kernel, in floats. K^ and Q^ live only until K K^T and Q K^T are
+// in registers; then G and QK take K^'s place and A and T take Q^'s, so the peak is two
+// C x (D+4) areas (70 KB at C = 64, D = 128) and two workgroups fit on a CU.
 template <int D, int C>
 struct IntraLayout {
   static constexpr int KP = D + 4;  // padded row of K^/Q^
   static constexpr int CP = C + 4;  // padded row of C x C matrices
-  static constexpr int R1_A = 2 * C * KP;
-  static constexpr int R1_B = 2 * C * CP + 3 * 16 * 20;
-  static constexpr int R1 = R1_A > R1_B ? R1_A : R1_B;  // K^, Q^  alias  A, T, W
-  static constexpr int OFF_G = R1;
-  static constexpr int OFF_QK = OFF_G + C * CP;
-  static constexpr int OFF_GAM = OFF_QK + C * CP;
+  static constexpr int RS = (C * KP > 2 * C * CP) ? C * KP : 2 * C * CP;  // one area
+  static constexpr int OFF_K = 0;        // K^   alias  G, QK
+  static constexpr int OFF_G = 0;
+  static constexpr int OFF_QK = C * CP;
+  static constexpr int OFF_Q = RS;       // Q^   alias  A, T
+  static constexpr int OFF_A = RS;
+  static constexpr int OFF_T = RS + C * CP;
+  static constexpr int OFF_GAM = 2 * RS;
   static constexpr int OFF_BET = OFF_GAM + C;
   static constexpr int TOTAL = OFF_BET + C;
 };
@@ -203,10 +208,10 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   constexpr int NVF = D / KSTEP;              // k-steps over the head dim
   constexpr int NKF = FragCount<POL>::nk(C);  // k-steps over the chunk (padded)
   __shared__ __attribute__((aligned(16))) float smem[Lo::TOTAL];
-  float(*Kh)[KP] = reinterpret_cast<float(*)[KP]>(smem);
-  float(*Qh)[KP] = reinterpret_cast<float(*)[KP]>(smem + C * KP);
-  float(*Am)[CP] = reinterpret_cast<float(*)[CP]>(smem);
-  float(*Tm)[CP] = reinterpret_cast<float(*)[CP]>(smem + C * CP);
+  float(*Kh)[KP] = reinterpret_cast<float(*)[KP]>(smem + Lo::OFF_K);
+  float(*Qh)[KP] = reinterpret_cast<float(*)[KP]>(smem + Lo::OFF_Q);
+  float(*Am)[CP] = reinterpret_cast<float(*)[CP]>(smem + Lo::OFF_A);
+  float(*Tm)[CP] = reinterpret_cast<float(*)[CP]>(smem + Lo::OFF_T);
   float(*Gm)[CP] = reinterpret_cast<float(*)[CP]>(smem + Lo::OFF_G);
   float(*QKm)[CP] = reinterpret_cast<float(*)[CP]>(smem + Lo::OFF_QK);
   float* gam = smem + Lo::OFF_GAM;
@@ -285,30 +290,49 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     }
   }
 
-  // 2. G = K^ K^T and QK = Q^ K^T on the lower-triangular 16x16 tiles
+  // 2. G = K^ K^T and QK = Q^ K^T on the lower-triangular 16x16 tiles, held in registers
+  // until every wave is done reading K^ and Q^, then written over them
   {
     constexpr int NT = NB * (NB + 1) / 2;
+    constexpr int MAXI = (2 * NT + kWaves - 1) / kWaves;  // tiles per wave
     const int kl = KPL * lg;
-    for (int item = wave; item < 2 * NT; item += kWaves) {
-      const bool isq = item >= NT;
-      const int it = isq ? item - NT : item;
-      int ti = 0;
-      while ((ti + 1) * (ti + 2) / 2 <= it) ++ti;
-      const int tj = it - ti * (ti + 1) / 2;
-      const float(*Aop)[KP] = isq ? Qh : Kh;
-      f32x4 a3[3];
-      zero3(a3);
+    f32x4 res[MAXI];
 #pragma unroll
-      for (int v = 0; v < NVF; ++v) {
-        float av[KPL], bv[KPL];
-        load_k<KPL>(&Aop[ti * 16 + l16][kl + v * KSTEP], av);
-        load_k<KPL>(&Kh[tj * 16 + l16][kl + v * KSTEP], bv);
-        M::mma3(a3, M::frag(av), M::frag(bv));
+    for (int q = 0; q < MAXI; ++q) {
+      const int item = wave + q * kWaves;
+      if (item < 2 * NT) {
+        const bool isq = item >= NT;
+        const int it = isq ? item - NT : item;
+        int ti = 0;
+        while ((ti + 1) * (ti + 2) / 2 <= it) ++ti;
+        const int tj = it - ti * (ti + 1) / 2;
+        const float(*Aop)[KP] = isq ? Qh : Kh;
+        f32x4 a3[3];
+        zero3(a3);
+#pragma unroll
+        for (int v = 0; v < NVF; ++v) {
+          float av[KPL], bv[KPL];
+          load_k<KPL>(&Aop[ti * 16 + l16][kl + v * KSTEP], av);
+          load_k<KPL>(&Kh[tj * 16 + l16][kl + v * KSTEP], bv);
+          M::mma3(a3, M::frag(av), M::frag(bv));
+        }
+        res[q] = total(a3);
       }
-      const f32x4 acc = total(a3);
-      float(*Out)[CP] = isq ? QKm : Gm;
+    }
+    __syncthreads();  // K^ and Q^ are dead
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) Out[ti * 16 + 4 * lg + rr][tj * 16 + l16] = acc[rr];
+    for (int q = 0; q < MAXI; ++q) {
+      const int item = wave + q * kWaves;
+      if (item < 2 * NT) {
+        const bool isq = item >= NT;
+        const int it = isq ? item - NT : item;
+        int ti = 0;
+        while ((ti + 1) * (ti + 2) / 2 <= it) ++ti;
+        const int tj = it - ti * (ti + 1) / 2;
+        float(*Out)[CP] = isq ? QKm : Gm;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) Out[ti * 16 + 4 * lg + rr][tj * 16 + l16] = res[q][rr];
+      }
     }
   }
   __syncthreads();
