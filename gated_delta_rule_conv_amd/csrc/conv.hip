@@ -22,7 +22,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kDecThreads = 64;  // decode: one wave per workgroup
 constexpr int kVec = 8;
-constexpr int kStrip = 16;  // tokens per block in prefill mode
+constexpr int kStrip = 8;  // tokens per block in prefill mode
 
 template <typename T, int K>
 struct ConvTaps {

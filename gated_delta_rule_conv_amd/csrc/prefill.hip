@@ -118,14 +118,25 @@ Workspace carve(void* base, int hk, int hv, int d, int chunk, int num_seqs, int 
 }
 
 // ------------------------------------------------------------------------ chunk table
+// One workgroup. Each thread reads its sequence's bounds once (all reads independent),
+// the chunk counts are scanned in LDS, and each thread writes its own sequence's chunk
+// entries; the longest-first order is ranked from lengths kept in LDS, so the kernel
+// makes a single dependent round trip to global memory.
 __global__ __launch_bounds__(kMetaThreads) void chunk_table_kernel(const int* __restrict__ cu, int N, int C,
                                                                   Workspace w) {
   __shared__ int scan[kMetaThreads];
+  __shared__ int lens[kLptMaxSeqs];
   const int tid = threadIdx.x;
   int carry = 0;
   for (int base = 0; base < N; base += kMetaThreads) {
     const int s = base + tid;
-    const int nc = s < N ? (cu[s + 1] - cu[s] + C - 1) / C : 0;
+    int start = 0, len = 0;
+    if (s < N) {
+      start = cu[s];
+      len = cu[s + 1] - start;
+    }
+    const int nc = (len + C - 1) / C;
+    if (N <= kLptMaxSeqs && s < N) lens[s] = len;
     scan[tid] = nc;
     __syncthreads();
     for (int off = 1; off < kMetaThreads; off <<= 1) {
@@ -134,7 +145,11 @@ __global__ __launch_bounds__(kMetaThreads) void chunk_table_kernel(const int* __
       scan[tid] += add;
       __syncthreads();
     }
-    if (s < N) w.chunk_off[s] = carry + scan[tid] - nc;
+    const int first = carry + scan[tid] - nc;  // this sequence's first chunk index
+    if (s < N) {
+      w.chunk_off[s] = first;
+      for (int c = 0; c < nc; ++c) w.table[first + c] = make_int4(s, start + c * C, min(C, len - c * C), c);
+    }
     carry += scan[kMetaThreads - 1];
     __syncthreads();
   }
@@ -142,20 +157,14 @@ __global__ __launch_bounds__(kMetaThreads) void chunk_table_kernel(const int* __
     w.chunk_off[N] = carry;
     *w.n_chunks = carry;
   }
-  for (int s = tid; s < N; s += kMetaThreads) {
-    const int start = cu[s];
-    const int len = cu[s + 1] - start;
-    const int off = w.chunk_off[s];  // written by this thread above
-    for (int c = 0; c * C < len; ++c) w.table[off + c] = make_int4(s, start + c * C, min(C, len - c * C), c);
-  }
   // longest sequence first, so its long chain of chunks starts with the first wave of
   // workgroups (ties by index)
   for (int s = tid; s < N; s += kMetaThreads) {
     if (N <= kLptMaxSeqs) {
-      const int ls = cu[s + 1] - cu[s];
+      const int ls = lens[s];
       int rank = 0;
       for (int q = 0; q < N; ++q) {
-        const int lq = cu[q + 1] - cu[q];
+        const int lq = lens[q];
         rank += (lq > ls) || (lq == ls && q < s);
       }
       w.order[rank] = s;

@@ -210,3 +210,22 @@ def test_run_twice_is_deterministic():
 
 def bits_of_np(a):
     return np.ascontiguousarray(a).view(np.int32)
+
+
+def test_many_short_sequences():
+    """1100 packed sequences of 0..5 tokens (zero-length ones included): the chunk table
+    scans more than one 1024-sequence tile and skips the longest-first ordering (more than
+    256 sequences). Every sequence is checked against the oracle, and zero-length
+    sequences keep their state bits."""
+    announce("prefill 1100 short sequences, fp32, d=32, chunk 16")
+    rng = np.random.default_rng(77)
+    lens = tuple(int(v) for v in rng.integers(0, 6, size=1100))
+    shape = LayerShape(2, 2, 32, conv_width=4, chunk=16, in_dtype="f32")
+    inp = make_prefill(0, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
+    run = PrefillRun(inp)
+    o, S = run.run()
+    ref = _oracle(inp)
+    _check(o, S, ref, inp["cu_seqlens"], TOL_F32, label="1100 seqs")
+    empty = [i for i, n in enumerate(lens) if n == 0]
+    assert empty
+    np.testing.assert_array_equal(S[empty].view(np.int32), inp["S0"][empty].view(np.int32))
