@@ -27,7 +27,8 @@
 //   inter_chunk_kernel : one workgroup per (sequence, v-head, 16 state rows), walking the
 //                        chunks of its sequence in order with its 16 x d slice of the
 //                        state resident in registers/LDS; the contractions K S^T, Q S^T,
-//                        T R, P U and U^T K run on MFMA. The 16-row slices of one head are
+//                        T R, P U and U^T K run on MFMA (K^ is staged through LDS for the
+//                        last one, whose contraction runs over tokens). The 16-row slices of one head are
 //                        mapped to one XCD so they share K, Q, T and P through its L2.
 
 #include "launch.h"
@@ -46,8 +47,7 @@ constexpr int kLptMaxSeqs = 256;   // longest-first ordering only up to this man
 // Per-chunk operands the intra-chunk kernel hands to the inter-chunk kernel, stored in
 // fragment order for the MFMA policy (FragIO<> in mma.h), zero-padded past the chunk:
 //   per (chunk, k-head): K^ and Q^ (q already scaled) as A operands (rows = tokens,
-//                        k = head dim), then K^ as the B operand of the state update
-//                        (rows = head dim, k = tokens)
+//                        k = head dim)
 //   per (chunk, v-head): T, then P, as A operands (rows and k = tokens); then gam [C]
 //                        (fp32, padded with gam_{n-1}) and beta [C] (fp32, padded with 0)
 struct Workspace {
@@ -67,16 +67,14 @@ inline size_t max_chunks_of(int chunk, int num_seqs, int total_tokens) {
   return static_cast<size_t>(total_tokens) / chunk + static_cast<size_t>(num_seqs);
 }
 
-// fragment counts: NT token tiles, NV k-steps over the head dim, ST head-dim tiles,
-// NK k-steps over the chunk's tokens (padded up to a whole k-step)
+// fragment counts: token tiles (C / 16), k-steps over the head dim (D / KSTEP) and over
+// the chunk's tokens (nk, padded up to a whole k-step)
 template <int POL>
 struct FragCount {
   static constexpr int KSTEP = Mma<POL>::KSTEP;
   static constexpr int BYTES = FragIO<POL>::BYTES;
   __host__ __device__ static constexpr int nk(int C) { return (C + KSTEP - 1) / KSTEP; }
-  __host__ __device__ static constexpr size_t kq(int D, int C) {
-    return (2ull * (C / 16) * (D / KSTEP) + static_cast<size_t>(D / 16) * nk(C)) * BYTES;
-  }
+  __host__ __device__ static constexpr size_t kq(int D, int C) { return 2ull * (C / 16) * (D / KSTEP) * BYTES; }
   __host__ __device__ static constexpr size_t tp(int C) { return 2ull * (C / 16) * nk(C) * BYTES + 2ull * C * 4; }
 };
 
@@ -270,13 +268,11 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   }
   __syncthreads();
 
-  // 1b. export K^, Q^ (A operands) and K^ as the update's B operand, in fragment order.
-  // Thread e writes lane e % 64 of fragment block e / 64, so each wave stores whole
-  // contiguous KiBs.
+  // 1b. export K^ and Q^ as A operands in fragment order. Thread e writes lane e % 64 of
+  // fragment block e / 64, so each wave stores whole contiguous KiBs.
   {
     char* kq = w.kq + (static_cast<int64_t>(chunk) * r.hk + h) * w.kq_stride;
     char* qq = kq + static_cast<size_t>(C / 16) * NVF * FIO::BYTES;
-    char* kt = qq + static_cast<size_t>(C / 16) * NVF * FIO::BYTES;
     for (int e = tid; e < (C / 16) * NVF * 64; e += kThreads) {
       const int blk = e / 64, ln = e % 64;
       const int t = (blk / NVF) * 16 + ln % 16, d0 = (blk % NVF) * KSTEP + KPL * (ln / 16);
@@ -288,14 +284,6 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
       }
       FIO::store(kq + static_cast<size_t>(blk) * FIO::BYTES, ln, kx);
       FIO::store(qq + static_cast<size_t>(blk) * FIO::BYTES, ln, qx);
-    }
-    for (int e = tid; e < (D / 16) * NKF * 64; e += kThreads) {
-      const int blk = e / 64, ln = e % 64;
-      const int dk = (blk / NKF) * 16 + ln % 16, s0 = (blk % NKF) * KSTEP + KPL * (ln / 16);
-      float kx[KPL];
-#pragma unroll
-      for (int i = 0; i < KPL; ++i) kx[i] = (s0 + i < C) ? Kh[s0 + i][dk] : 0.f;
-      FIO::store(kt + static_cast<size_t>(blk) * FIO::BYTES, ln, kx);
     }
   }
 
@@ -452,6 +440,54 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
 }
 
 // ------------------------------------------------------------------------ inter-chunk
+// K^ of the current chunk in LDS as a C x D matrix (one plane per operand part: bf16 hi
+// and lo, or fp32), written by rows from the K side's A fragments and read by columns as
+// the B operand of the state update, whose contraction runs over tokens. A row is D
+// values in 16-byte groups; group g of row t is stored at position g ^ swz(t). For the
+// row-wise fragment writes (8 lanes: 8 consecutive rows, one group) and the column-wise
+// reads (4 row groups 8 apart, 2 groups of one row each) that spreads the 16-byte groups
+// one instruction touches over 8 distinct positions of an aligned 128 bytes, so neither
+// access conflicts on LDS banks (at D = 128; smaller D only loses that spread).
+template <int POL, int D, int C>
+struct KTile {
+  using F = typename Mma<POL>::Frag;
+  static constexpr int KPL = Mma<POL>::KPL;
+  static constexpr int ES = POL == kPolBF16X3 ? 2 : 4;  // bytes per element of a plane
+  static constexpr int ROW = D * ES;
+  static constexpr int GPR = ROW / 16;  // 16-byte groups per row
+  static constexpr int PLANE = C * ROW;
+  static constexpr int BYTES = POL == kPolBF16X3 ? 2 * PLANE : PLANE;
+  __device__ __forceinline__ static int swz(int t) { return ((t & 7) ^ (((t >> 3) & 3) << 1)) & (GPR - 1); }
+  __device__ __forceinline__ static int off(int t, int d) {
+    return t * ROW + ((((d * ES) >> 4) ^ swz(t)) << 4) + ((d * ES) & 15);
+  }
+  // the A fragment holding row t, head-dim values d0 .. d0 + KPL - 1 (one 16-byte group)
+  __device__ __forceinline__ static void put(char* base, int t, int d0, const F& f) {
+    char* p = base + off(t, d0);
+    if constexpr (POL == kPolBF16X3) {
+      *reinterpret_cast<bf16x8*>(p) = f.hi;
+      *reinterpret_cast<bf16x8*>(p + PLANE) = f.lo;
+    } else {
+      *reinterpret_cast<float4*>(p) = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
+    }
+  }
+  // B fragment: column d, rows t0 .. t0 + KPL - 1
+  __device__ __forceinline__ static F column(const char* base, int d, int t0) {
+    F f;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const char* p = base + off(t0 + i, d);
+      if constexpr (POL == kPolBF16X3) {
+        f.hi[i] = *reinterpret_cast<const __bf16*>(p);
+        f.lo[i] = *reinterpret_cast<const __bf16*>(p + PLANE);
+      } else {
+        f.v[i] = *reinterpret_cast<const float*>(p);
+      }
+    }
+    return f;
+  }
+};
+
 // Everything one wave reads from global memory for one chunk; loaded one chunk ahead so
 // the loads overlap the previous chunk's arithmetic. Waves 0-3 ("K side") hold K^ rows
 // and T rows, waves 4-7 ("Q side") hold Q^ rows and P rows, of token tile wave % 4.
@@ -463,7 +499,6 @@ struct ChunkIn {
   static constexpr int NK = (C + KSTEP - 1) / KSTEP;  // k-steps over the chunk's tokens
   F af[NV];     // K^ (or Q^) row of token 16*tt + l16
   F mf[NK];     // T (or P) row of token 16*tt + l16
-  F kt[NK];     // K^T row 16*wave + l16 (this wave's state tile)
   float vv[4];  // v at the 4 output rows this lane holds (K side; rows >= n masked at use)
   float gt[4], bt[4];
   float gn;     // gam of the chunk's last token
@@ -477,6 +512,7 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
   using F = typename M::Frag;
   using In = ChunkIn<POL, D, C>;
   using FIO = FragIO<POL>;
+  using KT = KTile<POL, D, C>;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
   constexpr int NBLK = D / kDVB;  // state-row blocks per head
   constexpr int NT = C / 16;      // token tiles per chunk
@@ -487,11 +523,12 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
   constexpr int RLD = C + PADE;
   constexpr int S_BYTES = kDVB * SLD * 4;
   constexpr int R_BYTES = kDVB * RLD * 4;
-  __shared__ __attribute__((aligned(16))) char lds[S_BYTES + 3 * R_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[S_BYTES + 3 * R_BYTES + KT::BYTES];
   char* Sl = lds;                     // state slice  [16][D]   B operand of K^S^T, Q^S^T
   char* Rt = lds + S_BYTES;           // R^T          [16][C]   B operand of T R
   char* Ut = Rt + R_BYTES;            // U^T          [16][C]   B operand of P U
   char* Us = Ut + R_BYTES;            // (e^{gam_n-gam} U)^T    A operand of the update
+  char* Kl = Us + R_BYTES;            // K^           [C][D]    B operand of the update
 
   const RecurArgs& r = a.r;
   const int per_seq = NBLK * r.hv;
@@ -565,12 +602,6 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
         in.vv[rr] = r.v[static_cast<int64_t>(t0 + tc) * r.v_stride + j * D + blk * kDVB + l16];
       }
     }
-    if (has_tile) {
-      const char* ktp = kq + 2 * static_cast<size_t>(NT) * NV * FIO::BYTES;
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-        in.kt[kk] = FIO::load(ktp + static_cast<size_t>(wave * NK + kk) * FIO::BYTES, lane);
-    }
   };
 
   auto process = [&](int c, In& in) {
@@ -584,6 +615,9 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
       for (int v = 0; v < NV; ++v) M::mma3(a3, in.af[v], SP::load(Sl, kDVB, SLD, l16, kl + v * KSTEP));
       const f32x4 acc = total(a3);
       if (!qside) {
+        // K^ rows of this token tile into LDS for the update (read after two barriers)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) KT::put(Kl, tt * 16 + l16, v * KSTEP + kl, in.af[v]);
         float rv[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -643,8 +677,10 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
       zero3(s3);
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const F ua = (kFullK || kk * KSTEP + kl < C) ? SP::load(Us, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
-        M::mma3(s3, ua, in.kt[kk]);
+        const bool live = kFullK || kk * KSTEP + kl < C;
+        const F ua = live ? SP::load(Us, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+        const F kb = live ? KT::column(Kl, wave * 16 + l16, kk * KSTEP + kl) : SP::zero();
+        M::mma3(s3, ua, kb);
       }
       const f32x4 upd = total(s3);
       f32x4 acc;
