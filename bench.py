@@ -6,7 +6,8 @@ One step = one pass of the whole hot path:
     layer = gdn_conv_update (decode mode) + gdn_decode_batched over 32 v-heads x
     128x128 fp32 states addressed through per-layer device u64 pointer arrays. The
     step is captured once in a HIP graph and replayed (the serving-loop form); the
-    eager (one ctypes call per launch) step is timed too;
+    eager (one ctypes call per launch) step is timed too, and so is the same step as
+    one gdn_decode_fused call per layer (conv + commit + norm + delta rule);
   * prefill: one 4096-token sequence (16 q/k heads, 32 v-heads, d = 128, bf16 input,
     chunk 64) = gdn_conv_update (prefill mode) + gdn_prefill_chunked. The 8-sequence
     ragged pack (T = 15717) is timed as well.
@@ -35,11 +36,16 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 STATE_BYTES_PER_SLOT_LAYER = 2 * 32 * 128 * 128 * 4  # read + write of one 2 MiB state
+# Everything one slot-layer of the fused decode must move: the state (read + write), the
+# conv state (3 rows x 8192 channels bf16, read + write), x (8192 bf16), o (32 x 128 fp32)
+# and g, beta (32 fp32 each); plus the conv taps (8192 x 4 bf16) once per launch.
+FUSED_BYTES_PER_SLOT_LAYER = STATE_BYTES_PER_SLOT_LAYER + 2 * 3 * 8192 * 2 + 8192 * 2 + 32 * 128 * 4 + 2 * 32 * 4
+CONV_TAP_BYTES = 8192 * 4 * 2
 
 
 def measured_traffic():
-    """HBM bytes per decode-kernel launch (m = 64) from the committed counter summary,
-    or None when csrc/decode.hip has changed since those counters were taken."""
+    """HBM bytes per decode-kernel launch (m = 64) from the committed counter summary, or
+    None when csrc/decode.hip has changed since those counters were taken."""
     import hashlib
 
     prof = os.path.join(ROOT, "profiles", "hbm_counters_decode_kernel_m64.md")
@@ -73,7 +79,8 @@ def ev():
 class DecodeRig:
     """30 layers of slot pools (256 slots each) and m active slots per layer."""
 
-    def __init__(self, m: int, layers: int = 30, pool: int = 256, n_inputs: int = 8, device="cuda"):
+    def __init__(self, m: int, layers: int = 30, pool: int = 256, n_inputs: int = 8, device="cuda",
+                 fused: bool = False):
         import numpy as np
         import torch
 
@@ -104,13 +111,24 @@ class DecodeRig:
         self.y = torch.empty((m, C), dtype=torch.float32, device=device)
         self.o = torch.empty((m, Hv, sh.head_dim), dtype=torch.float32, device=device)
         self.q, self.k, self.v = gdn.qkv_views(self.dims, self.y)
+        self.fused = fused
+        self.counters = gdn.decode_counters(self.dims, m, device=device)
         self.graph = None
 
     def layer(self, layer: int, s: int) -> None:
         import gated_delta_rule_conv_amd as gdn
 
+        if self.fused:
+            self.fused_only(layer, s)
+            return
         gdn.conv_update(self.dims, self.x[s], self.y, self.conv_w[layer], None, self.cptr[layer])
         self.decode_only(layer, s)
+
+    def fused_only(self, layer: int, s: int) -> None:
+        import gated_delta_rule_conv_amd as gdn
+
+        gdn.decode_fused(self.dims, self.x[s], self.conv_w[layer], None, self.g[s], self.beta[s], self.o,
+                         self.sptr[layer], self.cptr[layer], self.counters)
 
     def decode_only(self, layer: int, s: int) -> None:
         import gated_delta_rule_conv_amd as gdn
@@ -124,7 +142,7 @@ class DecodeRig:
             self.layer(layer, layer % self.n_inputs)
 
     def capture(self) -> None:
-        """Capture one whole step (30 x (conv + decode)) in a HIP graph."""
+        """Capture one whole step (30 layers) in a HIP graph."""
         import torch
 
         side = torch.cuda.Stream()
@@ -245,16 +263,18 @@ def time_graph(rig: DecodeRig, steps: int, warmup: int) -> float:
 
 
 def time_decode_kernel(rig: DecodeRig, rounds: int) -> float:
-    """Mean us per decode-kernel launch: the 30 layers' decode launches back to back
-    (no conv in between), `rounds` times, events on the launching stream."""
+    """Mean us per launch of the rig's decode kernel (fused, or the plain decode kernel
+    of the two-call form): the 30 layers' launches back to back (no conv launches in
+    between), `rounds` times, events on the launching stream."""
     import torch
 
+    one = rig.fused_only if rig.fused else rig.decode_only
     a, b = ev(), ev()
     torch.cuda.synchronize()
     a.record()
     for _ in range(rounds):
         for layer in range(rig.layers):
-            rig.decode_only(layer, layer % rig.n_inputs)
+            one(layer, layer % rig.n_inputs)
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e3 / (rounds * rig.layers)
@@ -300,54 +320,58 @@ def main() -> int:
     K, W = args.steps, args.warmup
 
     # ---------------------------------------------------------------- decode, m = 64
-    rig = DecodeRig(args.m)
-    log("decode rig ready")
-    for _ in range(W):
-        rig.step()
-    torch.cuda.synchronize()
-    # eager step
-    a, b = ev(), ev()
-    a.record()
-    for _ in range(K):
-        rig.step()
-    b.record()
-    torch.cuda.synchronize()
-    eager_ms = a.elapsed_time(b) / K
-    # graph-replayed step
-    rig.capture()
-    log("decode step captured")
-    t_start = time.perf_counter()
-    graph_ms = time_graph(rig, K, W)
-    wall = time.perf_counter() - t_start
-    kern_us = time_decode_kernel(rig, max(2, K // 4))
-    log(f"decode: eager {eager_ms:.3f} ms/step, graph {graph_ms:.3f} ms/step, kernel {kern_us:.2f} us")
+    def run_decode(fused: bool):
+        rig = DecodeRig(args.m, fused=fused)
+        for _ in range(W):
+            rig.step()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(K):
+            rig.step()
+        b.record()
+        torch.cuda.synchronize()
+        eager_ms = a.elapsed_time(b) / K
+        rig.capture()
+        t_start = time.perf_counter()
+        graph_ms = time_graph(rig, K, W)
+        wall = time.perf_counter() - t_start
+        kern_us = time_decode_kernel(rig, max(2, K // 4))
+        log(f"decode ({'fused' if fused else 'conv + decode'}): eager {eager_ms:.3f} ms/step, graph "
+            f"{graph_ms:.3f} ms/step, kernel {kern_us:.2f} us")
+        del rig
+        torch.cuda.empty_cache()
+        return eager_ms, graph_ms, wall, kern_us
 
-    state_bytes_step = rig.layers * args.m * STATE_BYTES_PER_SLOT_LAYER
+    eager_ms, graph_ms, wall, kern_us = run_decode(False)
+    f_eager_ms, f_graph_ms, _, f_kern_us = run_decode(True)
+    state_bytes_step = 30 * args.m * STATE_BYTES_PER_SLOT_LAYER
     value = state_bytes_step / (graph_ms * 1e-3) / 1e9
     bytes_per_launch = args.m * STATE_BYTES_PER_SLOT_LAYER
     achieved = bytes_per_launch / (kern_us * 1e-6) / 1e9
-    del rig
-    torch.cuda.empty_cache()
+    f_bytes_per_launch = args.m * FUSED_BYTES_PER_SLOT_LAYER + CONV_TAP_BYTES
 
     sweep = None
     if not args.no_sweep:
         sweep = {}
         for mm in (1, 4, 16):
-            r = DecodeRig(mm)
-            for _ in range(2):
-                r.step()
-            r.capture()
-            ms = time_graph(r, K, W)
-            kus = time_decode_kernel(r, max(2, K // 4))
-            sweep[str(mm)] = {
-                "ms_per_step": round(ms, 4),
-                "state_GBps": round(r.layers * mm * STATE_BYTES_PER_SLOT_LAYER / ms / 1e6, 1),
-                "decode_kernel_us": round(kus, 2),
-                "note": ("state footprint (%d MiB over 30 layers) fits the 256 MB Infinity Cache" % (mm * 60))
-                if mm * 60 < 256 else "",
-            }
-            del r
-            torch.cuda.empty_cache()
+            row = {}
+            for fused in (False, True):
+                r = DecodeRig(mm, fused=fused)
+                for _ in range(2):
+                    r.step()
+                r.capture()
+                ms = time_graph(r, K, W)
+                kus = time_decode_kernel(r, max(2, K // 4))
+                tag = "fused_" if fused else ""
+                row[tag + "ms_per_step"] = round(ms, 4)
+                row[tag + "state_GBps"] = round(r.layers * mm * STATE_BYTES_PER_SLOT_LAYER / ms / 1e6, 1)
+                row[tag + "decode_kernel_us"] = round(kus, 2)
+                del r
+                torch.cuda.empty_cache()
+            row["note"] = (("state footprint (%d MiB over 30 layers) fits the 256 MB Infinity Cache" % (mm * 60))
+                           if mm * 60 < 256 else "")
+            sweep[str(mm)] = row
         log("sweep done")
 
     # ---------------------------------------------------------------- prefill
@@ -411,6 +435,13 @@ def main() -> int:
                    "state_GBps_eager": round(state_bytes_step / (eager_ms * 1e-3) / 1e9, 2),
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
                    "decode_kernel_us": round(kern_us, 2)},
+        "decode_fused": {"note": "the same step as one gdn_decode_fused call per layer",
+                         "graph_ms_per_step": round(f_graph_ms, 4),
+                         "eager_ms_per_step": round(f_eager_ms, 4),
+                         "state_GBps_graph": round(state_bytes_step / (f_graph_ms * 1e-3) / 1e9, 2),
+                         "fused_kernel_us": round(f_kern_us, 2),
+                         "fused_kernel_bytes_per_launch": f_bytes_per_launch,
+                         "fused_kernel_GBps": round(f_bytes_per_launch / (f_kern_us * 1e-6) / 1e9, 2)},
         "decode_sweep": sweep,
         "prefill": prefill,
         "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,1,false>", "achieved": round(achieved, 2),

@@ -20,6 +20,8 @@ from ._lib import (  # noqa: F401
     gdn_abi_version,
     gdn_conv_update,
     gdn_decode_batched,
+    gdn_decode_fused,
+    gdn_decode_fused_workspace_size,
     gdn_dims,
     gdn_last_error,
     gdn_prefill_chunked,
@@ -28,4 +30,14 @@ from ._lib import (  # noqa: F401
     gdn_slot_pointers,
     make_dims,
 )
-from .layer import SlotPool, channels, conv_update, decode, prefill, prefill_workspace, qkv_views  # noqa: F401
+from .layer import (  # noqa: F401
+    SlotPool,
+    channels,
+    conv_update,
+    decode,
+    decode_counters,
+    decode_fused,
+    prefill,
+    prefill_workspace,
+    qkv_views,
+)

@@ -31,6 +31,12 @@ FLAGS = [
 ]
 
 
+# Per-file additions. decode.hip: the fused decode kernel's one counter atomic is issued
+# early and its result used only at the end; the default wave-level atomic combining
+# would consume the result at once and stall wave 0 on the round trip.
+FILE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -40,7 +46,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *FILE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -13,6 +13,7 @@
 // The op is purely HBM-bound (8 flops per element), so there is no LDS staging: a
 // thread walks a strip of tokens keeping the K-1 previous rows of z in registers.
 
+#include "conv_taps.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -21,73 +22,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kDecThreads = 64;  // decode: one wave per workgroup
-constexpr int kVec = 8;
+constexpr int kVec = kConvVec;
 constexpr int kStrip = 8;  // tokens per block in prefill mode
-
-template <typename T, int K>
-struct ConvTaps {
-  float w[K][kVec];
-  float b[kVec];
-
-  __device__ __forceinline__ void load(const T* __restrict__ wp, const T* __restrict__ bp, int ch0) {
-    // w is [C][K]: the 8*K taps of channels ch0..ch0+7 are contiguous and 16-byte aligned.
-    float flat[K * kVec];
-#pragma unroll
-    for (int i = 0; i < K; ++i) {
-      float tmp[kVec];
-      Vec8<T>::load(wp + static_cast<int64_t>(ch0) * K + i * kVec, tmp);
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) flat[i * kVec + e] = tmp[e];
-    }
-#pragma unroll
-    for (int c = 0; c < kVec; ++c)
-#pragma unroll
-      for (int j = 0; j < K; ++j) w[j][c] = flat[c * K + j];
-    if (bp) {
-      Vec8<T>::load(bp + ch0, b);
-    } else {
-#pragma unroll
-      for (int c = 0; c < kVec; ++c) b[c] = 0.f;
-    }
-  }
-
-  // the same from raw (unconverted) tap and bias vectors
-  __device__ __forceinline__ void from_raw(const typename Vec8<T>::Raw (&wr)[K], const typename Vec8<T>::Raw& br,
-                                           bool has_b) {
-    float flat[K * kVec];
-#pragma unroll
-    for (int i = 0; i < K; ++i) {
-      float tmp[kVec];
-      Vec8<T>::convert(wr[i], tmp);
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) flat[i * kVec + e] = tmp[e];
-    }
-#pragma unroll
-    for (int c = 0; c < kVec; ++c)
-#pragma unroll
-      for (int j = 0; j < K; ++j) w[j][c] = flat[c * K + j];
-    if (has_b) {
-      Vec8<T>::convert(br, b);
-    } else {
-#pragma unroll
-      for (int c = 0; c < kVec; ++c) b[c] = 0.f;
-    }
-  }
-
-  // win[0..K-2] = z rows preceding the current token (oldest first), cur = current token.
-  __device__ __forceinline__ void apply(const float (&win)[K - 1][kVec], const float (&cur)[kVec], bool silu,
-                                        float (&out)[kVec]) const {
-#pragma unroll
-    for (int c = 0; c < kVec; ++c) {
-      float acc = b[c];
-#pragma unroll
-      for (int j = 0; j < K - 1; ++j) acc = fmaf(w[j][c], win[j][c], acc);
-      acc = fmaf(w[K - 1][c], cur[c], acc);
-      if (silu) acc = acc / (1.0f + expf(-acc));
-      out[c] = acc;
-    }
-  }
-};
 
 template <typename T, int K>
 __global__ __launch_bounds__(kThreads) void conv_prefill_kernel(ConvArgs a) {

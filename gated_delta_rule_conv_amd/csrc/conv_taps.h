@@ -1,0 +1,100 @@
+// The taps of the depthwise causal conv for 8 adjacent channels, and the conv of one
+// token: y[c] = act(b[c] + sum_{j<K} w[c][j] z_j[c]), z_0 .. z_{K-2} the preceding rows
+// (oldest first) and z_{K-1} the current token. Shared by the conv kernels and the fused
+// decode kernel so that both produce the same bits.
+#pragma once
+
+#include "device_common.h"
+
+namespace gdn {
+
+constexpr int kConvVec = 8;  // channels per thread
+
+template <typename T, int K>
+struct ConvTaps {
+  float w[K][kConvVec];
+  float b[kConvVec];
+
+  __device__ __forceinline__ void load(const T* __restrict__ wp, const T* __restrict__ bp, int ch0) {
+    // w is [C][K]: the 8*K taps of channels ch0..ch0+7 are contiguous and 16-byte aligned.
+    float flat[K * kConvVec];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      float tmp[kConvVec];
+      Vec8<T>::load(wp + static_cast<int64_t>(ch0) * K + i * kConvVec, tmp);
+#pragma unroll
+      for (int e = 0; e < kConvVec; ++e) flat[i * kConvVec + e] = tmp[e];
+    }
+#pragma unroll
+    for (int c = 0; c < kConvVec; ++c)
+#pragma unroll
+      for (int j = 0; j < K; ++j) w[j][c] = flat[c * K + j];
+    if (bp) {
+      Vec8<T>::load(bp + ch0, b);
+    } else {
+#pragma unroll
+      for (int c = 0; c < kConvVec; ++c) b[c] = 0.f;
+    }
+  }
+
+  // the same from raw (unconverted) tap and bias vectors
+  __device__ __forceinline__ void from_raw(const typename Vec8<T>::Raw (&wr)[K], const typename Vec8<T>::Raw& br,
+                                           bool has_b) {
+    float flat[K * kConvVec];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      float tmp[kConvVec];
+      Vec8<T>::convert(wr[i], tmp);
+#pragma unroll
+      for (int e = 0; e < kConvVec; ++e) flat[i * kConvVec + e] = tmp[e];
+    }
+#pragma unroll
+    for (int c = 0; c < kConvVec; ++c)
+#pragma unroll
+      for (int j = 0; j < K; ++j) w[j][c] = flat[c * K + j];
+    if (has_b) {
+      Vec8<T>::convert(br, b);
+    } else {
+#pragma unroll
+      for (int c = 0; c < kConvVec; ++c) b[c] = 0.f;
+    }
+  }
+
+  // win[0..K-2] = z rows preceding the current token (oldest first), cur = current token.
+  __device__ __forceinline__ void apply(const float (&win)[K - 1][kConvVec], const float (&cur)[kConvVec], bool silu,
+                                        float (&out)[kConvVec]) const {
+#pragma unroll
+    for (int c = 0; c < kConvVec; ++c) {
+      float acc = b[c];
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) acc = fmaf(w[j][c], win[j][c], acc);
+      acc = fmaf(w[K - 1][c], cur[c], acc);
+      if (silu) acc = acc / (1.0f + expf(-acc));
+      out[c] = acc;
+    }
+  }
+};
+
+// The conv of 8 adjacent channels straight from the loaded (raw) taps [8][K], bias,
+// K-1 preceding rows and current token, converting one channel at a time so that few
+// values are live at once. The operations and their order are those of ConvTaps::apply
+// (acc = b; acc = fma(w_j, z_j, acc) for j = 0 .. K-1; then the activation), so both
+// give the same bits.
+template <typename T, int K>
+__device__ __forceinline__ void conv8_raw(const typename Vec8<T>::Raw (&wr)[K], const typename Vec8<T>::Raw& br,
+                                          bool has_b, const typename Vec8<T>::Raw (&rows)[K - 1],
+                                          const typename Vec8<T>::Raw& cur, bool silu, float (&out)[kConvVec]) {
+  using V8 = Vec8<T>;
+#pragma unroll
+  for (int c = 0; c < kConvVec; ++c) {
+    float acc = has_b ? V8::elem(br, c) : 0.f;
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j)
+      acc = fmaf(V8::elem(wr[(c * K + j) / kConvVec], (c * K + j) % kConvVec), V8::elem(rows[j], c), acc);
+    acc = fmaf(V8::elem(wr[(c * K + K - 1) / kConvVec], (c * K + K - 1) % kConvVec), V8::elem(cur, c), acc);
+    if (silu) acc = acc / (1.0f + expf(-acc));
+    out[c] = acc;
+  }
+}
+
+}  // namespace gdn

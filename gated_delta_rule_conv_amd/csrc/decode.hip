@@ -31,6 +31,7 @@
 // bits of a slot's result depend neither on m, nor on the unit size, nor on which
 // other slots are in the call.
 
+#include "conv_taps.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -55,6 +56,69 @@ struct DecodeCfg {
   static constexpr int NPART = D / ROWS;      // units per (slot, head)
   static_assert(NPART * ROWS == D, "units must tile the head");
 };
+
+// The arithmetic of one unit once its loads are in registers: normalise k and q (the
+// lane holds 16 columns of each), then for each of the P row passes the two row dots,
+// the delta-rule update of the rows and their outputs. Both decode kernels call this, so
+// the fused kernel's bits equal the separate conv + decode launches.
+template <int D, int P>
+__device__ __forceinline__ void decode_rows(const f32x4 (&s)[P][4], f32x4 (&kv)[4], f32x4 (&qv)[4], const float (&vr)[P],
+                                            float gval, float beta, float eps, float scale, gf32x4* S, gfloat* orow,
+                                            int row0, int c) {
+  using Cfg = DecodeCfg<D, P>;
+  constexpr int LPR = Cfg::LPR, RPP = Cfg::RPP;
+  // k^ and q^ at this lane's 16 columns, and k^ . q^
+  float kk = 0.f, qq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    kk = fmaf(kv[e].x, kv[e].x, kk); kk = fmaf(kv[e].y, kv[e].y, kk);
+    kk = fmaf(kv[e].z, kv[e].z, kk); kk = fmaf(kv[e].w, kv[e].w, kk);
+    qq = fmaf(qv[e].x, qv[e].x, qq); qq = fmaf(qv[e].y, qv[e].y, qq);
+    qq = fmaf(qv[e].z, qv[e].z, qq); qq = fmaf(qv[e].w, qv[e].w, qq);
+  }
+  kk = group_sum<LPR>(kk);
+  qq = group_sum<LPR>(qq);
+  const float rk = 1.0f / sqrtf(kk + eps);
+  const float rq = scale / sqrtf(qq + eps);
+  float kq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    kv[e].x *= rk; kv[e].y *= rk; kv[e].z *= rk; kv[e].w *= rk;
+    qv[e].x *= rq; qv[e].y *= rq; qv[e].z *= rq; qv[e].w *= rq;
+    kq = fmaf(kv[e].x, qv[e].x, kq); kq = fmaf(kv[e].y, qv[e].y, kq);
+    kq = fmaf(kv[e].z, qv[e].z, kq); kq = fmaf(kv[e].w, qv[e].w, kq);
+  }
+  kq = group_sum<LPR>(kq);
+  const float alpha = expf(gval);
+
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int r = row0 + p * RPP;
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sk = fmaf(s[p][e].x, kv[e].x, sk); sk = fmaf(s[p][e].y, kv[e].y, sk);
+      sk = fmaf(s[p][e].z, kv[e].z, sk); sk = fmaf(s[p][e].w, kv[e].w, sk);
+      sq = fmaf(s[p][e].x, qv[e].x, sq); sq = fmaf(s[p][e].y, qv[e].y, sq);
+      sq = fmaf(s[p][e].z, qv[e].z, sq); sq = fmaf(s[p][e].w, qv[e].w, sq);
+    }
+    sk = group_sum<LPR>(sk);
+    sq = group_sum<LPR>(sq);
+    const float ur = beta * (vr[p] - alpha * sk);
+    gf32x4* rowp = S + static_cast<int64_t>(r) * (D / 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f32x4 n;
+      n.x = fmaf(ur, kv[e].x, alpha * s[p][e].x);
+      n.y = fmaf(ur, kv[e].y, alpha * s[p][e].y);
+      n.z = fmaf(ur, kv[e].z, alpha * s[p][e].z);
+      n.w = fmaf(ur, kv[e].w, alpha * s[p][e].w);
+      __builtin_nontemporal_store(n, rowp + c + LPR * e);
+    }
+    if (c == 0) orow[r] = fmaf(ur, kq, alpha * sq);
+  }
+}
+
 
 template <int D, int P, bool SCHED_FENCE>
 __global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(RecurArgs a, int32_t total_units) {
@@ -100,57 +164,7 @@ __global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(RecurArgs a
   const float beta = ((cfloat*)a.beta)[gi];
   if constexpr (SCHED_FENCE) __builtin_amdgcn_sched_barrier(0);
 
-  // k^ and q^ at this lane's 16 columns, and k^ . q^
-  float kk = 0.f, qq = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    kk = fmaf(kv[e].x, kv[e].x, kk); kk = fmaf(kv[e].y, kv[e].y, kk);
-    kk = fmaf(kv[e].z, kv[e].z, kk); kk = fmaf(kv[e].w, kv[e].w, kk);
-    qq = fmaf(qv[e].x, qv[e].x, qq); qq = fmaf(qv[e].y, qv[e].y, qq);
-    qq = fmaf(qv[e].z, qv[e].z, qq); qq = fmaf(qv[e].w, qv[e].w, qq);
-  }
-  kk = group_sum<LPR>(kk);
-  qq = group_sum<LPR>(qq);
-  const float rk = 1.0f / sqrtf(kk + a.eps);
-  const float rq = a.scale / sqrtf(qq + a.eps);
-  float kq = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    kv[e].x *= rk; kv[e].y *= rk; kv[e].z *= rk; kv[e].w *= rk;
-    qv[e].x *= rq; qv[e].y *= rq; qv[e].z *= rq; qv[e].w *= rq;
-    kq = fmaf(kv[e].x, qv[e].x, kq); kq = fmaf(kv[e].y, qv[e].y, kq);
-    kq = fmaf(kv[e].z, qv[e].z, kq); kq = fmaf(kv[e].w, qv[e].w, kq);
-  }
-  kq = group_sum<LPR>(kq);
-  const float alpha = expf(gval);
-  gfloat* orow = (gfloat*)(a.o + gi * D);
-
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int r = row0 + p * RPP;
-    float sk = 0.f, sq = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sk = fmaf(s[p][e].x, kv[e].x, sk); sk = fmaf(s[p][e].y, kv[e].y, sk);
-      sk = fmaf(s[p][e].z, kv[e].z, sk); sk = fmaf(s[p][e].w, kv[e].w, sk);
-      sq = fmaf(s[p][e].x, qv[e].x, sq); sq = fmaf(s[p][e].y, qv[e].y, sq);
-      sq = fmaf(s[p][e].z, qv[e].z, sq); sq = fmaf(s[p][e].w, qv[e].w, sq);
-    }
-    sk = group_sum<LPR>(sk);
-    sq = group_sum<LPR>(sq);
-    const float ur = beta * (vr[p] - alpha * sk);
-    gf32x4* rowp = S + static_cast<int64_t>(r) * (D / 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f32x4 n;
-      n.x = fmaf(ur, kv[e].x, alpha * s[p][e].x);
-      n.y = fmaf(ur, kv[e].y, alpha * s[p][e].y);
-      n.z = fmaf(ur, kv[e].z, alpha * s[p][e].z);
-      n.w = fmaf(ur, kv[e].w, alpha * s[p][e].w);
-      __builtin_nontemporal_store(n, rowp + c + LPR * e);
-    }
-    if (c == 0) orow[r] = fmaf(ur, kq, alpha * sq);
-  }
+  decode_rows<D, P>(s, kv, qv, vr, gval, beta, a.eps, a.scale, S, (gfloat*)(a.o + gi * D), row0, c);
 }
 
 template <int D, int P, bool F>
@@ -174,6 +188,184 @@ hipError_t launch_decode(const RecurArgs& a, int32_t m, hipStream_t s) {
     case 64: return big ? launch_units<64, 1, false>(a, m, s) : launch_units<64, 2, true>(a, m, s);
     default: return big ? launch_units<128, 1, false>(a, m, s) : launch_units<128, 2, true>(a, m, s);
   }
+}
+
+namespace {
+// ---------------------------------------------------------------- fused conv + decode
+// One launch for the whole decode step of a layer: the depthwise conv of the token's
+// q, k and v channels (against the slot's conv state), the conv state commit, and the
+// decode above. A workgroup is WPB units of one (slot, v-head), i.e. VR consecutive
+// state rows. Lanes of wave 0 first convolve 8 channels each -- the 2d q/k channels of
+// the head's k-head and the VR v channels of the workgroup's rows -- into LDS with the
+// conv kernels' arithmetic (conv8_raw), while every wave's state loads are in flight;
+// the waves then take k, q and v from LDS and run decode_rows unchanged.
+//
+// Conv state commit. The v channels of a workgroup's rows are read by that workgroup
+// alone, so their lanes write the shifted state right after reading it. The q/k
+// channels of k-head h are read by every workgroup of the (hv/hk) v-heads sharing it;
+// each of those workgroups adds one to counters[slot][h] once all its reads have
+// returned, and the one that brings it to the total writes the q/k conv state (from
+// the rows it keeps in LDS) and resets the counter to zero for the next call.
+template <int D, int P>
+struct FusedCfg {
+  static constexpr int NPART = DecodeCfg<D, P>::NPART;
+  static constexpr int WPB = NPART < kDecodeWaves ? NPART : kDecodeWaves;  // waves per workgroup
+  static constexpr int BPH = NPART / WPB;                                 // workgroups per (slot, v-head)
+  static constexpr int NT = WPB * kWave;
+  static constexpr int VR = WPB * DecodeCfg<D, P>::ROWS;                  // state rows per workgroup
+  static constexpr int GQK = 2 * D / kConvVec;                            // q/k channel groups
+  static constexpr int GV = VR / kConvVec;                                // v channel groups
+  static_assert(GQK + GV <= kWave, "one channel group per lane of wave 0");
+  // One-pass units with bf16 inputs fit 72 VGPRs, i.e. 7 waves per SIMD (one register
+  // more would cost a wave); fp32 inputs need more registers for the raw conv inputs.
+  template <typename T>
+  static constexpr int min_blocks() { return (P == 1 && sizeof(T) == 2 && WPB == 4) ? 7 : 1; }
+};
+
+template <typename T, int K, int D, int P, bool SCHED_FENCE>
+__global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min_blocks<T>())) void fused_decode_kernel(FusedArgs f) {
+  using Cfg = DecodeCfg<D, P>;
+  using FC = FusedCfg<D, P>;
+  using V8 = Vec8<T>;
+  constexpr int LPR = Cfg::LPR, RPP = Cfg::RPP, ROWS = Cfg::ROWS;
+  constexpr int WPB = FC::WPB, BPH = FC::BPH, VR = FC::VR, GQK = FC::GQK, GV = FC::GV;
+  constexpr int V = kConvVec;
+  typedef __attribute__((address_space(1))) T GT;
+  __shared__ __attribute__((aligned(16))) float yqk[2 * D];  // q then k of the k-head
+  __shared__ __attribute__((aligned(16))) float yv[VR];
+  __shared__ typename Vec8<T>::Raw qk_rows[K - 1][GQK];  // new q/k conv-state rows
+  const RecurArgs& a = f.r;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int bh = blockIdx.x % BPH;
+  const int j = (blockIdx.x / BPH) % a.hv;
+  const int i = (blockIdx.x / BPH) / a.hv;
+  const uint64_t sp = ((cu64*)a.state_ptrs)[i];
+  const uint64_t cp = ((cu64*)f.conv_ptrs)[i];
+  if (sp == 0 || cp == 0) return;  // inactive slot (the whole workgroup)
+  const int h = j / (a.hv / a.hk);
+  const int part = bh * WPB + w;
+  const int c = lane % LPR;
+  const int rl = lane / LPR;
+  const int row0 = part * ROWS + rl;
+  gf32x4* S = (gf32x4*)(reinterpret_cast<float*>(sp) + static_cast<int64_t>(j) * D * D);
+  GT* cs = (GT*)reinterpret_cast<T*>(cp);
+  const int C = f.channels;
+
+  // State rows first (every wave), then wave 0's conv inputs, lane l taking channel
+  // group l (q/k groups, then v groups; lanes past them repeat a group and drop it).
+  // Everything is in flight before anything waits.
+  f32x4 s[P][4];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      s[p][e] = __builtin_nontemporal_load(S + static_cast<int64_t>(row0 + p * RPP) * (D / 4) + c + LPR * e);
+  const int64_t gi = static_cast<int64_t>(i) * a.hv + j;
+  const float gval = ((cfloat*)a.g)[gi];
+  const float beta = ((cfloat*)a.beta)[gi];
+  const int grp = lane % (GQK + GV);
+  const bool is_qk = grp < GQK;
+  const int ch0 = is_qk ? (grp * V < D ? h * D + grp * V : a.hk * D + h * D + (grp * V - D))
+                        : 2 * a.hk * D + j * D + bh * VR + (grp - GQK) * V;
+  if constexpr (SCHED_FENCE) __builtin_amdgcn_sched_barrier(0);
+
+  // Wave 0 alone reads conv state. Once its reads have returned (their values are
+  // consumed here) it counts this workgroup in, with a relaxed atomic: no later write
+  // can reach a read that is done, and the commit needs nothing from the other
+  // workgroups but the count itself. (Acquire or release at device scope would write
+  // back and invalidate this XCD's L2.) The count comes back while the waves compute.
+  int32_t* ctr = f.counters + static_cast<int64_t>(i) * a.hk + h;
+  int before = 0;
+  if (w == 0) {
+    // (loads and arithmetic in one block: no raw value lives past it)
+    typename V8::Raw xr, sr[K - 1], wr[K], br;
+#pragma unroll
+    for (int t = 0; t < K; ++t) wr[t] = V8::load_raw(static_cast<const T*>(f.w) + static_cast<int64_t>(ch0) * K + t * V);
+#pragma unroll
+    for (int t = 0; t < K - 1; ++t) sr[t] = V8::load_raw_g(cs + static_cast<int64_t>(t) * C + ch0);
+    xr = V8::load_raw(static_cast<const T*>(f.x) + static_cast<int64_t>(i) * f.x_stride + ch0);
+    // with no bias, taps stand in for the load and are never used
+    br = V8::load_raw(static_cast<const T*>(f.b ? f.b : f.w) + ch0);
+    float out[V];
+    conv8_raw<T, K>(wr, br, f.b != nullptr, sr, xr, f.silu != 0, out);
+    if (lane < GQK + GV) {
+      float* dst = is_qk ? &yqk[grp * V] : &yv[(grp - GQK) * V];
+      *reinterpret_cast<f32x4*>(dst) = f32x4{out[0], out[1], out[2], out[3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{out[4], out[5], out[6], out[7]};
+      // new conv-state rows = old rows 1 .. K-2, then x
+      if (!is_qk) {
+        // v channels: this lane is their only reader, so they are written now
+#pragma unroll
+        for (int t = 0; t < K - 2; ++t) V8::store_raw_g(cs + static_cast<int64_t>(t) * C + ch0, sr[t + 1]);
+        V8::store_raw_g(cs + static_cast<int64_t>(K - 2) * C + ch0, xr);
+      } else {
+        // q/k channels: kept in LDS for the commit, in case this workgroup is the last
+#pragma unroll
+        for (int t = 0; t < K - 2; ++t) qk_rows[t][grp] = sr[t + 1];
+        qk_rows[K - 2][grp] = xr;
+      }
+    }
+    if (lane == 0) before = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+
+  f32x4 kv[4], qv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    qv[e] = *reinterpret_cast<const f32x4*>(&yqk[4 * (c + LPR * e)]);
+    kv[e] = *reinterpret_cast<const f32x4*>(&yqk[D + 4 * (c + LPR * e)]);
+  }
+  float vr[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) vr[p] = yv[w * ROWS + rl + p * RPP];
+  decode_rows<D, P>(s, kv, qv, vr, gval, beta, a.eps, a.scale, S, (gfloat*)(a.o + gi * D), row0, c);
+
+  // the last workgroup of (slot, k-head) writes the q/k conv state (wave 0, from the
+  // rows it put in LDS itself) and leaves the counter at zero
+  if (w == 0 && __builtin_amdgcn_readfirstlane(before) == (a.hv / a.hk) * BPH - 1) {
+    if (lane < GQK) {
+#pragma unroll
+      for (int t = 0; t < K - 1; ++t) V8::store_raw_g(cs + static_cast<int64_t>(t) * C + ch0, qk_rows[t][lane]);
+    }
+    if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <typename T, int K, int D, int P, bool F>
+hipError_t launch_fused_units(const FusedArgs& f, int32_t m, hipStream_t s) {
+  using FC = FusedCfg<D, P>;
+  const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(m) * f.r.hv * FC::BPH);
+  fused_decode_kernel<T, K, D, P, F><<<blocks, FC::NT, 0, s>>>(f);
+  return hipGetLastError();
+}
+
+template <typename T, int K>
+hipError_t launch_fused_k(const FusedArgs& f, int32_t m, hipStream_t s) {
+  const bool big = static_cast<int64_t>(m) * f.r.hv >= 1024;
+  switch (f.r.d) {
+    case 32: return launch_fused_units<T, K, 32, 1, false>(f, m, s);
+    case 64: return big ? launch_fused_units<T, K, 64, 1, false>(f, m, s) : launch_fused_units<T, K, 64, 2, true>(f, m, s);
+    default:
+      return big ? launch_fused_units<T, K, 128, 1, false>(f, m, s) : launch_fused_units<T, K, 128, 2, true>(f, m, s);
+  }
+}
+
+template <typename T>
+hipError_t launch_fused_t(const FusedArgs& f, int32_t m, hipStream_t s) {
+  switch (f.width) {
+    case 2: return launch_fused_k<T, 2>(f, m, s);
+    case 3: return launch_fused_k<T, 3>(f, m, s);
+    default: return launch_fused_k<T, 4>(f, m, s);
+  }
+}
+}  // namespace
+
+// Same unit-size rule as launch_decode.
+hipError_t launch_decode_fused(const FusedArgs& f, int32_t m, hipStream_t s) {
+  if (m == 0) return hipSuccess;
+  return f.bf16 ? launch_fused_t<uint16_t>(f, m, s) : launch_fused_t<float>(f, m, s);
 }
 
 namespace {

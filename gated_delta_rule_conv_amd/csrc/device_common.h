@@ -47,6 +47,8 @@ struct Vec8<float> {
     ((G4*)p)[0] = r.a;
     ((G4*)p)[1] = r.b;
   }
+  // element e (compile-time) of a raw vector, as fp32
+  __device__ __forceinline__ static float elem(const Raw& r, int e) { return e < 4 ? r.a[e] : r.b[e - 4]; }
   __device__ __forceinline__ static void convert(const Raw& r, float (&v)[8]) {
     v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
     v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
@@ -75,6 +77,9 @@ struct Vec8<uint16_t> {
   __device__ __forceinline__ static void store_raw_g(GT* p, const Raw& r) {
     typedef __attribute__((address_space(1))) Raw G4;
     *(G4*)p = r;
+  }
+  __device__ __forceinline__ static float elem(const Raw& a, int e) {
+    return (e & 1) ? __uint_as_float(a[e >> 1] & 0xFFFF0000u) : __uint_as_float(a[e >> 1] << 16);
   }
   __device__ __forceinline__ static void convert(const Raw& a, float (&v)[8]) {
 #pragma unroll

@@ -191,6 +191,54 @@ gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_st
   return hip_status(gdn::launch_decode(a, m, static_cast<hipStream_t>(stream)), fn);
 }
 
+gdn_status gdn_decode_fused_workspace_size(const gdn_dims* dims, int32_t m, size_t* bytes) {
+  const char* fn = "gdn_decode_fused_workspace_size";
+  if (gdn_status st = check_dims(dims, fn)) return st;
+  if (!bytes) return fail(GDN_ERR_NULL, "%s: bytes is NULL", fn);
+  if (m < 0) return fail(GDN_ERR_SHAPE, "%s: negative m", fn);
+  *bytes = static_cast<size_t>(m) * dims->num_k_heads * sizeof(int32_t);
+  return GDN_OK;
+}
+
+gdn_status gdn_decode_fused(const gdn_dims* dims, const void* x, int64_t x_stride, const void* conv_w,
+                            const void* conv_b, const float* g, const float* beta, float* o,
+                            const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, int32_t m,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_decode_fused";
+  if (gdn_status st = check_dims(dims, fn)) return st;
+  if (m < 0) return fail(GDN_ERR_SHAPE, "%s: negative m", fn);
+  if (m == 0) return GDN_OK;
+  if (!x || !conv_w || !g || !beta || !o || !state_ptrs || !conv_state_ptrs)
+    return fail(GDN_ERR_NULL, "%s: x, conv_w, g, beta, o, state_ptrs and conv_state_ptrs are required", fn);
+  const int64_t C = channels(dims);
+  const int64_t esz = dims->in_dtype == GDN_BF16 ? 2 : 4;
+  if (x_stride < 0 || (m > 1 && x_stride < C))
+    return fail(GDN_ERR_SHAPE, "%s: x row stride %lld below channel count %lld", fn, static_cast<long long>(x_stride),
+                static_cast<long long>(C));
+  if (!aligned16(x) || !aligned16(conv_w) || (conv_b && !aligned16(conv_b)) || (x_stride * esz) % 16)
+    return fail(GDN_ERR_ALIGN, "%s: x, conv_w, conv_b must be 16-byte aligned and x_stride a multiple of 16 bytes", fn);
+  const size_t need = static_cast<size_t>(m) * dims->num_k_heads * sizeof(int32_t);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+    return fail(GDN_ERR_WORKSPACE, "%s: a 4-byte aligned counter workspace of %zu bytes is needed, %zu given", fn, need,
+                workspace_bytes);
+  const int64_t blocks = static_cast<int64_t>(m) * dims->num_v_heads * (dims->head_dim / 32);
+  if (blocks > 0x7fffffff) return fail(GDN_ERR_SHAPE, "%s: m = %d too large for one launch", fn, m);
+  gdn::FusedArgs f{};
+  f.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, nullptr, 0, g, beta, o, state_ptrs, dims->num_k_heads,
+                       dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale};
+  f.x = x;
+  f.x_stride = x_stride;
+  f.w = conv_w;
+  f.b = conv_b;
+  f.conv_ptrs = conv_state_ptrs;
+  f.counters = static_cast<int32_t*>(workspace);
+  f.channels = static_cast<int32_t>(C);
+  f.width = dims->conv_width;
+  f.silu = dims->activation == GDN_ACT_SILU;
+  f.bf16 = dims->in_dtype == GDN_BF16;
+  return hip_status(gdn::launch_decode_fused(f, m, static_cast<hipStream_t>(stream)), fn);
+}
+
 gdn_status gdn_slot_copy(const gdn_dims* dims, const uint64_t* src_state_ptrs, const uint64_t* dst_state_ptrs,
                          const uint64_t* src_conv_ptrs, const uint64_t* dst_conv_ptrs, int32_t n, void* stream) {
   const char* fn = "gdn_slot_copy";

@@ -48,6 +48,23 @@ struct RecurArgs {
 
 hipError_t launch_decode(const RecurArgs& a, int32_t m, hipStream_t s);
 
+// Conv + decode in one launch (r.q, r.k, r.v unused).
+struct FusedArgs {
+  RecurArgs r;
+  const void* x;
+  int64_t x_stride;
+  const void* w;
+  const void* b;  // nullable
+  const uint64_t* conv_ptrs;
+  int32_t* counters;  // [m][hk], zero on entry and on exit
+  int32_t channels;
+  int32_t width;
+  int32_t silu;
+  int32_t bf16;
+};
+
+hipError_t launch_decode_fused(const FusedArgs& f, int32_t m, hipStream_t s);
+
 struct PrefillArgs {
   RecurArgs r;
   const int32_t* cu_seqlens;

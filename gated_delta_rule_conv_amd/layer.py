@@ -6,7 +6,7 @@ u64 pointer arrays built on the device by gdn_slot_pointers ("qLLM", "What this
 is": a fixed-size recurrent-state / conv-buffer slot pool; aprender #5279,
 "Phase plan", P5: a device u64[m] array of per-slot state pointers).
 
-``conv_update``, ``prefill`` and ``decode`` derive pointers, strides and views from
+``conv_update``, ``prefill``, ``decode`` and ``decode_fused`` derive pointers, strides and views from
 torch tensors and call the library; all arithmetic happens in the HIP kernels.
 """
 
@@ -102,10 +102,24 @@ def decode(dims: gdn_dims, y: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
                             state_ptrs.numel(), stream)
 
 
+def decode_fused(dims: gdn_dims, x: torch.Tensor, conv_w: torch.Tensor, conv_b, g: torch.Tensor, beta: torch.Tensor,
+                 o: torch.Tensor, state_ptrs: torch.Tensor, conv_state_ptrs: torch.Tensor, counters: torch.Tensor,
+                 stream=None) -> None:
+    """conv_update (decode mode) + decode in one launch; counters from decode_counters()."""
+    _lib.gdn_decode_fused(dims, x, x.stride(0), conv_w, conv_b, g, beta, o, state_ptrs, conv_state_ptrs,
+                          state_ptrs.numel(), counters, counters.numel() * counters.element_size(), stream)
+
+
+def decode_counters(dims: gdn_dims, m: int, device="cuda") -> torch.Tensor:
+    """Zero-filled counter workspace of decode_fused for up to m slots (left zero by every call)."""
+    n = _lib.gdn_decode_fused_workspace_size(dims, m) // 4
+    return torch.zeros(max(n, 1), dtype=torch.int32, device=device)
+
+
 def prefill_workspace(dims: gdn_dims, num_seqs: int, total_tokens: int, device="cuda") -> torch.Tensor:
     nbytes = _lib.gdn_prefill_workspace_size(dims, num_seqs, total_tokens)
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-__all__ = ["SlotPool", "channels", "conv_update", "decode", "prefill", "prefill_workspace", "qkv_views",
-           "torch_in_dtype", "GDN_F32", "GDN_BF16"]
+__all__ = ["SlotPool", "channels", "conv_update", "decode", "decode_counters", "decode_fused", "prefill",
+           "prefill_workspace", "qkv_views", "torch_in_dtype", "GDN_F32", "GDN_BF16"]

@@ -176,6 +176,37 @@ gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_st
                               void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * gdn_decode_fused_workspace_size -- bytes of the counter workspace gdn_decode_fused
+ * needs for up to m slots (m * Hk int32 counters), written to *bytes.
+ */
+gdn_status gdn_decode_fused_workspace_size(const gdn_dims* dims, int32_t m, size_t* bytes);
+
+/* ---------------------------------------------------------------------------------
+ * gdn_decode_fused -- the whole decode step of a layer in one launch: the conv of
+ * gdn_conv_update in decode mode (token i <-> slot i), its conv-state commit, then
+ * gdn_decode_batched on the conv output, which never leaves the chip. o, the states
+ * and the conv states come out bit-identical to those two calls in sequence. (The same
+ * passages as gdn_conv_update and gdn_decode_batched: "System Design", "GDN Kernel
+ * Dispatch Detail", decode branch: conv state update, then the decay and delta write,
+ * then the query against the state.)
+ *
+ *  x, x_stride, conv_w, conv_b   as gdn_conv_update (x: [m][C] in_dtype).
+ *  g, beta, o                    as gdn_decode_batched.
+ *  state_ptrs, conv_state_ptrs   device u64 [m]: slot i's recurrent state and conv
+ *             state. Slot i is inactive (nothing read or written, o rows untouched) when
+ *             either entry is 0.
+ *  workspace  device int32 counters, at least gdn_decode_fused_workspace_size(dims, m)
+ *             bytes, 4-byte aligned. They must be zero before the first call (e.g.
+ *             zero-filled once when allocated); every call leaves them zero again. Calls
+ *             that share a workspace must not overlap in time (same stream is fine).
+ *  Alignment: x, conv_w, conv_b 16-byte aligned, x_stride a multiple of 16 bytes.
+ */
+gdn_status gdn_decode_fused(const gdn_dims* dims, const void* x, int64_t x_stride, const void* conv_w,
+                            const void* conv_b, const float* g, const float* beta, float* o,
+                            const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, int32_t m,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * gdn_slot_pointers -- build a device u64 pointer array from slot indices, on the
  * device: out_ptrs[i] = pool_base + slot_idx[i] * slot_bytes, or 0 when slot_idx[i]
  * is outside [0, pool_slots) (an inactive slot). The slot pool is one caller-owned

@@ -109,6 +109,34 @@ def test_decode_argument_checks():
     gdn.gdn_decode_batched(d, *ok, FAKE, 0, 0)
 
 
+def test_decode_fused_argument_checks():
+    d = dims()
+    C = 8192
+    need = gdn.gdn_decode_fused_workspace_size(d, 4)
+    assert need == 4 * 16 * 4
+    assert _status(gdn.gdn_decode_fused_workspace_size, d, -1)[0] == _lib.GDN_ERR_SHAPE
+    ok_pre = (FAKE, C, FAKE, None, FAKE, FAKE, FAKE)  # x, x_stride, conv_w, conv_b, g, beta, o
+    # every pointer array is required
+    assert _status(gdn.gdn_decode_fused, d, *ok_pre, None, FAKE, 4, FAKE, need, 0)[0] == _lib.GDN_ERR_NULL
+    assert _status(gdn.gdn_decode_fused, d, *ok_pre, FAKE, None, 4, FAKE, need, 0)[0] == _lib.GDN_ERR_NULL
+    assert _status(gdn.gdn_decode_fused, d, None, C, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, need,
+                   0)[0] == _lib.GDN_ERR_NULL
+    # workspace missing, too small or misaligned
+    assert _status(gdn.gdn_decode_fused, d, *ok_pre, FAKE, FAKE, 4, None, need, 0)[0] == _lib.GDN_ERR_WORKSPACE
+    assert _status(gdn.gdn_decode_fused, d, *ok_pre, FAKE, FAKE, 4, FAKE, need - 4, 0)[0] == _lib.GDN_ERR_WORKSPACE
+    assert _status(gdn.gdn_decode_fused, d, *ok_pre, FAKE, FAKE, 4, FAKE + 2, need, 0)[0] == _lib.GDN_ERR_WORKSPACE
+    # x stride below C, or not a multiple of 16 bytes; misaligned x
+    assert _status(gdn.gdn_decode_fused, d, FAKE, C - 8, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, need,
+                   0)[0] == _lib.GDN_ERR_SHAPE
+    assert _status(gdn.gdn_decode_fused, d, FAKE, C + 4, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, need,
+                   0)[0] == _lib.GDN_ERR_ALIGN
+    assert _status(gdn.gdn_decode_fused, d, FAKE + 8, C, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, need,
+                   0)[0] == _lib.GDN_ERR_ALIGN
+    assert _status(gdn.gdn_decode_fused, d, *ok_pre, FAKE, FAKE, -1, FAKE, need, 0)[0] == _lib.GDN_ERR_SHAPE
+    # m = 0 launches nothing
+    gdn.gdn_decode_fused(d, *ok_pre, FAKE, FAKE, 0, None, 0, 0)
+
+
 def test_conv_argument_checks():
     d = dims()
     C = 8192
