@@ -41,6 +41,9 @@ constexpr int kThreads = 512;      // intra-chunk workgroup: 8 waves
 constexpr int kWaves = 8;
 constexpr int kInterThreads = 512; // inter-chunk workgroup: 8 waves
 constexpr int kDVB = 16;           // state rows per inter-chunk workgroup
+// Inter-chunk variant choice: with at least two workgroups per CU (MI355X: 256 CUs) the
+// lean, two-per-CU variant runs; below that the one-per-CU variant that prefetches.
+constexpr int kInterPrefetchMaxCUs = 256;
 constexpr int kMetaThreads = 1024;
 constexpr int kLptMaxSeqs = 256;   // longest-first ordering only up to this many sequences
 
@@ -505,8 +508,8 @@ struct ChunkIn {
   int n;        // tokens in the chunk
 };
 
-template <int POL, int D, int C>
-__global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs a, Workspace w) {
+template <int POL, int D, int C, bool PF>
+__global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(PrefillArgs a, Workspace w) {
   using M = Mma<POL>;
   using SP = Split<POL>;
   using F = typename M::Frag;
@@ -693,17 +696,28 @@ __global__ __launch_bounds__(kInterThreads) void inter_chunk_kernel(PrefillArgs 
     __syncthreads();
   };
 
-  // Two operand buffers, one chunk ahead. The prefetch index is clamped rather than
-  // guarded (the last chunk is simply read twice), so no load sits under a branch.
-  In in0, in1;
-  load(0, in0);
-  __syncthreads();  // Sl filled
-  for (int c = 0; c < nch; c += 2) {
-    load(min(c + 1, nch - 1), in1);
-    process(c, in0);
-    if (c + 1 >= nch) break;
-    load(min(c + 2, nch - 1), in0);
-    process(c + 1, in1);
+  if constexpr (PF) {
+    // Two operand buffers, one chunk ahead. The prefetch index is clamped rather than
+    // guarded (the last chunk is simply read twice), so no load sits under a branch.
+    In in0, in1;
+    load(0, in0);
+    __syncthreads();  // Sl filled
+    for (int c = 0; c < nch; c += 2) {
+      load(min(c + 1, nch - 1), in1);
+      process(c, in0);
+      if (c + 1 >= nch) break;
+      load(min(c + 2, nch - 1), in0);
+      process(c + 1, in1);
+    }
+  } else {
+    // One operand buffer, loaded at the top of each step: half the registers, so two
+    // workgroups share a CU and each one's load latency is covered by the other's work.
+    In in0;
+    __syncthreads();  // Sl filled
+    for (int c = 0; c < nch; ++c) {
+      load(c, in0);
+      process(c, in0);
+    }
   }
 
   if (has_tile) {
@@ -719,7 +733,10 @@ hipError_t launch_chunked(const PrefillArgs& a, const Workspace& w, hipStream_t 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned blocks = static_cast<unsigned>((D / kDVB) * a.r.hv * a.num_seqs);
-  inter_chunk_kernel<POL, D, C><<<blocks, kInterThreads, 0, s>>>(a, w);
+  if (blocks >= 2 * kInterPrefetchMaxCUs)
+    inter_chunk_kernel<POL, D, C, false><<<blocks, kInterThreads, 0, s>>>(a, w);
+  else
+    inter_chunk_kernel<POL, D, C, true><<<blocks, kInterThreads, 0, s>>>(a, w);
   return hipGetLastError();
 }
 

@@ -152,6 +152,26 @@ def test_packed_equals_solo_bit_exact():
         np.testing.assert_array_equal(S1[0].view(np.int32), S[s].view(np.int32))
 
 
+def test_one_and_two_workgroups_per_cu_variants_bit_exact():
+    """The inter-chunk launch has two variants with the same arithmetic: below 512
+    workgroups one per CU with the next chunk's operands prefetched, from 512 on two per
+    CU without prefetch. At 16/32 heads and d = 128 a sequence alone has 256 workgroups and
+    packed with a second sequence 512, so the two runs take different variants; the
+    sequence's o and state must agree bit for bit."""
+    announce("prefill inter variants (prefetch vs two per CU) bit-exact")
+    lens = (300, 130)
+    inp = make_prefill(1, lens=lens, s0_std=0.02, conv_state_std=1.0)
+    o, S = PrefillRun(inp).run()
+    solo = dict(inp, x=inp["x"][:300], cu_seqlens=np.array([0, 300], dtype=np.int32),
+                conv_state=inp["conv_state"][:1], S0=inp["S0"][:1], g=inp["g"][:300], beta=inp["beta"][:300],
+                lens=(300,))
+    o1, S1 = PrefillRun(solo).run()
+    np.testing.assert_array_equal(o1.view(np.int32), o[:300].view(np.int32))
+    np.testing.assert_array_equal(S1[0].view(np.int32), S[0].view(np.int32))
+    ref = _oracle(inp, v_heads=[3, 20])
+    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16, heads=[3, 20], label="two per CU")
+
+
 def test_split_and_decode_continuation():
     """prefill(L1) then prefill(L2) and prefill(L) then decode continue the same sequence
     (chunk boundaries differ, so this is a tolerance check against the oracle's full run)."""
