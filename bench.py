@@ -161,19 +161,19 @@ class DecodeRig:
 
 
 class PrefillRig:
-    def __init__(self, cfg: int = 1, device="cuda"):
+    def __init__(self, cfg: int = 1, device="cuda", shape=None, form: int = 0):
         import numpy as np
         import torch
 
         import gated_delta_rule_conv_amd as gdn
         from gen import make_prefill
 
-        inp = make_prefill(cfg)
+        inp = make_prefill(cfg, shape=shape)
         sh = inp["shape"]
         self.sh = sh
         self.lens = list(inp["lens"])
         self.dims = gdn.make_dims(sh.num_k_heads, sh.num_v_heads, sh.head_dim, conv_width=sh.conv_width,
-                                  chunk_size=sh.chunk, in_dtype=gdn.GDN_BF16)
+                                  chunk_size=sh.chunk, in_dtype=gdn.GDN_BF16, prefill_form=form)
         T = inp["x"].shape[0]
         N = len(inp["lens"])
         self.T, self.N = T, N
@@ -378,10 +378,18 @@ def main() -> int:
     prefill = None
     if not args.no_prefill:
         prefill = {}
-        for cfg, name in ((1, "L4096"), (4, "ragged8_T15717")):
+        from gen.inputs import LayerShape
+
+        # the last two: one GPU's share of an 8-way head split of the same layer (2 q/k
+        # heads, 4 v-heads), as the library runs it (chunk-parallel form) and forced to
+        # walk whole sequences
+        share = LayerShape(2, 4, 128, conv_width=4, chunk=64, in_dtype="bf16")
+        runs = [(1, "L4096", None, 0), (4, "ragged8_T15717", None, 0),
+                (1, "L4096_hk2_hv4", share, 0), (1, "L4096_hk2_hv4_whole_sequence", share, 1)]
+        for cfg, name, shape, form in runs:
             if cfg == 4 and args.no_ragged:
                 continue
-            pre = PrefillRig(cfg)
+            pre = PrefillRig(cfg, shape=shape, form=form)
             for _ in range(W):
                 pre.step()
             torch.cuda.synchronize()
@@ -399,7 +407,9 @@ def main() -> int:
                 "frac_of_bf16_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
                 "gflop": round(fl / 1e9, 3),
                 "note": "conv_update (prefill mode) + prefill_chunked (bf16x3 MFMA: 3 bf16 products per "
-                        "algorithmic product)"}
+                        "algorithmic product)" + (f"; {shape.num_k_heads} q/k heads, {shape.num_v_heads} v-heads, "
+                                                 f"{'chunk-parallel' if form == 0 else 'whole-sequence'} form"
+                                                 if shape is not None else "")}
             del pre
             torch.cuda.empty_cache()
             log(f"prefill {name}: {ms:.3f} ms")

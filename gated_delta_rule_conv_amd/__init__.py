@@ -15,6 +15,9 @@ from ._lib import (  # noqa: F401
     GDN_MMA_AUTO,
     GDN_MMA_BF16X3,
     GDN_MMA_FP32,
+    GDN_PREFILL_AUTO,
+    GDN_PREFILL_SEGMENTS,
+    GDN_PREFILL_WHOLE,
     GDNError,
     LIB_PATH,
     gdn_abi_version,

@@ -21,6 +21,7 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_
 GDN_F32, GDN_BF16 = 0, 1
 GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 GDN_MMA_AUTO, GDN_MMA_FP32, GDN_MMA_BF16X3 = 0, 1, 2
+GDN_PREFILL_AUTO, GDN_PREFILL_WHOLE, GDN_PREFILL_SEGMENTS = 0, 1, 2
 
 EXPORTED = ("gdn_conv_update", "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_decode_batched",
             "gdn_decode_fused_workspace_size", "gdn_decode_fused", "gdn_slot_copy", "gdn_slot_pointers",
@@ -40,14 +41,15 @@ class gdn_dims(ctypes.Structure):
         ("mma", ctypes.c_int32),
         ("l2_eps", ctypes.c_float),
         ("scale", ctypes.c_float),
+        ("prefill_form", ctypes.c_int32),
     ]
 
 
 def make_dims(num_k_heads: int, num_v_heads: int, head_dim: int, conv_width: int = 4, chunk_size: int = 64,
               activation: int = GDN_ACT_NONE, in_dtype: int = GDN_BF16, mma: int = GDN_MMA_AUTO,
-              l2_eps: float = 1e-6, scale: float = 1.0) -> gdn_dims:
+              l2_eps: float = 1e-6, scale: float = 1.0, prefill_form: int = 0) -> gdn_dims:
     return gdn_dims(ctypes.sizeof(gdn_dims), num_k_heads, num_v_heads, head_dim, conv_width, chunk_size,
-                    activation, in_dtype, mma, l2_eps, scale)
+                    activation, in_dtype, mma, l2_eps, scale, prefill_form)
 
 
 class GDNError(RuntimeError):

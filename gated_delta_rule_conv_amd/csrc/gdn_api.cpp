@@ -55,6 +55,9 @@ gdn_status check_dims(const gdn_dims* d, const char* fn) {
     return fail(GDN_ERR_DTYPE, "%s: unknown in_dtype %d", fn, d->in_dtype);
   if (d->mma != GDN_MMA_AUTO && d->mma != GDN_MMA_FP32 && d->mma != GDN_MMA_BF16X3)
     return fail(GDN_ERR_DTYPE, "%s: unknown mma policy %d", fn, d->mma);
+  if (d->prefill_form != GDN_PREFILL_AUTO && d->prefill_form != GDN_PREFILL_WHOLE &&
+      d->prefill_form != GDN_PREFILL_SEGMENTS)
+    return fail(GDN_ERR_SHAPE, "%s: unknown prefill_form %d", fn, d->prefill_form);
   if (!(d->l2_eps >= 0.0f) || !(d->l2_eps < 1e30f))
     return fail(GDN_ERR_SHAPE, "%s: l2_eps must be finite and >= 0", fn);
   if (!(d->scale == d->scale) || d->scale > 1e30f || d->scale < -1e30f)
@@ -135,7 +138,7 @@ gdn_status gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, in
   if (!bytes) return fail(GDN_ERR_NULL, "%s: bytes is NULL", fn);
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_SHAPE, "%s: negative count", fn);
   *bytes = gdn::prefill_workspace_bytes(dims->num_k_heads, dims->num_v_heads, dims->head_dim, dims->chunk_size, num_seqs,
-                                      total_tokens);
+                                      total_tokens, dims->prefill_form);
   return GDN_OK;
 }
 
@@ -158,7 +161,7 @@ gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_s
   }
   const size_t need =
       gdn::prefill_workspace_bytes(dims->num_k_heads, dims->num_v_heads, dims->head_dim, dims->chunk_size, num_seqs,
-                                      total_tokens);
+                                      total_tokens, dims->prefill_form);
   if (!workspace || workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, need, workspace_bytes,
                 workspace ? "" : " (NULL)");
@@ -171,6 +174,7 @@ gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_s
   a.num_seqs = num_seqs;
   a.total_tokens = total_tokens;
   a.chunk = dims->chunk_size;
+  a.form = dims->prefill_form;
   a.mma = resolve_mma(dims);
   a.workspace = workspace;
   return hip_status(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)), fn);

@@ -72,11 +72,12 @@ struct PrefillArgs {
   int32_t total_tokens;
   int32_t chunk;
   int32_t mma;  // 1 = fp32, 2 = bf16x3 (resolved)
+  int32_t form;  // gdn_prefill_form
   void* workspace;
 };
 
 size_t prefill_workspace_bytes(int32_t hk, int32_t hv, int32_t d, int32_t chunk, int32_t num_seqs,
-                               int32_t total_tokens);
+                               int32_t total_tokens, int32_t form);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 hipError_t launch_slot_copy(const uint64_t* src, const uint64_t* dst, int64_t bytes, int32_t n, hipStream_t s);

@@ -31,6 +31,9 @@
 //                        last one, whose contraction runs over tokens). The 16-row slices of one head are
 //                        mapped to one XCD so they share K, Q, T and P through its L2.
 
+#include <algorithm>
+#include <cmath>
+
 #include "launch.h"
 #include "mma.h"
 
@@ -53,6 +56,9 @@ constexpr int kLptMaxSeqs = 256;   // longest-first ordering only up to this man
 //                        k = head dim)
 //   per (chunk, v-head): T, then P, as A operands (rows and k = tokens); then gam [C]
 //                        (fp32, padded with gam_{n-1}) and beta [C] (fp32, padded with 0)
+//   chunk-parallel form only (segmented): per (segment, v-head) three d x d fp32
+//   matrices: the segment's start state Z, the transposed linear part M^T of its affine
+//   map S -> S M + B, and B.
 struct Workspace {
   int* n_chunks;
   int4* table;  // (sequence, first token, length, index in sequence)
@@ -62,6 +68,13 @@ struct Workspace {
   char* tp;
   int64_t kq_stride;  // bytes per (chunk, k-head)
   int64_t tp_stride;  // bytes per (chunk, v-head)
+  int segmented;      // chunk-parallel form (else whole sequences)
+  int* n_segs;
+  int* seg_off;       // [N+1] first segment of each sequence
+  int4* seg_table;    // (sequence, first chunk, end chunk, last segment of its sequence?)
+  float* zs;
+  float* mt;
+  float* bt;
 };
 
 inline size_t up256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
@@ -91,14 +104,53 @@ inline size_t tp_stride(int C) {
   return a > b ? a : b;
 }
 
-size_t workspace_bytes(int hk, int hv, int d, int chunk, int num_seqs, int total_tokens) {
-  const size_t mc = max_chunks_of(chunk, num_seqs, total_tokens);
-  return 256 + up256(mc * sizeof(int4)) + up256((static_cast<size_t>(num_seqs) + 1) * sizeof(int)) +
-         up256(static_cast<size_t>(num_seqs) * sizeof(int) + 4) + up256(mc * hk * kq_stride(d, chunk)) +
-         up256(mc * hv * tp_stride(chunk));
+// Chunk-parallel prefill. When a launch has fewer state-row workgroups than CUs (few
+// heads, e.g. one GPU's share of a head-sharded layer, and few sequences), a sequence of
+// n >= 8 chunks is cut into segments of sc chunks. Every segment's affine map
+// S -> S M + B is computed in parallel (rows of the state evolve independently: M's rows
+// are the recurrence run from identity rows with v = 0, B's from zero rows with the real
+// v), a scan over segments gives each segment's start state, and then all segments
+// produce their outputs in parallel: a chain of about 2 sc chunk steps plus one small
+// product per segment instead of n chunk steps. sc is the largest k with k^2 <= n
+// (within [2, 32]), which balances the two (a scan step costs about 0.8 of a chunk step:
+// each streams a 64 KiB map through its CU); it depends on the sequence's own length
+// only, so within this form packing does not change a sequence's segments.
+constexpr int kSegmentBelowWGs = 256;  // MI355X CUs
+constexpr int kSegmentMinChunks = 8;
+
+// form: 0 auto, 1 whole sequences, 2 segments (gdn_prefill_form)
+bool use_segments(int hv, int d, int num_seqs, int form) {
+  if (form != 0) return form == 2;
+  return static_cast<long>(d / kDVB) * hv * num_seqs < kSegmentBelowWGs;
 }
 
-Workspace carve(void* base, int hk, int hv, int d, int chunk, int num_seqs, int total_tokens) {
+// A sequence of nc chunks has at most ceil(nc / 2) segments (sc >= 2), or one; with
+// sum nc <= T / C + N that is at most T / (2 C) + 1.5 N + 1 over a launch.
+inline size_t max_segments_of(int chunk, int num_seqs, int total_tokens) {
+  return static_cast<size_t>(total_tokens) / (2 * static_cast<size_t>(chunk)) + 2 * static_cast<size_t>(num_seqs) + 1;
+}
+
+__device__ __forceinline__ int segment_len(int nc) {
+  if (nc < kSegmentMinChunks) return nc > 0 ? nc : 1;
+  int k = 2;
+  while (k < 32 && (k + 1) * (k + 1) <= nc) ++k;
+  return k;
+}
+
+size_t workspace_bytes(int hk, int hv, int d, int chunk, int num_seqs, int total_tokens, int form) {
+  const size_t mc = max_chunks_of(chunk, num_seqs, total_tokens);
+  size_t b = 256 + up256(mc * sizeof(int4)) + up256((static_cast<size_t>(num_seqs) + 1) * sizeof(int)) +
+             up256(static_cast<size_t>(num_seqs) * sizeof(int) + 4) + up256(mc * hk * kq_stride(d, chunk)) +
+             up256(mc * hv * tp_stride(chunk));
+  if (use_segments(hv, d, num_seqs, form)) {
+    const size_t ns = max_segments_of(chunk, num_seqs, total_tokens);
+    b += 256 + up256((static_cast<size_t>(num_seqs) + 1) * sizeof(int)) + up256(ns * sizeof(int4)) +
+         3 * up256(ns * hv * static_cast<size_t>(d) * d * sizeof(float));
+  }
+  return b;
+}
+
+Workspace carve(void* base, int hk, int hv, int d, int chunk, int num_seqs, int total_tokens, int form) {
   char* p = static_cast<char*>(base);
   const size_t mc = max_chunks_of(chunk, num_seqs, total_tokens);
   Workspace w;
@@ -113,8 +165,29 @@ Workspace carve(void* base, int hk, int hv, int d, int chunk, int num_seqs, int 
   w.kq = p;
   p += up256(mc * hk * kq_stride(d, chunk));
   w.tp = p;
+  p += up256(mc * hv * tp_stride(chunk));
   w.kq_stride = static_cast<int64_t>(kq_stride(d, chunk));
   w.tp_stride = static_cast<int64_t>(tp_stride(chunk));
+  w.segmented = use_segments(hv, d, num_seqs, form) ? 1 : 0;
+  w.n_segs = nullptr;
+  w.seg_off = nullptr;
+  w.seg_table = nullptr;
+  w.zs = w.mt = w.bt = nullptr;
+  if (w.segmented) {
+    const size_t ns = max_segments_of(chunk, num_seqs, total_tokens);
+    const size_t mat = up256(ns * hv * static_cast<size_t>(d) * d * sizeof(float));
+    w.n_segs = reinterpret_cast<int*>(p);
+    p += 256;
+    w.seg_off = reinterpret_cast<int*>(p);
+    p += up256((static_cast<size_t>(num_seqs) + 1) * sizeof(int));
+    w.seg_table = reinterpret_cast<int4*>(p);
+    p += up256(ns * sizeof(int4));
+    w.zs = reinterpret_cast<float*>(p);
+    p += mat;
+    w.mt = reinterpret_cast<float*>(p);
+    p += mat;
+    w.bt = reinterpret_cast<float*>(p);
+  }
   return w;
 }
 
@@ -126,9 +199,11 @@ Workspace carve(void* base, int hk, int hv, int d, int chunk, int num_seqs, int 
 __global__ __launch_bounds__(kMetaThreads) void chunk_table_kernel(const int* __restrict__ cu, int N, int C,
                                                                   Workspace w) {
   __shared__ int scan[kMetaThreads];
+  __shared__ int scan_seg[kMetaThreads];
   __shared__ int lens[kLptMaxSeqs];
   const int tid = threadIdx.x;
-  int carry = 0;
+  const bool segmented = w.segmented != 0;
+  int carry = 0, carry_seg = 0;
   for (int base = 0; base < N; base += kMetaThreads) {
     const int s = base + tid;
     int start = 0, len = 0;
@@ -137,26 +212,42 @@ __global__ __launch_bounds__(kMetaThreads) void chunk_table_kernel(const int* __
       len = cu[s + 1] - start;
     }
     const int nc = (len + C - 1) / C;
+    const int sc = segment_len(nc);
+    const int ns = segmented ? (nc + sc - 1) / sc : 0;  // segments of this sequence
     if (N <= kLptMaxSeqs && s < N) lens[s] = len;
     scan[tid] = nc;
+    scan_seg[tid] = ns;
     __syncthreads();
     for (int off = 1; off < kMetaThreads; off <<= 1) {
       const int add = tid >= off ? scan[tid - off] : 0;
+      const int add_seg = tid >= off ? scan_seg[tid - off] : 0;
       __syncthreads();
       scan[tid] += add;
+      scan_seg[tid] += add_seg;
       __syncthreads();
     }
     const int first = carry + scan[tid] - nc;  // this sequence's first chunk index
+    const int first_seg = carry_seg + scan_seg[tid] - ns;
     if (s < N) {
       w.chunk_off[s] = first;
       for (int c = 0; c < nc; ++c) w.table[first + c] = make_int4(s, start + c * C, min(C, len - c * C), c);
+      if (segmented) {
+        w.seg_off[s] = first_seg;
+        for (int g = 0; g < ns; ++g)
+          w.seg_table[first_seg + g] = make_int4(s, g * sc, min(nc, (g + 1) * sc), g == ns - 1);
+      }
     }
     carry += scan[kMetaThreads - 1];
+    carry_seg += scan_seg[kMetaThreads - 1];
     __syncthreads();
   }
   if (tid == 0) {
     w.chunk_off[N] = carry;
     *w.n_chunks = carry;
+    if (segmented) {
+      w.seg_off[N] = carry_seg;
+      *w.n_segs = carry_seg;
+    }
   }
   // longest sequence first, so its long chain of chunks starts with the first wave of
   // workgroups (ties by index)
@@ -508,7 +599,17 @@ struct ChunkIn {
   int n;        // tokens in the chunk
 };
 
-template <int POL, int D, int C, bool PF>
+// What one launch of the inter-chunk kernel covers:
+//   kModeWhole    : whole sequences, from the state in place to the final state, with outputs;
+//   kModeTransfer : one segment's affine map: row blocks [0, d/16) run from identity rows
+//                   with v = 0 and give M, the rest run from zero rows and give B; no outputs;
+//   kModeSegment  : one segment's outputs, from its start state Z; the last segment of a
+//                   sequence writes the final state.
+constexpr int kModeWhole = 0;
+constexpr int kModeTransfer = 1;
+constexpr int kModeSegment = 2;
+
+template <int POL, int D, int C, bool PF, int MODE>
 __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(PrefillArgs a, Workspace w) {
   using M = Mma<POL>;
   using SP = Split<POL>;
@@ -534,21 +635,43 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
   char* Kl = Us + R_BYTES;            // K^           [C][D]    B operand of the update
 
   const RecurArgs& r = a.r;
-  const int per_seq = NBLK * r.hv;
+  constexpr int RB = MODE == kModeTransfer ? 2 * NBLK : NBLK;  // row blocks per head
+  const int per_unit = RB * r.hv;
   const int L = blockIdx.x;
-  const int zi = L / per_seq;
-  const int rem = L % per_seq;
+  const int zi = L / per_unit;
+  const int rem = L % per_unit;
   // workgroups are dealt round-robin to the 8 XCDs: give the slices of one head
   // consecutive virtual ids on one XCD so they share that XCD's L2
-  const int vid = (per_seq % 8 == 0) ? (rem % 8) * (per_seq / 8) + rem / 8 : rem;
-  const int j = vid / NBLK, blk = vid % NBLK;
-  const int s = w.order[zi];
+  const int vid = (per_unit % 8 == 0) ? (rem % 8) * (per_unit / 8) + rem / 8 : rem;
+  const int j = vid / RB, rb = vid % RB;
+  int s, seg = 0, c_begin = 0, c_seg_end = 0;
+  bool last_seg = true;
+  if constexpr (MODE == kModeWhole) {
+    s = w.order[zi];
+  } else {
+    if (zi >= *w.n_segs) return;
+    const int4 e = w.seg_table[zi];
+    s = e.x;
+    seg = zi;
+    c_begin = e.y;
+    c_seg_end = e.z;
+    last_seg = e.w != 0;
+    if (MODE == kModeTransfer && last_seg) return;  // (the last segment's map is never used)
+  }
+  const bool mrow = MODE == kModeTransfer && rb < NBLK;  // a row block of M (else of B, or the state)
+  const int blk = MODE == kModeTransfer && !mrow ? rb - NBLK : rb;
   const int start = a.cu_seqlens[s];
   const int len = a.cu_seqlens[s + 1] - start;
   if (len <= 0) return;
   const uint64_t sptr = r.state_ptrs[s];
   if (sptr == 0) return;
   const int h = j / (r.hv / r.hk);
+  const float vscale = mrow ? 0.f : 1.f;  // M's rows see v = 0
+  // (In transfer mode the Q-side waves still load and compute, and only skip the o
+  // store: one code shape for all modes keeps the registers within two workgroups per
+  // CU; skipping their work made the compiler need 161.)
+  constexpr bool kOut = MODE != kModeTransfer;  // outputs
+  const size_t mat = static_cast<size_t>(D) * D;
   float* Sg = reinterpret_cast<float*>(sptr) + (static_cast<int64_t>(j) * D + blk * kDVB) * D;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -561,15 +684,24 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
   const bool has_tile = ST >= 8 || wave < ST;  // this wave updates state tile `wave`
   constexpr bool kFullK = C % KSTEP == 0;      // every lane's k-slice of a chunk row is in range
   const int nch = (len + C - 1) / C;
+  const int c_end = MODE == kModeWhole ? nch : c_seg_end;
   const int cbase = w.chunk_off[s];
 
   f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
   if (has_tile) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const float v = Sg[(4 * lg + rr) * D + wave * 16 + l16];
+      const int row = 4 * lg + rr, col = wave * 16 + l16;
+      float v;
+      if constexpr (MODE == kModeWhole) {
+        v = Sg[row * D + col];
+      } else if constexpr (MODE == kModeSegment) {
+        v = w.zs[(static_cast<size_t>(seg) * r.hv + j) * mat + static_cast<size_t>(blk * kDVB + row) * D + col];
+      } else {
+        v = (mrow && blk * kDVB + row == col) ? 1.f : 0.f;
+      }
       sacc[rr] = v;
-      SP::store1(Sl, kDVB, SLD, 4 * lg + rr, wave * 16 + l16, v);
+      SP::store1(Sl, kDVB, SLD, row, col, v);
     }
   }
 
@@ -602,7 +734,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
         // are masked where the value is used (using a load in the step that issues it
         // would wait for every load before it, the prefetch included)
         const int tc = min(t, in.n - 1);
-        in.vv[rr] = r.v[static_cast<int64_t>(t0 + tc) * r.v_stride + j * D + blk * kDVB + l16];
+        in.vv[rr] = vscale * r.v[static_cast<int64_t>(t0 + tc) * r.v_stride + j * D + blk * kDVB + l16];
       }
     }
   };
@@ -671,7 +803,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int t = tt * 16 + 4 * lg + rr;
-        if (t < in.n) r.o[(static_cast<int64_t>(t0 + t) * r.hv + j) * D + blk * kDVB + l16] = oacc[rr];
+        if (kOut && t < in.n) r.o[(static_cast<int64_t>(t0 + t) * r.hv + j) * D + blk * kDVB + l16] = oacc[rr];
       }
     }
     if (has_tile) {
@@ -700,13 +832,13 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
     // Two operand buffers, one chunk ahead. The prefetch index is clamped rather than
     // guarded (the last chunk is simply read twice), so no load sits under a branch.
     In in0, in1;
-    load(0, in0);
+    load(c_begin, in0);
     __syncthreads();  // Sl filled
-    for (int c = 0; c < nch; c += 2) {
-      load(min(c + 1, nch - 1), in1);
+    for (int c = c_begin; c < c_end; c += 2) {
+      load(min(c + 1, c_end - 1), in1);
       process(c, in0);
-      if (c + 1 >= nch) break;
-      load(min(c + 2, nch - 1), in0);
+      if (c + 1 >= c_end) break;
+      load(min(c + 2, c_end - 1), in0);
       process(c + 1, in1);
     }
   } else {
@@ -714,15 +846,142 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
     // workgroups share a CU and each one's load latency is covered by the other's work.
     In in0;
     __syncthreads();  // Sl filled
-    for (int c = 0; c < nch; ++c) {
+    for (int c = c_begin; c < c_end; ++c) {
       load(c, in0);
       process(c, in0);
     }
   }
 
   if (has_tile) {
+    if constexpr (MODE == kModeTransfer) {
+      if (mrow) {
+        // M^T[n][i] for rows i = blk*16 + 4 lg + rr (consecutive) and column n of M
+        float* mt = w.mt + (static_cast<size_t>(seg) * r.hv + j) * mat;
+        *reinterpret_cast<float4*>(mt + static_cast<size_t>(wave * 16 + l16) * D + blk * kDVB + 4 * lg) =
+            make_float4(sacc[0], sacc[1], sacc[2], sacc[3]);
+      } else {
+        float* bt = w.bt + (static_cast<size_t>(seg) * r.hv + j) * mat + static_cast<size_t>(blk * kDVB) * D;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) Sg[(4 * lg + rr) * D + wave * 16 + l16] = sacc[rr];
+        for (int rr = 0; rr < 4; ++rr) bt[(4 * lg + rr) * D + wave * 16 + l16] = sacc[rr];
+      }
+    } else if (last_seg) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) Sg[(4 * lg + rr) * D + wave * 16 + l16] = sacc[rr];
+    }
+  }
+}
+
+// Start states of the segments of the chunk-parallel form: Z_0 = the state in place
+// (copied, so that the segment launch never reads memory it also writes), then
+// Z_{g+1} = Z_g M_g + B_g. One workgroup per (sequence, v-head, 16 state rows); wave w
+// computes columns [16 w, 16 w + 16) of the row slice, with Z in LDS as the A operand
+// and rows of M^T as the B operand. M_g and B_g do not depend on Z, so they are loaded
+// ahead of use, and Z alternates between two LDS buffers (one barrier a step).
+template <int POL, int D>
+struct ScanIn {
+  static constexpr int NV = D / Mma<POL>::KSTEP;
+  float m[NV][Mma<POL>::KPL];  // row n of M^T, this lane's k-slices
+  float b[4];                  // B at this lane's 4 output rows
+};
+
+template <int POL, int D>
+__global__ __launch_bounds__(kInterThreads) void segment_scan_kernel(PrefillArgs a, Workspace w) {
+  using M = Mma<POL>;
+  using SP = Split<POL>;
+  using In = ScanIn<POL, D>;
+  constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
+  constexpr int NBLK = D / kDVB, ST = D / 16, NV = In::NV;
+  constexpr int PADE = POL == kPolBF16X3 ? 8 : 4;
+  constexpr int SLD = D + PADE;
+  constexpr int ZB = kDVB * SLD * 4;
+  __shared__ __attribute__((aligned(16))) char Sl[2 * ZB];
+  const RecurArgs& r = a.r;
+  const int per_seq = NBLK * r.hv;
+  const int s = blockIdx.x / per_seq, rem = blockIdx.x % per_seq;
+  const int j = rem / NBLK, blk = rem % NBLK;
+  if (a.cu_seqlens[s + 1] - a.cu_seqlens[s] <= 0) return;
+  const uint64_t sptr = r.state_ptrs[s];
+  if (sptr == 0) return;
+  const int g0 = w.seg_off[s], ns = w.seg_off[s + 1] - g0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int kl = KPL * lg;
+  const bool has_tile = ST >= 8 || wave < ST;
+  const int col = wave * 16 + l16;
+  const size_t mat = static_cast<size_t>(D) * D;
+  const size_t rows = static_cast<size_t>(blk * kDVB) * D;  // offset of the row slice
+  const float* S0 = reinterpret_cast<const float*>(sptr) + static_cast<size_t>(j) * mat + rows;
+  float* zs = w.zs + (static_cast<size_t>(g0) * r.hv + j) * mat + rows;  // Z_0's slice
+  const size_t zstep = static_cast<size_t>(r.hv) * mat;                  // to the next segment
+
+  auto load = [&](int g, In& in) {
+    const size_t base = (static_cast<size_t>(g0 + g) * r.hv + j) * mat;
+    const float* mrow = w.mt + base + static_cast<size_t>(col) * D;  // row n = col of M^T
+#pragma unroll
+    for (int v = 0; v < NV; ++v) load_k<KPL>(mrow + kl + v * KSTEP, in.m[v]);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) in.b[rr] = w.bt[base + rows + (4 * lg + rr) * D + col];
+  };
+  // Z_{g+1} = Z_g M_g + B_g from buffer `cur` of Sl into the other one and into zs
+  auto step = [&](int g, const In& in, int cur) {
+    const char* zin = Sl + cur * ZB;
+    char* zout = Sl + (cur ^ 1) * ZB;
+    f32x4 a3[3];
+    zero3(a3);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) M::mma3(a3, SP::load(zin, kDVB, SLD, l16, kl + v * KSTEP), M::frag(in.m[v]));
+    const f32x4 prod = total(a3);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float z = in.b[rr] + prod[rr];
+      SP::store1(zout, kDVB, SLD, 4 * lg + rr, col, z);
+      zs[static_cast<size_t>(g + 1) * zstep + (4 * lg + rr) * D + col] = z;
+    }
+  };
+
+  if (has_tile) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float v = S0[(4 * lg + rr) * D + col];
+      SP::store1(Sl, kDVB, SLD, 4 * lg + rr, col, v);
+      zs[(4 * lg + rr) * D + col] = v;
+    }
+  }
+  // M_g and B_g come from memory written by the previous launch (about 2 us away), so
+  // they are loaded three steps ahead, into four rotating register buffers; prefetch
+  // indices are clamped, not guarded (the last step's operands may be read again).
+  const int nsteps = ns - 1;
+  In b0, b1, b2, b3;
+  if (has_tile && nsteps > 0) {
+    load(0, b0);
+    load(min(1, nsteps - 1), b1);
+    load(min(2, nsteps - 1), b2);
+  }
+  __syncthreads();
+  for (int g = 0; g < nsteps; g += 4) {
+    if (has_tile) {
+      load(min(g + 3, nsteps - 1), b3);
+      step(g, b0, 0);
+    }
+    __syncthreads();
+    if (g + 1 >= nsteps) break;
+    if (has_tile) {
+      load(min(g + 4, nsteps - 1), b0);
+      step(g + 1, b1, 1);
+    }
+    __syncthreads();
+    if (g + 2 >= nsteps) break;
+    if (has_tile) {
+      load(min(g + 5, nsteps - 1), b1);
+      step(g + 2, b2, 0);
+    }
+    __syncthreads();
+    if (g + 3 >= nsteps) break;
+    if (has_tile) {
+      load(min(g + 6, nsteps - 1), b2);
+      step(g + 3, b3, 1);
+    }
+    __syncthreads();
   }
 }
 
@@ -732,11 +991,26 @@ hipError_t launch_chunked(const PrefillArgs& a, const Workspace& w, hipStream_t 
   intra_chunk_kernel<POL, D, C><<<dim3(static_cast<unsigned>(mc), a.r.hk), kThreads, 0, s>>>(a, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned blocks = static_cast<unsigned>((D / kDVB) * a.r.hv * a.num_seqs);
+  constexpr int NBLK = D / kDVB;
+  if (w.segmented) {
+    // chunk-parallel form: segment maps, then the scan, then every segment's outputs
+    const size_t ns = max_segments_of(C, a.num_seqs, a.total_tokens);
+    inter_chunk_kernel<POL, D, C, false, kModeTransfer>
+        <<<static_cast<unsigned>(ns * a.r.hv * 2 * NBLK), kInterThreads, 0, s>>>(a, w);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    segment_scan_kernel<POL, D><<<static_cast<unsigned>(a.num_seqs * a.r.hv * NBLK), kInterThreads, 0, s>>>(a, w);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    inter_chunk_kernel<POL, D, C, false, kModeSegment>
+        <<<static_cast<unsigned>(ns * a.r.hv * NBLK), kInterThreads, 0, s>>>(a, w);
+    return hipGetLastError();
+  }
+  const unsigned blocks = static_cast<unsigned>(NBLK * a.r.hv * a.num_seqs);
   if (blocks >= 2 * kInterPrefetchMaxCUs)
-    inter_chunk_kernel<POL, D, C, false><<<blocks, kInterThreads, 0, s>>>(a, w);
+    inter_chunk_kernel<POL, D, C, false, kModeWhole><<<blocks, kInterThreads, 0, s>>>(a, w);
   else
-    inter_chunk_kernel<POL, D, C, true><<<blocks, kInterThreads, 0, s>>>(a, w);
+    inter_chunk_kernel<POL, D, C, true, kModeWhole><<<blocks, kInterThreads, 0, s>>>(a, w);
   return hipGetLastError();
 }
 
@@ -761,13 +1035,13 @@ hipError_t by_dim(const PrefillArgs& a, const Workspace& w, hipStream_t s) {
 }  // namespace
 
 size_t prefill_workspace_bytes(int32_t hk, int32_t hv, int32_t d, int32_t chunk, int32_t num_seqs,
-                               int32_t total_tokens) {
-  return workspace_bytes(hk, hv, d, chunk, num_seqs, total_tokens);
+                               int32_t total_tokens, int32_t form) {
+  return workspace_bytes(hk, hv, d, chunk, num_seqs, total_tokens, form);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (a.num_seqs == 0 || a.total_tokens == 0) return hipSuccess;
-  const Workspace w = carve(a.workspace, a.r.hk, a.r.hv, a.r.d, a.chunk, a.num_seqs, a.total_tokens);
+  const Workspace w = carve(a.workspace, a.r.hk, a.r.hv, a.r.d, a.chunk, a.num_seqs, a.total_tokens, a.form);
   chunk_table_kernel<<<1, kMetaThreads, 0, s>>>(a.cu_seqlens, a.num_seqs, a.chunk, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -69,6 +69,20 @@ typedef enum gdn_activation { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_activatio
  *           ("bf16x3", Henry, Tang & Heinecke, ARITH 2019). */
 typedef enum gdn_mma { GDN_MMA_AUTO = 0, GDN_MMA_FP32 = 1, GDN_MMA_BF16X3 = 2 } gdn_mma;
 
+/* How gdn_prefill_chunked walks a sequence's chunks.
+ *  WHOLE    : one pass over every sequence's chunks in order, the state slice resident.
+ *  SEGMENTS : chunk-parallel: a sequence of 8 or more chunks is cut into segments (their
+ *             length set by the sequence's own chunk count n: the largest k with
+ *             k^2 <= n, within [2, 32]); each segment's affine state map S -> S M + B
+ *             is computed in parallel, a scan gives every segment's start state, then all
+ *             segments produce their outputs in parallel. More arithmetic, a much shorter
+ *             sequential chain: for launches too small to fill the GPU.
+ *  AUTO     : SEGMENTS when (d / 16) * Hv * num_seqs is below 256 (fewer state-row
+ *             workgroups than MI355X CUs), else WHOLE.
+ * The two forms agree to rounding; within one form a sequence's result does not depend
+ * on what else is packed with it. */
+typedef enum gdn_prefill_form { GDN_PREFILL_AUTO = 0, GDN_PREFILL_WHOLE = 1, GDN_PREFILL_SEGMENTS = 2 } gdn_prefill_form;
+
 /* Layer dimensions and options, passed by pointer. struct_size must be
  * sizeof(gdn_dims) as compiled by the caller (lets the struct grow later). */
 typedef struct gdn_dims {
@@ -83,6 +97,7 @@ typedef struct gdn_dims {
   int32_t mma;         /* gdn_mma */
   float l2_eps;        /* k^ = k / sqrt(|k|^2 + l2_eps); q^ likewise, then times scale */
   float scale;         /* multiplies q^ (1.0 = no scaling) */
+  int32_t prefill_form; /* gdn_prefill_form */
 } gdn_dims;
 
 /* Conv channel count C = 2*Hk*d + Hv*d, channels ordered [q heads | k heads | v heads]. */

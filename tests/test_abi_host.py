@@ -34,8 +34,8 @@ def test_header_symbols_are_exported():
 
 
 def test_abi_version_and_struct_size():
-    assert gdn.gdn_abi_version() == 1
-    assert ctypes.sizeof(_lib.gdn_dims) == 11 * 4
+    assert gdn.gdn_abi_version() == 2
+    assert ctypes.sizeof(_lib.gdn_dims) == 12 * 4
 
 
 def dims(**kw):
@@ -61,6 +61,7 @@ def _status(fn, *args):
     (dict(activation=3), _lib.GDN_ERR_DTYPE),
     (dict(mma=9), _lib.GDN_ERR_DTYPE),
     (dict(l2_eps=-1.0), _lib.GDN_ERR_SHAPE),
+    (dict(prefill_form=3), _lib.GDN_ERR_SHAPE),
 ])
 def test_bad_dims_rejected_everywhere(kw, status):
     d = dims(**kw)
@@ -178,6 +179,26 @@ def test_prefill_workspace_and_checks():
     assert _status(gdn.gdn_prefill_chunked, d, *qkv, FAKE, 0, 5, FAKE, FAKE, need, 0)[0] == _lib.GDN_ERR_SHAPE
     # no sequences: no-op
     gdn.gdn_prefill_chunked(d, *qkv, FAKE, 0, 0, FAKE, None, 0, 0)
+
+
+def test_prefill_form_workspace():
+    """The chunk-parallel form needs room for per-segment state maps; AUTO takes it below
+    256 state-row workgroups ((d / 16) * Hv * num_seqs) and matches the explicit choice."""
+    few = dict(num_k_heads=2, num_v_heads=4)  # 8 * 4 = 32 workgroups per sequence
+    whole = gdn.gdn_prefill_workspace_size(dims(**few, prefill_form=_lib.GDN_PREFILL_WHOLE), 1, 4096)
+    segs = gdn.gdn_prefill_workspace_size(dims(**few, prefill_form=_lib.GDN_PREFILL_SEGMENTS), 1, 4096)
+    auto = gdn.gdn_prefill_workspace_size(dims(**few), 1, 4096)
+    assert segs > whole and auto == segs
+    # 8 sequences of 32 workgroups fill 256 CUs: AUTO keeps whole sequences
+    assert gdn.gdn_prefill_workspace_size(dims(**few), 8, 4096) == \
+        gdn.gdn_prefill_workspace_size(dims(**few, prefill_form=_lib.GDN_PREFILL_WHOLE), 8, 4096)
+    # the 16/32-head layer has 256 workgroups per sequence: whole sequences
+    assert gdn.gdn_prefill_workspace_size(dims(), 1, 4096) == \
+        gdn.gdn_prefill_workspace_size(dims(prefill_form=_lib.GDN_PREFILL_WHOLE), 1, 4096)
+    # room for the largest possible number of segments: T / (2 C) + 2 N + 1 state maps of
+    # 3 x d x d fp32 per v-head
+    extra = segs - whole
+    assert extra >= (4096 // 128 + 3) * 4 * 3 * 128 * 128 * 4
 
 
 def test_slot_pointer_checks():

@@ -18,25 +18,25 @@ from tests.gpu_helpers import (TOL_BF16, TOL_F32, announce, bits_of, max_block_e
 pytestmark = pytest.mark.gpu
 
 
-def _dims(shape, act=0, mma=0):
+def _dims(shape, act=0, mma=0, form=0):
     import gated_delta_rule_conv_amd as gdn
 
     return gdn.make_dims(shape.num_k_heads, shape.num_v_heads, shape.head_dim, conv_width=shape.conv_width,
-                         chunk_size=shape.chunk, activation=act, mma=mma,
+                         chunk_size=shape.chunk, activation=act, mma=mma, prefill_form=form,
                          in_dtype=gdn.GDN_BF16 if shape.in_dtype == "bf16" else gdn.GDN_F32)
 
 
 class PrefillRun:
     """Device copies of one packed batch; run() does conv + prefill through the C ABI."""
 
-    def __init__(self, inp, act=0, mma=0, g=None):
+    def __init__(self, inp, act=0, mma=0, g=None, form=0):
         import torch
 
         import gated_delta_rule_conv_amd as gdn
 
         sh = inp["shape"]
         self.inp, self.sh = inp, sh
-        self.dims = _dims(sh, act, mma)
+        self.dims = _dims(sh, act, mma, form)
         self.N = len(inp["lens"])
         self.T = int(inp["cu_seqlens"][-1])
         self.pool = gdn.SlotPool(self.dims, max(self.N, 1), state=to_dev(inp["S0"], "f32"),
