@@ -17,19 +17,25 @@
 // Every decay factor is exp of gam_t - gam_s with t >= s (or gam alone, <= 0): nothing
 // can overflow, so no clamp is needed.
 //
-// Three launches, in stream order:
+// Launches, in stream order:
 //   chunk_table_kernel : cu_seqlens -> chunk table (sequence, start, length), per-sequence
-//                        chunk offsets and a longest-first sequence order, on the device.
+//                        chunk offsets, a longest-first sequence order and (chunk-parallel
+//                        form) the segment table, on the device.
 //   intra_chunk_kernel : one workgroup per (chunk, k-head), all chunks in parallel:
 //                        normalised K, Q in LDS; K K^T and Q K^T on MFMA; for each v-head
 //                        sharing the k-head: the decay mask, A, T by blocked (16x16)
-//                        forward substitution, and P. T and P go to the workspace.
+//                        forward substitution, and P. K^, Q^, T and P go to the workspace.
 //   inter_chunk_kernel : one workgroup per (sequence, v-head, 16 state rows), walking the
 //                        chunks of its sequence in order with its 16 x d slice of the
 //                        state resident in registers/LDS; the contractions K S^T, Q S^T,
 //                        T R, P U and U^T K run on MFMA (K^ is staged through LDS for the
-//                        last one, whose contraction runs over tokens). The 16-row slices of one head are
-//                        mapped to one XCD so they share K, Q, T and P through its L2.
+//                        last one, whose contraction runs over tokens). The 16-row slices
+//                        of one head are mapped to one XCD so they share K, Q, T and P
+//                        through its L2. Below 512 workgroups one runs per CU and prefetches
+//                        the next chunk's operands; from 512 on two share a CU instead.
+// In the chunk-parallel form the last launch is replaced by three: the inter-chunk kernel
+// computing every segment's affine state map, segment_scan_kernel forming the segments'
+// start states, and the inter-chunk kernel producing every segment's outputs.
 
 #include <algorithm>
 #include <cmath>
@@ -327,6 +333,12 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int group = r.hv / r.hk;
+  float g_first = 0.f, b_first = 0.f;  // wave 0: g and beta of the first v-head, read early
+  if (wave == 0) {
+    const int tl = min(lane, n - 1);
+    g_first = r.g[static_cast<int64_t>(t0 + tl) * r.hv + h * group];
+    b_first = r.beta[static_cast<int64_t>(t0 + tl) * r.hv + h * group];
+  }
 
   // 1. normalised K and Q rows of the chunk into LDS; rows >= n are zero
   constexpr int TPR = 8;
@@ -428,18 +440,24 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   }
   __syncthreads();
 
-  // 3. per v-head of this k-head's group: decay mask, A, T = (I + A)^-1, P
+  // 3. per v-head of this k-head's group: decay mask, A, T = (I + A)^-1, P. Wave 0 reads
+  // each v-head's g and beta one v-head ahead (the first ones at the start), so their
+  // memory latency stays off the chain of barriers.
+  float g_next = g_first, b_next = b_first;
+  auto load_gb = [&](int j) {
+    const int tl = min(lane, n - 1);  // (a valid token; lanes >= n are masked at use)
+    g_next = r.g[static_cast<int64_t>(t0 + tl) * r.hv + j];
+    b_next = r.beta[static_cast<int64_t>(t0 + tl) * r.hv + j];
+  };
   for (int jj = 0; jj < group; ++jj) {
     const int j = h * group + jj;
     char* tp = w.tp + (static_cast<int64_t>(chunk) * r.hv + j) * w.tp_stride;
     char* pp = tp + static_cast<size_t>(C / 16) * NKF * FIO::BYTES;
     float* gam_out = reinterpret_cast<float*>(pp + static_cast<size_t>(C / 16) * NKF * FIO::BYTES);
     if (wave == 0) {
-      float gv = 0.f, bv = 0.f;
-      if (lane < n) {
-        gv = r.g[static_cast<int64_t>(t0 + lane) * r.hv + j];
-        bv = r.beta[static_cast<int64_t>(t0 + lane) * r.hv + j];
-      }
+      float gv = lane < n ? g_next : 0.f;
+      const float bv = lane < n ? b_next : 0.f;
+      if (jj + 1 < group) load_gb(j + 1);
       gv = wave_inclusive_scan(gv);
       if (lane < C) {
         gam[lane] = gv;

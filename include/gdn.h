@@ -145,8 +145,9 @@ gdn_status gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, in
  * chunked gated-delta-rule kernel on (q, k, v, g, beta, state), then updates the
  * temporal state).
  *
- * Chunks of chunk_size tokens start at each sequence's own first token, so the
- * arithmetic of a sequence does not depend on what else is packed with it.
+ * Chunks of chunk_size tokens start at each sequence's own first token, so within one
+ * dims->prefill_form the arithmetic of a sequence does not depend on what else is packed
+ * with it (AUTO picks the form from Hv, d and num_seqs: see gdn_prefill_form).
  *
  *  q, k       [total_tokens][Hk*d] fp32 (raw conv output; normalised inside), row
  *             strides q_stride, k_stride.   v: [total_tokens][Hv*d] fp32, stride v_stride.
