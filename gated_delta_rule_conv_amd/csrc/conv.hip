@@ -13,6 +13,8 @@
 // The op is purely HBM-bound (8 flops per element), so there is no LDS staging: a
 // thread walks a strip of tokens keeping the K-1 previous rows of z in registers.
 
+#include <type_traits>
+
 #include "conv_taps.h"
 #include "device_common.h"
 #include "launch.h"
@@ -25,24 +27,65 @@ constexpr int kDecThreads = 64;  // decode: one wave per workgroup
 constexpr int kVec = kConvVec;
 constexpr int kStrip = 8;  // tokens per block in prefill mode
 
+// Prefill mode. A wave covers 512 channels: lane l owns channels 4l..4l+3 and
+// 256+4l..256+4l+3 of them, so each of its loads (4 channels) and stores (4 fp32) is one
+// contiguous run across the wave -- 512 B of bf16 input and 1 KiB of fp32 output per
+// instruction. A thread walks a strip of kStrip tokens.
+template <typename T>
+struct Half4 {
+  // raw storage of 4 elements: uint2 for bf16, float4 for fp32
+  typedef typename std::conditional<sizeof(T) == 2, uint2, float4>::type Raw;
+  __device__ __forceinline__ static Raw load(const T* p) { return *reinterpret_cast<const Raw*>(p); }
+  __device__ __forceinline__ static void convert(const Raw& r, float* v) {
+    if constexpr (sizeof(T) == 2) {
+      v[0] = __uint_as_float(r.x << 16);
+      v[1] = __uint_as_float(r.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(r.y << 16);
+      v[3] = __uint_as_float(r.y & 0xFFFF0000u);
+    } else {
+      v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+    }
+  }
+};
+
 template <typename T, int K>
 __global__ __launch_bounds__(kThreads) void conv_prefill_kernel(ConvArgs a) {
-  const int ch0 = (blockIdx.x * kThreads + threadIdx.x) * kVec;
-  if (ch0 >= a.channels) return;
+  using H = Half4<T>;
   const int C = a.channels;
+  const int lane = threadIdx.x & 63;
+  const int wbase = (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 512;
+  if (wbase >= C) return;
+  // channel groups of this lane; past the channel count the loads are clamped to the last
+  // group (valid memory) and the stores are skipped
+  const int chA = wbase + 4 * lane, chB = chA + 256;
+  const bool okA = chA < C, okB = chB < C;
+  const int ldA = min(chA, C - 4), ldB = min(chB, C - 4);
   const T* __restrict__ x = static_cast<const T*>(a.x);
   const int* __restrict__ cu = a.cu_seqlens;
   const int t0 = blockIdx.y * kStrip;
   const int nt = min(kStrip, a.total_tokens - t0);
 
   // every x row of the strip is loaded up front (rows past the end repeat the last one),
-  // so the strip's loads are all in flight together
-  typename Vec8<T>::Raw xr[kStrip];
+  // so the strip's loads are all in flight together; then the K-1 rows before the strip,
+  // on the guess that they belong to the sequence of the strip's first token (true unless
+  // that sequence starts less than K-1 tokens before it; checked below), so the common
+  // case needs no second round trip
+  typename H::Raw xa[kStrip], xb[kStrip], ha[K - 1], hb[K - 1];
 #pragma unroll
-  for (int u = 0; u < kStrip; ++u) xr[u] = Vec8<T>::load_raw(x + static_cast<int64_t>(t0 + min(u, nt - 1)) * a.x_stride + ch0);
+  for (int u = 0; u < kStrip; ++u) {
+    const T* row = x + static_cast<int64_t>(t0 + min(u, nt - 1)) * a.x_stride;
+    xa[u] = H::load(row + ldA);
+    xb[u] = H::load(row + ldB);
+  }
+#pragma unroll
+  for (int i = 0; i < K - 1; ++i) {
+    const T* row = x + static_cast<int64_t>(max(t0 - (K - 1) + i, 0)) * a.x_stride;
+    ha[i] = H::load(row + ldA);
+    hb[i] = H::load(row + ldB);
+  }
 
   ConvTaps<T, K> taps;
-  taps.load(static_cast<const T*>(a.w), static_cast<const T*>(a.b), ch0);
+  taps.load_halves(static_cast<const T*>(a.w), static_cast<const T*>(a.b), ldA, ldB);
 
   // sequence holding t0: largest s with cu[s] <= t0 (cu[n] = total_tokens > t0)
   int lo = 0, hi = a.n;
@@ -55,10 +98,10 @@ __global__ __launch_bounds__(kThreads) void conv_prefill_kernel(ConvArgs a) {
   int seq_end = cu[s + 1];
 
   float win[K - 1][kVec];
-  bool reload = true;
+  bool reload = true, first = true;
 #pragma unroll
   for (int u = 0; u < kStrip; ++u) {
-    if (u < nt) {  // (a guard, not a break: the loop must unroll fully to keep xr in registers)
+    if (u < nt) {  // (a guard, not a break: the loop must unroll fully to keep the rows in registers)
       const int t = t0 + u;
       while (t >= seq_end) {  // next non-empty sequence starts at t
         ++s;
@@ -68,21 +111,34 @@ __global__ __launch_bounds__(kThreads) void conv_prefill_kernel(ConvArgs a) {
       }
       if (reload) {
         const int p = t - seq_start;  // position of t in its sequence
-        const T* cs = reinterpret_cast<const T*>(a.state_ptrs[s]);
+        if (first && p >= K - 1) {
+          // the rows before the strip are this sequence's tokens t0-K+1 .. t0-1: loaded above
 #pragma unroll
-        for (int i = 0; i < K - 1; ++i) {
-          const int r = p + i;  // z row feeding tap i of token t
-          if (r < K - 1)
-            Vec8<T>::load(cs + static_cast<int64_t>(r) * C + ch0, win[i]);
-          else
-            Vec8<T>::load(x + static_cast<int64_t>(seq_start + r - (K - 1)) * a.x_stride + ch0, win[i]);
+          for (int i = 0; i < K - 1; ++i) {
+            H::convert(ha[i], &win[i][0]);
+            H::convert(hb[i], &win[i][4]);
+          }
+        } else {
+          const T* cs = reinterpret_cast<const T*>(a.state_ptrs[s]);
+#pragma unroll
+          for (int i = 0; i < K - 1; ++i) {
+            const int r = p + i;  // z row feeding tap i of token t
+            const T* row = r < K - 1 ? cs + static_cast<int64_t>(r) * C
+                                     : x + static_cast<int64_t>(seq_start + r - (K - 1)) * a.x_stride;
+            H::convert(H::load(row + ldA), &win[i][0]);
+            H::convert(H::load(row + ldB), &win[i][4]);
+          }
         }
         reload = false;
       }
+      first = false;
       float cur[kVec], out[kVec];
-      Vec8<T>::convert(xr[u], cur);
+      H::convert(xa[u], &cur[0]);
+      H::convert(xb[u], &cur[4]);
       taps.apply(win, cur, a.silu != 0, out);
-      Vec8<float>::store(a.y + static_cast<int64_t>(t) * a.y_stride + ch0, out);
+      float* yrow = a.y + static_cast<int64_t>(t) * a.y_stride;
+      if (okA) *reinterpret_cast<float4*>(yrow + chA) = make_float4(out[0], out[1], out[2], out[3]);
+      if (okB) *reinterpret_cast<float4*>(yrow + chB) = make_float4(out[4], out[5], out[6], out[7]);
 #pragma unroll
       for (int i = 0; i < K - 2; ++i)
 #pragma unroll
@@ -171,7 +227,7 @@ hipError_t launch_all(const ConvArgs& a, hipStream_t s, bool decode) {
     return hipGetLastError();
   }
   if (a.total_tokens > 0) {
-    dim3 grid(gx, (a.total_tokens + kStrip - 1) / kStrip);
+    dim3 grid((a.channels + 512 * (kThreads / 64) - 1) / (512 * (kThreads / 64)), (a.total_tokens + kStrip - 1) / kStrip);
     switch (a.width) {
       case 2: conv_prefill_kernel<T, 2><<<grid, kThreads, 0, s>>>(a); break;
       case 3: conv_prefill_kernel<T, 3><<<grid, kThreads, 0, s>>>(a); break;

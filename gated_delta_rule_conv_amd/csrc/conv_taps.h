@@ -10,6 +10,21 @@ namespace gdn {
 
 constexpr int kConvVec = 8;  // channels per thread
 
+// 4 consecutive elements as fp32: 8 bytes (bf16, 8-byte aligned) or 16 bytes (fp32, 16-byte aligned)
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float* v) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 r = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(r.x << 16);
+    v[1] = __uint_as_float(r.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(r.y << 16);
+    v[3] = __uint_as_float(r.y & 0xFFFF0000u);
+  } else {
+    const float4 r = *reinterpret_cast<const float4*>(p);
+    v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+  }
+}
+
 template <typename T, int K>
 struct ConvTaps {
   float w[K][kConvVec];
@@ -31,6 +46,29 @@ struct ConvTaps {
       for (int j = 0; j < K; ++j) w[j][c] = flat[c * K + j];
     if (bp) {
       Vec8<T>::load(bp + ch0, b);
+    } else {
+#pragma unroll
+      for (int c = 0; c < kConvVec; ++c) b[c] = 0.f;
+    }
+  }
+
+  // The same for two groups of 4 channels, chA..chA+3 (as channels 0-3) and chB..chB+3
+  // (as 4-7): their 4*K taps each are contiguous and at least 8-byte aligned.
+  __device__ __forceinline__ void load_halves(const T* __restrict__ wp, const T* __restrict__ bp, int chA, int chB) {
+    float flat[2][4 * K];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const T* src = wp + static_cast<int64_t>(hh ? chB : chA) * K;
+#pragma unroll
+      for (int i = 0; i < K; ++i) load4<T>(src + 4 * i, &flat[hh][4 * i]);
+    }
+#pragma unroll
+    for (int c = 0; c < kConvVec; ++c)
+#pragma unroll
+      for (int j = 0; j < K; ++j) w[j][c] = flat[c / 4][(c % 4) * K + j];
+    if (bp) {
+      load4<T>(bp + chA, &b[0]);
+      load4<T>(bp + chB, &b[4]);
     } else {
 #pragma unroll
       for (int c = 0; c < kConvVec; ++c) b[c] = 0.f;
