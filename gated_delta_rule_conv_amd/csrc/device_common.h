@@ -11,6 +11,12 @@ constexpr int kWave = 64;  // CDNA wavefront width
 // Native clang vector (the nontemporal builtins and MFMA operands need these).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Waits until every vector memory load and store this wave has issued is complete:
+// s_waitcnt with vmcnt = 0 and the export and LDS/scalar counters at their maxima (7, 15),
+// i.e. not waited on (gfx9 field layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------- bf16 <-> fp32
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);

@@ -43,6 +43,12 @@
 #include "launch.h"
 #include "mma.h"
 
+// Multiply-adds are fused only within one source expression (a * b + c), never across
+// statements: the compiler's cross-statement fusion depends on the surrounding code, and
+// the inter-chunk kernel's variants (and the segmented form) must round the same
+// arithmetic the same way to give bit-identical results.
+#pragma clang fp contract(on)
+
 namespace gdn {
 namespace {
 
@@ -723,20 +729,37 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
     }
   }
 
-  auto load = [&](int c, In& in) {
-    const int t0 = start + c * C;
-    in.n = min(C, len - c * C);
+  // The operand loads of one chunk, in three groups so that the prefetching variant can
+  // issue them at different points of the previous step.
+  auto chunk_ptrs = [&](int c, const char*& kq, const char*& tp, const float*& gb) {
     const int64_t gc = cbase + c;
     // every operand fragment is one contiguous KiB per plane (fragment order, zero-padded)
-    const char* kq = w.kq + (gc * r.hk + h) * w.kq_stride;
-    const char* tp = w.tp + (gc * r.hv + j) * w.tp_stride;
-    const float* gb = reinterpret_cast<const float*>(tp + 2 * static_cast<size_t>(NT) * NK * FIO::BYTES);
-    in.gn = gb[C - 1];
+    kq = w.kq + (gc * r.hk + h) * w.kq_stride;
+    tp = w.tp + (gc * r.hv + j) * w.tp_stride;
+    gb = reinterpret_cast<const float*>(tp + 2 * static_cast<size_t>(NT) * NK * FIO::BYTES);
+  };
+  // K^ (or Q^) rows of this wave's token tile: the A operand of phase 1
+  auto load_a = [&](int c, In& in) {
+    const char *kq, *tp;
+    const float* gb;
+    chunk_ptrs(c, kq, tp, gb);
     if (active) {
       const char* arows = kq + (qside ? static_cast<size_t>(NT) * NV * FIO::BYTES : 0);
-      const char* mrows = tp + (qside ? static_cast<size_t>(NT) * NK * FIO::BYTES : 0);
 #pragma unroll
       for (int v = 0; v < NV; ++v) in.af[v] = FIO::load(arows + static_cast<size_t>(tt * NV + v) * FIO::BYTES, lane);
+    }
+  };
+  // T (or P) rows, gam, beta, gam_n and v (used by the K side only; with_v is a constant
+  // at every call, so no load sits under a branch)
+  auto load_m = [&](int c, In& in, bool with_v) {
+    const char *kq, *tp;
+    const float* gb;
+    chunk_ptrs(c, kq, tp, gb);
+    const int t0 = start + c * C;
+    in.n = min(C, len - c * C);
+    in.gn = gb[C - 1];
+    if (active) {
+      const char* mrows = tp + (qside ? static_cast<size_t>(NT) * NK * FIO::BYTES : 0);
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
         in.mf[kk] = FIO::load(mrows + static_cast<size_t>(tt * NK + kk) * FIO::BYTES, lane);
@@ -745,119 +768,170 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
       const float4 b4 = *reinterpret_cast<const float4*>(gb + C + tt * 16 + 4 * lg);
       in.gt[0] = g4.x; in.gt[1] = g4.y; in.gt[2] = g4.z; in.gt[3] = g4.w;
       in.bt[0] = b4.x; in.bt[1] = b4.y; in.bt[2] = b4.z; in.bt[3] = b4.w;
+      if (with_v) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int t = tt * 16 + 4 * lg + rr;
-        // a valid row of this sequence, read unconditionally; rows past the chunk's end
-        // are masked where the value is used (using a load in the step that issues it
-        // would wait for every load before it, the prefetch included)
-        const int tc = min(t, in.n - 1);
-        in.vv[rr] = vscale * r.v[static_cast<int64_t>(t0 + tc) * r.v_stride + j * D + blk * kDVB + l16];
+        for (int rr = 0; rr < 4; ++rr) {
+          const int t = tt * 16 + 4 * lg + rr;
+          // a valid row of this sequence, read unconditionally; rows past the chunk's end
+          // are masked where the value is used (using a load in the step that issues it
+          // would wait for every load before it, the prefetch included)
+          const int tc = min(t, in.n - 1);
+          in.vv[rr] = vscale * r.v[static_cast<int64_t>(t0 + tc) * r.v_stride + j * D + blk * kDVB + l16];
+        }
       }
     }
   };
+  auto load = [&](int c, In& in, bool with_v) {
+    load_a(c, in);
+    load_m(c, in, with_v);
+  };
 
-  auto process = [&](int c, In& in) {
+  // phase 1: X = K^ S^T (K side; then R = diag(beta) (V - diag(e^gam) X) into LDS and the
+  // K^ rows into the K^ tile) or Y = Q^ S^T (Q side; returns e^gam Y)
+  auto phase1 = [&](const In& in, f32x4& oacc) {
+    f32x4 a3[3];
+    zero3(a3);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) M::mma3(a3, in.af[v], SP::load(Sl, kDVB, SLD, l16, kl + v * KSTEP));
+    const f32x4 acc = total(a3);
+    if (!qside) {
+      // K^ rows of this token tile into LDS for the update (read after two barriers)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) KT::put(Kl, tt * 16 + l16, v * KSTEP + kl, in.af[v]);
+      float rv[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float vt = (tt * 16 + 4 * lg + rr < in.n) ? in.vv[rr] : 0.f;
+        rv[rr] = in.bt[rr] * (vt - expf(in.gt[rr]) * acc[rr]);
+      }
+      SP::store(Rt, kDVB, RLD, l16, tt * 16 + 4 * lg, rv, 4);
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) oacc[rr] = expf(in.gt[rr]) * acc[rr];
+    }
+  };
+  // phase 2 (K side): U = T R, T lower triangular; U^T and (e^{gam_n - gam} U)^T into LDS
+  auto phase2 = [&](const In& in) {
+    f32x4 u3[3];
+    zero3(u3);
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      if (kk * KSTEP < tt * 16 + 16) {
+        const F rf = (kFullK || kk * KSTEP + kl < C) ? SP::load(Rt, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+        M::mma3(u3, in.mf[kk], rf);
+      }
+    }
+    const f32x4 uacc = total(u3);
+    float ut[4], us[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      ut[rr] = uacc[rr];
+      us[rr] = expf(in.gn - in.gt[rr]) * uacc[rr];
+    }
+    SP::store(Ut, kDVB, RLD, l16, tt * 16 + 4 * lg, ut, 4);
+    SP::store(Us, kDVB, RLD, l16, tt * 16 + 4 * lg, us, 4);
+  };
+  // rows t < n of this wave's token tile of O for chunk c
+  auto store_o = [&](int c, int n, const f32x4& o) {
     const int t0 = start + c * C;
-    f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
-    // phase 1: X = K^ S^T (K side) or Y = Q^ S^T (Q side)
-    if (active) {
-      f32x4 a3[3];
-      zero3(a3);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) M::mma3(a3, in.af[v], SP::load(Sl, kDVB, SLD, l16, kl + v * KSTEP));
-      const f32x4 acc = total(a3);
-      if (!qside) {
-        // K^ rows of this token tile into LDS for the update (read after two barriers)
+    for (int rr = 0; rr < 4; ++rr) {
+      const int t = tt * 16 + 4 * lg + rr;
+      if (kOut && t < n) r.o[(static_cast<int64_t>(t0 + t) * r.hv + j) * D + blk * kDVB + l16] = o[rr];
+    }
+  };
+  // phase 3, Q side: O = e^gam Y + P U
+  auto phase3_out = [&](const In& in, f32x4& oacc) {
+    f32x4 o3[3];
+    zero3(o3);
 #pragma unroll
-        for (int v = 0; v < NV; ++v) KT::put(Kl, tt * 16 + l16, v * KSTEP + kl, in.af[v]);
-        float rv[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float vt = (tt * 16 + 4 * lg + rr < in.n) ? in.vv[rr] : 0.f;
-          rv[rr] = in.bt[rr] * (vt - expf(in.gt[rr]) * acc[rr]);
-        }
-        SP::store(Rt, kDVB, RLD, l16, tt * 16 + 4 * lg, rv, 4);
-      } else {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) oacc[rr] = expf(in.gt[rr]) * acc[rr];
+    for (int kk = 0; kk < NK; ++kk) {
+      if (kk * KSTEP < tt * 16 + 16) {
+        const F uf = (kFullK || kk * KSTEP + kl < C) ? SP::load(Ut, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+        M::mma3(o3, in.mf[kk], uf);
       }
     }
-    __syncthreads();
-    // phase 2 (K side): U = T R, T lower triangular
-    if (active && !qside) {
-      f32x4 u3[3];
-      zero3(u3);
+    oacc += total(o3);
+  };
+  // phase 3, state tile `wave`: S <- e^{gam_n} S + Us^T K^
+  auto phase3_state = [&](const In& in) {
+    const float egn = expf(in.gn);
+    f32x4 s3[3];
+    zero3(s3);
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        if (kk * KSTEP < tt * 16 + 16) {
-          const F rf = (kFullK || kk * KSTEP + kl < C) ? SP::load(Rt, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
-          M::mma3(u3, in.mf[kk], rf);
-        }
-      }
-      const f32x4 uacc = total(u3);
-      float ut[4], us[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        ut[rr] = uacc[rr];
-        us[rr] = expf(in.gn - in.gt[rr]) * uacc[rr];
-      }
-      SP::store(Ut, kDVB, RLD, l16, tt * 16 + 4 * lg, ut, 4);
-      SP::store(Us, kDVB, RLD, l16, tt * 16 + 4 * lg, us, 4);
+    for (int kk = 0; kk < NK; ++kk) {
+      const bool live = kFullK || kk * KSTEP + kl < C;
+      const F ua = live ? SP::load(Us, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+      const F kb = live ? KT::column(Kl, wave * 16 + l16, kk * KSTEP + kl) : SP::zero();
+      M::mma3(s3, ua, kb);
     }
-    __syncthreads();
-    // phase 3: O = e^gam Y + P U (Q side); S <- e^{gam_n} S + Us^T K^ (state tiles)
-    if (active && qside) {
-      f32x4 o3[3];
-      zero3(o3);
+    const f32x4 upd = total(s3);
+    f32x4 acc;
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        if (kk * KSTEP < tt * 16 + 16) {
-          const F uf = (kFullK || kk * KSTEP + kl < C) ? SP::load(Ut, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
-          M::mma3(o3, in.mf[kk], uf);
-        }
-      }
-      oacc += total(o3);
+    for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sacc[rr], egn, upd[rr]);
+    sacc = acc;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int t = tt * 16 + 4 * lg + rr;
-        if (kOut && t < in.n) r.o[(static_cast<int64_t>(t0 + t) * r.hv + j) * D + blk * kDVB + l16] = oacc[rr];
-      }
-    }
-    if (has_tile) {
-      const float egn = expf(in.gn);
-      f32x4 s3[3];
-      zero3(s3);
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        const bool live = kFullK || kk * KSTEP + kl < C;
-        const F ua = live ? SP::load(Us, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
-        const F kb = live ? KT::column(Kl, wave * 16 + l16, kk * KSTEP + kl) : SP::zero();
-        M::mma3(s3, ua, kb);
-      }
-      const f32x4 upd = total(s3);
-      f32x4 acc;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sacc[rr], egn, upd[rr]);
-      sacc = acc;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) SP::store1(Sl, kDVB, SLD, 4 * lg + rr, wave * 16 + l16, acc[rr]);
-    }
-    __syncthreads();
+    for (int rr = 0; rr < 4; ++rr) SP::store1(Sl, kDVB, SLD, 4 * lg + rr, wave * 16 + l16, acc[rr]);
   };
 
   if constexpr (PF) {
-    // Two operand buffers, one chunk ahead. The prefetch index is clamped rather than
-    // guarded (the last chunk is simply read twice), so no load sits under a branch.
+    // Two operand buffers, one chunk ahead. The next chunk's loads are spread over the
+    // step so that the 8 waves do not all queue theirs at the CU's load unit at once (a
+    // burst stalls the issuing waves for longer than the loads take): K-side waves issue
+    // the A rows at the top of the step and the rest after the second barrier; Q-side
+    // waves, idle while the K side computes U, issue all of theirs after the first. The
+    // two sides run separate loops with the same barriers, so that each side's loads are
+    // straight-line code (loads under a branch inside one loop made the compiler wait for
+    // the whole prefetch). Each step starts by waiting for all of the wave's outstanding
+    // vector memory operations (its operands, issued one step earlier); the Q side then
+    // stores the previous chunk's outputs, so that no store is in flight when a later
+    // wait would otherwise have to include it (with loads and stores both outstanding the
+    // compiler can only wait for everything). The prefetch index is clamped rather than
+    // guarded (the last chunk is simply read twice).
     In in0, in1;
-    load(c_begin, in0);
+    load(c_begin, in0, !qside);
     __syncthreads();  // Sl filled
-    for (int c = c_begin; c < c_end; c += 2) {
-      load(min(c + 1, c_end - 1), in1);
-      process(c, in0);
-      if (c + 1 >= c_end) break;
-      load(min(c + 2, c_end - 1), in0);
-      process(c + 1, in1);
+    auto step_k = [&](int c, const In& in, In& nxt, int cn) {
+      wait_vmem();
+      load_a(cn, nxt);
+      f32x4 unused;
+      if (active) phase1(in, unused);
+      __syncthreads();
+      if (active) phase2(in);
+      __syncthreads();
+      load_m(cn, nxt, true);
+      if (has_tile) phase3_state(in);
+      __syncthreads();
+    };
+    f32x4 oprev = {0.f, 0.f, 0.f, 0.f};  // outputs of the previous chunk, stored one step late
+    int nprev = 0;                          // (0: nothing to store)
+    auto step_q = [&](int c, const In& in, In& nxt, int cn) {
+      wait_vmem();
+      store_o(c - 1, nprev, oprev);
+      f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+      if (active) phase1(in, oacc);
+      __syncthreads();
+      load(cn, nxt, false);
+      __syncthreads();
+      if (active) phase3_out(in, oacc);
+      if (has_tile) phase3_state(in);
+      __syncthreads();
+      oprev = oacc;
+      nprev = in.n;
+    };
+    if (!qside) {
+      for (int c = c_begin; c < c_end; c += 2) {
+        step_k(c, in0, in1, min(c + 1, c_end - 1));
+        if (c + 1 >= c_end) break;
+        step_k(c + 1, in1, in0, min(c + 2, c_end - 1));
+      }
+    } else {
+      for (int c = c_begin; c < c_end; c += 2) {
+        step_q(c, in0, in1, min(c + 1, c_end - 1));
+        if (c + 1 >= c_end) break;
+        step_q(c + 1, in1, in0, min(c + 2, c_end - 1));
+      }
+      store_o(c_end - 1, nprev, oprev);
     }
   } else {
     // One operand buffer, loaded at the top of each step: half the registers, so two
@@ -865,8 +939,18 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
     In in0;
     __syncthreads();  // Sl filled
     for (int c = c_begin; c < c_end; ++c) {
-      load(c, in0);
-      process(c, in0);
+      load(c, in0, true);  // (the Q side loads v too: fewer registers than a branch)
+      f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+      if (active) phase1(in0, oacc);
+      __syncthreads();
+      if (active && !qside) phase2(in0);
+      __syncthreads();
+      if (active && qside) {
+        phase3_out(in0, oacc);
+        store_o(c, in0.n, oacc);
+      }
+      if (has_tile) phase3_state(in0);
+      __syncthreads();
     }
   }
 
