@@ -589,6 +589,37 @@ struct KTile {
       *reinterpret_cast<float4*>(p) = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
     }
   }
+  // The fragment of column d = d0 + l16 (d0 a multiple of 16), rows t0 .. t0 + KPL - 1,
+  // for lane l16 of a 16-lane group (all 16 lanes of the group call it with the same d0
+  // and t0). bf16 planes: gfx950's transposing LDS read (ds_read_b64_tr_b16) -- lane
+  // s = 4 k + c of the group reads the 4 values of row k, columns 4 c .. 4 c + 3 of a 4 x 16
+  // block, and lane j receives column j of the block, rows 0 .. 3 -- two per plane instead
+  // of 8 single-value reads.
+  __device__ __forceinline__ static F column16(const char* base, int d0, int t0, int l16) {
+    if constexpr (POL == kPolBF16X3) {
+      typedef short i16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      // (a chunk shorter than a k-step leaves groups of lanes past its last row; callers
+      // discard their values, and the clamp keeps their reads inside the tile)
+      if constexpr (C % Mma<POL>::KSTEP != 0) t0 = min(t0, C - 8);
+      const int tr = t0 + (l16 >> 2), dc = d0 + 4 * (l16 & 3);
+      const char* p0 = base + off(tr, dc);      // rows t0 .. t0 + 3
+      const char* p1 = base + off(tr + 4, dc);  // rows t0 + 4 .. t0 + 7
+      const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+      const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+      const i16x4 l0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + PLANE));
+      const i16x4 l1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1 + PLANE));
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 hv = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      const i16x8 lv = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+      F f;
+      f.hi = __builtin_bit_cast(bf16x8, hv);
+      f.lo = __builtin_bit_cast(bf16x8, lv);
+      return f;
+    } else {
+      return column(base, d0 + l16, t0);
+    }
+  }
   // B fragment: column d, rows t0 .. t0 + KPL - 1
   __device__ __forceinline__ static F column(const char* base, int d, int t0) {
     F f;
@@ -711,22 +742,23 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
   const int c_end = MODE == kModeWhole ? nch : c_seg_end;
   const int cbase = w.chunk_off[s];
 
+  // Wave w's state tile is columns [16 w, 16 w + 16) of the slice; lane (l16, lg) holds
+  // row l16, columns 16 w + 4 lg .. + 3 (the update is computed transposed, so that these
+  // are 4 consecutive values: one 16-byte global and one 8- or 16-byte LDS access).
+  const int scol = wave * 16 + 4 * lg;
   f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
   if (has_tile) {
+    if constexpr (MODE == kModeWhole) {
+      sacc = *reinterpret_cast<const f32x4*>(Sg + l16 * D + scol);
+    } else if constexpr (MODE == kModeSegment) {
+      sacc = *reinterpret_cast<const f32x4*>(
+          w.zs + (static_cast<size_t>(seg) * r.hv + j) * mat + static_cast<size_t>(blk * kDVB + l16) * D + scol);
+    } else {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = 4 * lg + rr, col = wave * 16 + l16;
-      float v;
-      if constexpr (MODE == kModeWhole) {
-        v = Sg[row * D + col];
-      } else if constexpr (MODE == kModeSegment) {
-        v = w.zs[(static_cast<size_t>(seg) * r.hv + j) * mat + static_cast<size_t>(blk * kDVB + row) * D + col];
-      } else {
-        v = (mrow && blk * kDVB + row == col) ? 1.f : 0.f;
-      }
-      sacc[rr] = v;
-      SP::store1(Sl, kDVB, SLD, row, col, v);
+      for (int rr = 0; rr < 4; ++rr) sacc[rr] = (mrow && blk * kDVB + l16 == scol + rr) ? 1.f : 0.f;
     }
+    float sv[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
+    SP::store(Sl, kDVB, SLD, l16, scol, sv, 4);
   }
 
   // The operand loads of one chunk, in three groups so that the prefetching variant can
@@ -853,7 +885,8 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
     }
     oacc += total(o3);
   };
-  // phase 3, state tile `wave`: S <- e^{gam_n} S + Us^T K^
+  // phase 3, state tile `wave`: S <- e^{gam_n} S + Us^T K^, computed as its transpose
+  // K^T Us (A operand: columns of K^, B operand: rows of Us)
   auto phase3_state = [&](const In& in) {
     const float egn = expf(in.gn);
     f32x4 s3[3];
@@ -861,17 +894,16 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const bool live = kFullK || kk * KSTEP + kl < C;
-      const F ua = live ? SP::load(Us, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
-      const F kb = live ? KT::column(Kl, wave * 16 + l16, kk * KSTEP + kl) : SP::zero();
-      M::mma3(s3, ua, kb);
+      const F kc = live ? KT::column16(Kl, wave * 16, kk * KSTEP + kl, l16) : SP::zero();
+      const F ub = live ? SP::load(Us, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+      M::mma3(s3, kc, ub);
     }
     const f32x4 upd = total(s3);
-    f32x4 acc;
+    float sv[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sacc[rr], egn, upd[rr]);
-    sacc = acc;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) SP::store1(Sl, kDVB, SLD, 4 * lg + rr, wave * 16 + l16, acc[rr]);
+    for (int rr = 0; rr < 4; ++rr) sv[rr] = fmaf(sacc[rr], egn, upd[rr]);
+    sacc = f32x4{sv[0], sv[1], sv[2], sv[3]};
+    SP::store(Sl, kDVB, SLD, l16, scol, sv, 4);
   };
 
   if constexpr (PF) {
@@ -957,18 +989,16 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
   if (has_tile) {
     if constexpr (MODE == kModeTransfer) {
       if (mrow) {
-        // M^T[n][i] for rows i = blk*16 + 4 lg + rr (consecutive) and column n of M
+        // M^T[n][i] for row i = blk*16 + l16 and columns n = scol + rr of M
         float* mt = w.mt + (static_cast<size_t>(seg) * r.hv + j) * mat;
-        *reinterpret_cast<float4*>(mt + static_cast<size_t>(wave * 16 + l16) * D + blk * kDVB + 4 * lg) =
-            make_float4(sacc[0], sacc[1], sacc[2], sacc[3]);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) mt[static_cast<size_t>(scol + rr) * D + blk * kDVB + l16] = sacc[rr];
       } else {
         float* bt = w.bt + (static_cast<size_t>(seg) * r.hv + j) * mat + static_cast<size_t>(blk * kDVB) * D;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) bt[(4 * lg + rr) * D + wave * 16 + l16] = sacc[rr];
+        *reinterpret_cast<f32x4*>(bt + l16 * D + scol) = sacc;
       }
     } else if (last_seg) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) Sg[(4 * lg + rr) * D + wave * 16 + l16] = sacc[rr];
+      *reinterpret_cast<f32x4*>(Sg + l16 * D + scol) = sacc;
     }
   }
 }
