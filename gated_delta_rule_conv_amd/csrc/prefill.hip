@@ -66,8 +66,9 @@ constexpr int kLptMaxSeqs = 256;   // longest-first ordering only up to this man
 // fragment order for the MFMA policy (FragIO<> in mma.h), zero-padded past the chunk:
 //   per (chunk, k-head): K^ and Q^ (q already scaled) as A operands (rows = tokens,
 //                        k = head dim)
-//   per (chunk, v-head): T, then P, as A operands (rows and k = tokens); then gam [C]
-//                        (fp32, padded with gam_{n-1}) and beta [C] (fp32, padded with 0)
+//   per (chunk, v-head): T, then P, as A operands (rows and k = tokens); then the decay
+//                        factors e^gam [C] (fp32, padded with e^{gam_{n-1}}), beta [C]
+//                        (padded with 0) and e^{gam_{n-1} - gam} [C] (padded with 1)
 //   chunk-parallel form only (segmented): per (segment, v-head) three d x d fp32
 //   matrices: the segment's start state Z, the transposed linear part M^T of its affine
 //   map S -> S M + B, and B.
@@ -103,7 +104,7 @@ struct FragCount {
   static constexpr int BYTES = FragIO<POL>::BYTES;
   __host__ __device__ static constexpr int nk(int C) { return (C + KSTEP - 1) / KSTEP; }
   __host__ __device__ static constexpr size_t kq(int D, int C) { return 2ull * (C / 16) * (D / KSTEP) * BYTES; }
-  __host__ __device__ static constexpr size_t tp(int C) { return 2ull * (C / 16) * nk(C) * BYTES + 2ull * C * 4; }
+  __host__ __device__ static constexpr size_t tp(int C) { return 2ull * (C / 16) * nk(C) * BYTES + 3ull * C * 4; }
 };
 
 // per-chunk strides of the two operand regions: the larger of the two policies' sizes
@@ -465,11 +466,14 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
       const float bv = lane < n ? b_next : 0.f;
       if (jj + 1 < group) load_gb(j + 1);
       gv = wave_inclusive_scan(gv);
+      // the chunk's decay factors for the inter-chunk kernel (lanes >= n hold gam_{n-1})
+      const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), C - 1));
       if (lane < C) {
         gam[lane] = gv;
         bet[lane] = bv;
-        gam_out[lane] = gv;
+        gam_out[lane] = expf(gv);
         gam_out[C + lane] = bv;
+        gam_out[2 * C + lane] = expf(gn - gv);
       }
     }
     __syncthreads();
@@ -649,8 +653,10 @@ struct ChunkIn {
   F af[NV];     // K^ (or Q^) row of token 16*tt + l16
   F mf[NK];     // T (or P) row of token 16*tt + l16
   float vv[4];  // v at the 4 output rows this lane holds (K side; rows >= n masked at use)
-  float gt[4], bt[4];
-  float gn;     // gam of the chunk's last token
+  float eg[4];  // e^gam, beta and e^{gam_n - gam} at those rows
+  float bt[4];
+  float ed[4];
+  float egn;    // e^{gam_n}, gam_n = gam of the chunk's last token
   int n;        // tokens in the chunk
 };
 
@@ -781,25 +787,27 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
       for (int v = 0; v < NV; ++v) in.af[v] = FIO::load(arows + static_cast<size_t>(tt * NV + v) * FIO::BYTES, lane);
     }
   };
-  // T (or P) rows, gam, beta, gam_n and v (used by the K side only; with_v is a constant
-  // at every call, so no load sits under a branch)
+  // T (or P) rows, the decay factors, beta and v (used by the K side only; with_v is a
+  // constant at every call, so no load sits under a branch)
   auto load_m = [&](int c, In& in, bool with_v) {
     const char *kq, *tp;
     const float* gb;
     chunk_ptrs(c, kq, tp, gb);
     const int t0 = start + c * C;
     in.n = min(C, len - c * C);
-    in.gn = gb[C - 1];
+    in.egn = gb[C - 1];
     if (active) {
       const char* mrows = tp + (qside ? static_cast<size_t>(NT) * NK * FIO::BYTES : 0);
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
         in.mf[kk] = FIO::load(mrows + static_cast<size_t>(tt * NK + kk) * FIO::BYTES, lane);
-      // gam and beta of this lane's 4 output rows are 4 consecutive floats
+      // the factors of this lane's 4 output rows are 4 consecutive floats of each array
       const float4 g4 = *reinterpret_cast<const float4*>(gb + tt * 16 + 4 * lg);
       const float4 b4 = *reinterpret_cast<const float4*>(gb + C + tt * 16 + 4 * lg);
-      in.gt[0] = g4.x; in.gt[1] = g4.y; in.gt[2] = g4.z; in.gt[3] = g4.w;
+      in.eg[0] = g4.x; in.eg[1] = g4.y; in.eg[2] = g4.z; in.eg[3] = g4.w;
       in.bt[0] = b4.x; in.bt[1] = b4.y; in.bt[2] = b4.z; in.bt[3] = b4.w;
+      const float4 d4 = *reinterpret_cast<const float4*>(gb + 2 * C + tt * 16 + 4 * lg);
+      in.ed[0] = d4.x; in.ed[1] = d4.y; in.ed[2] = d4.z; in.ed[3] = d4.w;
       if (with_v) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -834,12 +842,12 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const float vt = (tt * 16 + 4 * lg + rr < in.n) ? in.vv[rr] : 0.f;
-        rv[rr] = in.bt[rr] * (vt - expf(in.gt[rr]) * acc[rr]);
+        rv[rr] = in.bt[rr] * (vt - in.eg[rr] * acc[rr]);
       }
       SP::store(Rt, kDVB, RLD, l16, tt * 16 + 4 * lg, rv, 4);
     } else {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) oacc[rr] = expf(in.gt[rr]) * acc[rr];
+      for (int rr = 0; rr < 4; ++rr) oacc[rr] = in.eg[rr] * acc[rr];
     }
   };
   // phase 2 (K side): U = T R, T lower triangular; U^T and (e^{gam_n - gam} U)^T into LDS
@@ -858,7 +866,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       ut[rr] = uacc[rr];
-      us[rr] = expf(in.gn - in.gt[rr]) * uacc[rr];
+      us[rr] = in.ed[rr] * uacc[rr];
     }
     SP::store(Ut, kDVB, RLD, l16, tt * 16 + 4 * lg, ut, 4);
     SP::store(Us, kDVB, RLD, l16, tt * 16 + 4 * lg, us, 4);
@@ -888,7 +896,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
   // phase 3, state tile `wave`: S <- e^{gam_n} S + Us^T K^, computed as its transpose
   // K^T Us (A operand: columns of K^, B operand: rows of Us)
   auto phase3_state = [&](const In& in) {
-    const float egn = expf(in.gn);
+    const float egn = in.egn;
     f32x4 s3[3];
     zero3(s3);
 #pragma unroll
