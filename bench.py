@@ -161,7 +161,7 @@ class DecodeRig:
 
 
 class PrefillRig:
-    def __init__(self, cfg: int = 1, device="cuda", shape=None, form: int = 0):
+    def __init__(self, cfg: int = 1, device="cuda", shape=None, form: int = 0, fused: bool = False):
         import numpy as np
         import torch
 
@@ -189,9 +189,14 @@ class PrefillRig:
         self.cu = torch.tensor(inp["cu_seqlens"], dtype=torch.int32, device=device)
         self.g = torch.from_numpy(inp["g"]).to(device)
         self.beta = torch.from_numpy(inp["beta"]).to(device)
-        self.y = torch.empty((T, sh.channels), dtype=torch.float32, device=device)
         self.o = torch.empty((T, sh.num_v_heads, sh.head_dim), dtype=torch.float32, device=device)
-        self.ws = gdn.prefill_workspace(self.dims, N, T, device=device)
+        self.fused = fused
+        if fused:
+            self.y = None
+            self.ws = gdn.prefill_fused_workspace(self.dims, N, T, device=device)
+        else:
+            self.y = torch.empty((T, sh.channels), dtype=torch.float32, device=device)
+            self.ws = gdn.prefill_workspace(self.dims, N, T, device=device)
 
     def flops(self) -> float:
         """Algorithmic flops of the chunked form per v-head, summed over chunks of n
@@ -208,8 +213,12 @@ class PrefillRig:
     def step(self) -> None:
         import gated_delta_rule_conv_amd as gdn
 
-        gdn.conv_update(self.dims, self.x, self.y, self.conv_w, None, self.cptr, self.cu)
-        gdn.prefill(self.dims, self.y, self.g, self.beta, self.o, self.cu, self.sptr, self.ws)
+        if self.fused:
+            gdn.prefill_fused(self.dims, self.x, self.conv_w, None, self.g, self.beta, self.o, self.cu, self.sptr,
+                              self.cptr, self.ws)
+        else:
+            gdn.conv_update(self.dims, self.x, self.y, self.conv_w, None, self.cptr, self.cu)
+            gdn.prefill(self.dims, self.y, self.g, self.beta, self.o, self.cu, self.sptr, self.ws)
 
 
 def cpu_baseline(seconds: float) -> dict:
@@ -384,12 +393,16 @@ def main() -> int:
         # heads, 4 v-heads), as the library runs it (chunk-parallel form) and forced to
         # walk whole sequences
         share = LayerShape(2, 4, 128, conv_width=4, chunk=64, in_dtype="bf16")
-        runs = [(1, "L4096", None, 0), (4, "ragged8_T15717", None, 0),
-                (1, "L4096_hk2_hv4", share, 0), (1, "L4096_hk2_hv4_whole_sequence", share, 1)]
-        for cfg, name, shape, form in runs:
+        # "_fused": the same prefill as one gdn_prefill_fused call (q/k conv inside the
+        # intra-chunk kernel; bit-identical results)
+        runs = [(1, "L4096", None, 0, False), (1, "L4096_fused", None, 0, True),
+                (4, "ragged8_T15717", None, 0, False), (4, "ragged8_T15717_fused", None, 0, True),
+                (1, "L4096_hk2_hv4", share, 0, False), (1, "L4096_hk2_hv4_fused", share, 0, True),
+                (1, "L4096_hk2_hv4_whole_sequence", share, 1, False)]
+        for cfg, name, shape, form, fused in runs:
             if cfg == 4 and args.no_ragged:
                 continue
-            pre = PrefillRig(cfg, shape=shape, form=form)
+            pre = PrefillRig(cfg, shape=shape, form=form, fused=fused)
             for _ in range(W):
                 pre.step()
             torch.cuda.synchronize()
@@ -406,7 +419,8 @@ def main() -> int:
                 "algorithmic_TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2),
                 "frac_of_bf16_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
                 "gflop": round(fl / 1e9, 3),
-                "note": "conv_update (prefill mode) + prefill_chunked (bf16x3 MFMA: 3 bf16 products per "
+                "note": ("prefill_fused" if fused else "conv_update (prefill mode) + prefill_chunked") +
+                        " (bf16x3 MFMA: 3 bf16 products per "
                         "algorithmic product)" + (f"; {shape.num_k_heads} q/k heads, {shape.num_v_heads} v-heads, "
                                                  f"{'chunk-parallel' if form == 0 else 'whole-sequence'} form"
                                                  if shape is not None else "")}

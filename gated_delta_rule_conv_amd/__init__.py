@@ -28,6 +28,8 @@ from ._lib import (  # noqa: F401
     gdn_dims,
     gdn_last_error,
     gdn_prefill_chunked,
+    gdn_prefill_fused,
+    gdn_prefill_fused_workspace_size,
     gdn_prefill_workspace_size,
     gdn_slot_copy,
     gdn_slot_pointers,
@@ -41,6 +43,8 @@ from .layer import (  # noqa: F401
     decode_counters,
     decode_fused,
     prefill,
+    prefill_fused,
+    prefill_fused_workspace,
     prefill_workspace,
     qkv_views,
 )

@@ -119,11 +119,11 @@ __global__ __launch_bounds__(kThreads) void conv_prefill_kernel(ConvArgs a) {
             H::convert(hb[i], &win[i][4]);
           }
         } else {
-          const T* cs = reinterpret_cast<const T*>(a.state_ptrs[s]);
+          const T* cs = reinterpret_cast<const T*>(a.state_ptrs[s]) + a.state_off;
 #pragma unroll
           for (int i = 0; i < K - 1; ++i) {
             const int r = p + i;  // z row feeding tap i of token t
-            const T* row = r < K - 1 ? cs + static_cast<int64_t>(r) * C
+            const T* row = r < K - 1 ? cs + static_cast<int64_t>(r) * a.state_stride
                                      : x + static_cast<int64_t>(seq_start + r - (K - 1)) * a.x_stride;
             H::convert(H::load(row + ldA), &win[i][0]);
             H::convert(H::load(row + ldB), &win[i][4]);
@@ -213,9 +213,11 @@ __global__ __launch_bounds__(kDecThreads) void conv_decode_kernel(ConvArgs a) {
   Vec8<T>::store_raw_g(cs + static_cast<int64_t>(K - 2) * C + ch0, xr);
 }
 
+// mode: 0 decode, 1 prefill conv + commit, 2 prefill conv only, 3 commit only
 template <typename T>
-hipError_t launch_all(const ConvArgs& a, hipStream_t s, bool decode) {
+hipError_t launch_all(const ConvArgs& a, hipStream_t s, int mode) {
   const unsigned gx = (a.channels / kVec + kThreads - 1) / kThreads;
+  const bool decode = mode == 0;
   if (decode) {
     if (a.n == 0) return hipSuccess;
     dim3 grid((a.channels / kVec + kDecThreads - 1) / kDecThreads, a.n);
@@ -226,7 +228,7 @@ hipError_t launch_all(const ConvArgs& a, hipStream_t s, bool decode) {
     }
     return hipGetLastError();
   }
-  if (a.total_tokens > 0) {
+  if (mode != 3 && a.total_tokens > 0) {
     dim3 grid((a.channels + 512 * (kThreads / 64) - 1) / (512 * (kThreads / 64)), (a.total_tokens + kStrip - 1) / kStrip);
     switch (a.width) {
       case 2: conv_prefill_kernel<T, 2><<<grid, kThreads, 0, s>>>(a); break;
@@ -236,7 +238,7 @@ hipError_t launch_all(const ConvArgs& a, hipStream_t s, bool decode) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.n == 0) return hipSuccess;
+  if (mode == 2 || a.n == 0) return hipSuccess;
   dim3 grid(gx, a.n);
   switch (a.width) {
     case 2: conv_commit_kernel<T, 2><<<grid, kThreads, 0, s>>>(a); break;
@@ -249,11 +251,19 @@ hipError_t launch_all(const ConvArgs& a, hipStream_t s, bool decode) {
 }  // namespace
 
 hipError_t launch_conv_prefill(const ConvArgs& a, hipStream_t s) {
-  return a.bf16 ? launch_all<uint16_t>(a, s, false) : launch_all<float>(a, s, false);
+  return a.bf16 ? launch_all<uint16_t>(a, s, 1) : launch_all<float>(a, s, 1);
+}
+
+hipError_t launch_conv_prefill_only(const ConvArgs& a, hipStream_t s) {
+  return a.bf16 ? launch_all<uint16_t>(a, s, 2) : launch_all<float>(a, s, 2);
+}
+
+hipError_t launch_conv_commit(const ConvArgs& a, hipStream_t s) {
+  return a.bf16 ? launch_all<uint16_t>(a, s, 3) : launch_all<float>(a, s, 3);
 }
 
 hipError_t launch_conv_decode(const ConvArgs& a, hipStream_t s) {
-  return a.bf16 ? launch_all<uint16_t>(a, s, true) : launch_all<float>(a, s, true);
+  return a.bf16 ? launch_all<uint16_t>(a, s, 0) : launch_all<float>(a, s, 0);
 }
 
 }  // namespace gdn

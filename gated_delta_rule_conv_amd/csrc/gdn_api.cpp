@@ -87,6 +87,14 @@ gdn_status check_qkv(const gdn_dims* d, const char* fn, const float* q, int64_t 
   return GDN_OK;
 }
 
+// the fused prefill's workspace: the chunked prefill's, then the v part of the conv output
+size_t fused_prefill_bytes(const gdn_dims* d, int32_t num_seqs, int32_t total_tokens) {
+  const size_t pre = gdn::prefill_workspace_bytes(d->num_k_heads, d->num_v_heads, d->head_dim, d->chunk_size,
+                                                  num_seqs, total_tokens, d->prefill_form);
+  const size_t yv = static_cast<size_t>(total_tokens) * d->num_v_heads * d->head_dim * sizeof(float);
+  return pre + ((yv + 255) & ~static_cast<size_t>(255));
+}
+
 int resolve_mma(const gdn_dims* d) {
   if (d->mma != GDN_MMA_AUTO) return d->mma;
   return d->in_dtype == GDN_F32 ? GDN_MMA_FP32 : GDN_MMA_BF16X3;
@@ -127,7 +135,7 @@ gdn_status gdn_conv_update(const gdn_dims* dims, const void* x, int64_t x_stride
                 fn);
   gdn::ConvArgs a{x, x_stride, y, y_stride, conv_w, conv_b, cu_seqlens, conv_state_ptrs, n, total_tokens,
                   static_cast<int32_t>(C), dims->conv_width, dims->activation == GDN_ACT_SILU,
-                  dims->in_dtype == GDN_BF16};
+                  dims->in_dtype == GDN_BF16, C, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(decode ? gdn::launch_conv_decode(a, s) : gdn::launch_conv_prefill(a, s), fn);
 }
@@ -178,6 +186,85 @@ gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_s
   a.mma = resolve_mma(dims);
   a.workspace = workspace;
   return hip_status(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+gdn_status gdn_prefill_fused_workspace_size(const gdn_dims* dims, int32_t num_seqs, int32_t total_tokens,
+                                            size_t* bytes) {
+  const char* fn = "gdn_prefill_fused_workspace_size";
+  if (gdn_status st = check_dims(dims, fn)) return st;
+  if (!bytes) return fail(GDN_ERR_NULL, "%s: bytes is NULL", fn);
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_SHAPE, "%s: negative count", fn);
+  *bytes = fused_prefill_bytes(dims, num_seqs, total_tokens);
+  return GDN_OK;
+}
+
+gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stride, const void* conv_w,
+                             const void* conv_b, const float* g, const float* beta, float* o,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                             const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_prefill_fused";
+  if (gdn_status st = check_dims(dims, fn)) return st;
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_SHAPE, "%s: negative count", fn);
+  if (num_seqs == 0) {
+    if (total_tokens != 0) return fail(GDN_ERR_SHAPE, "%s: tokens without sequences", fn);
+    return GDN_OK;
+  }
+  if (!cu_seqlens || !state_ptrs || !conv_state_ptrs)
+    return fail(GDN_ERR_NULL, "%s: cu_seqlens, state_ptrs and conv_state_ptrs are required", fn);
+  const int64_t C = channels(dims);
+  const int64_t esz = dims->in_dtype == GDN_BF16 ? 2 : 4;
+  const int64_t qk = 2 * static_cast<int64_t>(dims->num_k_heads) * dims->head_dim;  // q | k channels
+  const int64_t vw = static_cast<int64_t>(dims->num_v_heads) * dims->head_dim;
+  if (total_tokens > 0) {
+    if (!x || !conv_w || !g || !beta || !o)
+      return fail(GDN_ERR_NULL, "%s: x, conv_w, g, beta and o are required", fn);
+    if (x_stride < 0) return fail(GDN_ERR_SHAPE, "%s: negative stride", fn);
+    if (total_tokens > 1 && x_stride < C)
+      return fail(GDN_ERR_SHAPE, "%s: x row stride %lld below the channel count %lld", fn,
+                  static_cast<long long>(x_stride), static_cast<long long>(C));
+    if (!aligned16(x) || !aligned16(conv_w) || (conv_b && !aligned16(conv_b)) || (x_stride * esz) % 16)
+      return fail(GDN_ERR_ALIGN, "%s: x, conv_w, conv_b must be 16-byte aligned and x_stride a multiple of 16 bytes",
+                  fn);
+  }
+  const size_t pre = gdn::prefill_workspace_bytes(dims->num_k_heads, dims->num_v_heads, dims->head_dim,
+                                                  dims->chunk_size, num_seqs, total_tokens, dims->prefill_form);
+  const size_t need = fused_prefill_bytes(dims, num_seqs, total_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(GDN_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  if (total_tokens == 0) return GDN_OK;  // (zero-length sequences only: nothing changes)
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* yv = reinterpret_cast<float*>(static_cast<char*>(workspace) + pre);  // v part of the conv output
+  const int K = dims->conv_width;
+  const bool silu = dims->activation == GDN_ACT_SILU, bf16 = dims->in_dtype == GDN_BF16;
+  const char* xb = static_cast<const char*>(x);
+  const char* wb = static_cast<const char*>(conv_w);
+  const char* bb = static_cast<const char*>(conv_b);
+  // 1. the v channels' conv into the workspace (the conv states are committed last)
+  gdn::ConvArgs cv{xb + qk * esz, x_stride, yv, vw, wb + qk * K * esz, bb ? bb + qk * esz : nullptr, cu_seqlens,
+                   conv_state_ptrs, num_seqs, total_tokens, static_cast<int32_t>(vw), K, silu, bf16, C,
+                   static_cast<int32_t>(qk)};
+  if (gdn_status st = hip_status(gdn::launch_conv_prefill_only(cv, s), fn)) return st;
+  // 2. the chunked prefill, the q/k conv inside its intra-chunk kernel
+  gdn::PrefillArgs a{};
+  a.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, yv, vw, g, beta, o, state_ptrs, dims->num_k_heads,
+                       dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale};
+  a.conv = gdn::ConvIn{x, x_stride, conv_w, conv_b, conv_state_ptrs, static_cast<int32_t>(C), K, silu, bf16};
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.chunk = dims->chunk_size;
+  a.form = dims->prefill_form;
+  a.mma = resolve_mma(dims);
+  a.workspace = workspace;
+  if (gdn_status st = hip_status(gdn::launch_prefill(a, s), fn)) return st;
+  // 3. every channel's conv state: the last K-1 rows of the sequence's conv input
+  gdn::ConvArgs cc{x, x_stride, nullptr, 0, conv_w, conv_b, cu_seqlens, conv_state_ptrs, num_seqs, total_tokens,
+                   static_cast<int32_t>(C), K, silu, bf16, C, 0};
+  return hip_status(gdn::launch_conv_commit(cc, s), fn);
 }
 
 gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_stride, const float* k,

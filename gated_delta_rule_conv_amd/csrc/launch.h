@@ -23,9 +23,15 @@ struct ConvArgs {
   int32_t width;  // K
   int32_t silu;
   int32_t bf16;  // in_dtype == BF16
+  // prefill mode: conv state row r of a slot, channel c (of the `channels` processed) is
+  // element r * state_stride + state_off + c (all channels: channels, 0)
+  int64_t state_stride;
+  int32_t state_off;
 };
 
-hipError_t launch_conv_prefill(const ConvArgs& a, hipStream_t s);
+hipError_t launch_conv_prefill(const ConvArgs& a, hipStream_t s);  // conv, then the conv-state commit
+hipError_t launch_conv_prefill_only(const ConvArgs& a, hipStream_t s);
+hipError_t launch_conv_commit(const ConvArgs& a, hipStream_t s);
 hipError_t launch_conv_decode(const ConvArgs& a, hipStream_t s);
 
 struct RecurArgs {
@@ -65,8 +71,23 @@ struct FusedArgs {
 
 hipError_t launch_decode_fused(const FusedArgs& f, int32_t m, hipStream_t s);
 
+// The depthwise conv of the q and k channels, computed inside the prefill (fused entry
+// point); x == nullptr: q and k are read from RecurArgs instead.
+struct ConvIn {
+  const void* x;
+  int64_t x_stride;
+  const void* w;
+  const void* b;                 // nullable
+  const uint64_t* state_ptrs;    // per sequence, [K-1][channels] in the input dtype
+  int32_t channels;              // all channels (2 Hk + Hv) d: the row length of a conv state
+  int32_t width;
+  int32_t silu;
+  int32_t bf16;
+};
+
 struct PrefillArgs {
   RecurArgs r;
+  ConvIn conv;
   const int32_t* cu_seqlens;
   int32_t num_seqs;
   int32_t total_tokens;

@@ -40,6 +40,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "conv_taps.h"
 #include "launch.h"
 #include "mma.h"
 
@@ -291,6 +292,80 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
 }
 
 // ------------------------------------------------------------------------ intra-chunk
+// The fused entry point's q/k conv, inside the intra-chunk kernel: the chunk's q and k
+// channels of k-head h, convolved from x (and, before the sequence's first token, from
+// its conv state) into the LDS rows Qh / Kh, not yet normalised; rows >= n are zero. The
+// per-channel arithmetic is ConvTaps::apply, as in the conv kernels, so the values are
+// those the conv kernel would have written. A thread takes 8 adjacent channels (q's d/8
+// groups, then k's) of a strip of rows and loads the K-1 rows before the strip once.
+template <typename T, int K, int D, int C, int KP>
+__device__ __forceinline__ void conv_qk_rows_k(const PrefillArgs& a, int h, int t0, int n, int seq_start, int s,
+                                               float (*Kh)[KP], float (*Qh)[KP], int tid) {
+  using V8 = Vec8<T>;
+  constexpr int G = 2 * D / kConvVec;                                 // 8-channel groups
+  constexpr int RPT = (G * C >= kThreads) ? G * C / kThreads : 1;    // rows per thread
+  constexpr int NS = C / RPT;                                          // row strips
+  const T* __restrict__ x = static_cast<const T*>(a.conv.x);
+  const T* cs = reinterpret_cast<const T*>(a.conv.state_ptrs[s]);
+  const int64_t cstride = a.conv.channels;
+  const int pos0 = t0 - seq_start;  // position of the chunk's first row in its sequence
+  const bool silu = a.conv.silu != 0;
+  for (int e = tid; e < G * NS; e += kThreads) {
+    const int grp = e % G, strip = e / G;
+    const bool isq = grp < G / 2;
+    const int col = (isq ? grp : grp - G / 2) * kConvVec;  // column within the head
+    const int ch = (isq ? 0 : a.r.hk * D) + h * D + col;    // channel of x, the taps and the conv state
+    ConvTaps<T, K> taps;
+    taps.load(static_cast<const T*>(a.conv.w), static_cast<const T*>(a.conv.b), ch);
+    const int r0 = strip * RPT;
+    typename V8::Raw z[RPT + K - 1];  // z rows r0 - (K-1) .. r0 + RPT - 1 (chunk coordinates)
+#pragma unroll
+    for (int i = 0; i < RPT + K - 1; ++i) {
+      const int rr = min(r0 - (K - 1) + i, n - 1);  // rows past the chunk's end repeat its last
+      const int p = pos0 + rr;                       // position in the sequence
+      const T* src = p >= 0 ? x + static_cast<int64_t>(seq_start + p) * a.conv.x_stride + ch
+                            : cs + static_cast<int64_t>(p + K - 1) * cstride + ch;
+      z[i] = V8::load_raw(src);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = r0 + i;
+      float out[kConvVec];
+      if (row < n) {
+        float win[K - 1][kConvVec], cur[kConvVec];
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) V8::convert(z[i + j], win[j]);
+        V8::convert(z[i + K - 1], cur);
+        taps.apply(win, cur, silu, out);
+      } else {
+#pragma unroll
+        for (int c = 0; c < kConvVec; ++c) out[c] = 0.f;
+      }
+      float* dst = isq ? &Qh[row][col] : &Kh[row][col];
+      *reinterpret_cast<float4*>(dst) = make_float4(out[0], out[1], out[2], out[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(out[4], out[5], out[6], out[7]);
+    }
+  }
+}
+
+template <int D, int C, int KP>
+__device__ __forceinline__ void conv_qk_rows(const PrefillArgs& a, int h, int t0, int n, int seq_start, int s,
+                                             float (*Kh)[KP], float (*Qh)[KP], int tid) {
+  if (a.conv.bf16) {
+    switch (a.conv.width) {
+      case 2: conv_qk_rows_k<uint16_t, 2, D, C, KP>(a, h, t0, n, seq_start, s, Kh, Qh, tid); break;
+      case 3: conv_qk_rows_k<uint16_t, 3, D, C, KP>(a, h, t0, n, seq_start, s, Kh, Qh, tid); break;
+      default: conv_qk_rows_k<uint16_t, 4, D, C, KP>(a, h, t0, n, seq_start, s, Kh, Qh, tid); break;
+    }
+  } else {
+    switch (a.conv.width) {
+      case 2: conv_qk_rows_k<float, 2, D, C, KP>(a, h, t0, n, seq_start, s, Kh, Qh, tid); break;
+      case 3: conv_qk_rows_k<float, 3, D, C, KP>(a, h, t0, n, seq_start, s, Kh, Qh, tid); break;
+      default: conv_qk_rows_k<float, 4, D, C, KP>(a, h, t0, n, seq_start, s, Kh, Qh, tid); break;
+    }
+  }
+}
+
 // LDS of the intra-chunk kernel, in floats. K^ and Q^ live only until K K^T and Q K^T are
 // in registers; then G and QK take K^'s place and A and T take Q^'s, so the peak is two
 // C x (D+4) areas (70 KB at C = 64, D = 128) and two workgroups fit on a CU.
@@ -347,14 +422,23 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     b_first = r.beta[static_cast<int64_t>(t0 + tl) * r.hv + h * group];
   }
 
-  // 1. normalised K and Q rows of the chunk into LDS; rows >= n are zero
+  // 1. normalised K and Q rows of the chunk into LDS; rows >= n are zero. The fused entry
+  // point convolves the rows into LDS first and normalises them there.
   constexpr int TPR = 8;
   constexpr int EPT = D / TPR;
+  const bool fused = a.conv.x != nullptr;
+  if (fused) {
+    conv_qk_rows<D, C, KP>(a, h, t0, n, t0 - ent.w * C, ent.x, Kh, Qh, tid);
+    __syncthreads();
+  }
   for (int row = tid / TPR; row < C; row += kThreads / TPR) {
     const int part = tid % TPR;
     float kv[EPT], qv[EPT];
     const bool live = row < n;
-    if (live) {
+    if (live && fused) {
+      load_k<EPT>(&Kh[row][part * EPT], kv);
+      load_k<EPT>(&Qh[row][part * EPT], qv);
+    } else if (live) {
       load_k<EPT>(r.k + static_cast<int64_t>(t0 + row) * r.k_stride + h * D + part * EPT, kv);
       load_k<EPT>(r.q + static_cast<int64_t>(t0 + row) * r.q_stride + h * D + part * EPT, qv);
     } else {

@@ -95,6 +95,15 @@ def prefill(dims: gdn_dims, y: torch.Tensor, g: torch.Tensor, beta: torch.Tensor
                              workspace.numel() * workspace.element_size(), stream)
 
 
+def prefill_fused(dims: gdn_dims, x: torch.Tensor, conv_w: torch.Tensor, conv_b, g: torch.Tensor, beta: torch.Tensor,
+                  o: torch.Tensor, cu_seqlens: torch.Tensor, state_ptrs: torch.Tensor, conv_state_ptrs: torch.Tensor,
+                  workspace: torch.Tensor, stream=None) -> None:
+    """conv_update (prefill mode) + prefill in one call; workspace from prefill_fused_workspace()."""
+    _lib.gdn_prefill_fused(dims, x, x.stride(0), conv_w, conv_b, g, beta, o, cu_seqlens, state_ptrs.numel(),
+                           x.shape[0], state_ptrs, conv_state_ptrs, workspace,
+                           workspace.numel() * workspace.element_size(), stream)
+
+
 def decode(dims: gdn_dims, y: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, o: torch.Tensor,
            state_ptrs: torch.Tensor, stream=None) -> None:
     q, k, v = qkv_views(dims, y)
@@ -121,5 +130,11 @@ def prefill_workspace(dims: gdn_dims, num_seqs: int, total_tokens: int, device="
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+def prefill_fused_workspace(dims: gdn_dims, num_seqs: int, total_tokens: int, device="cuda") -> torch.Tensor:
+    nbytes = _lib.gdn_prefill_fused_workspace_size(dims, num_seqs, total_tokens)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
 __all__ = ["SlotPool", "channels", "conv_update", "decode", "decode_counters", "decode_fused", "prefill",
-           "prefill_workspace", "qkv_views", "torch_in_dtype", "GDN_F32", "GDN_BF16"]
+           "prefill_fused", "prefill_fused_workspace", "prefill_workspace", "qkv_views", "torch_in_dtype", "GDN_F32",
+           "GDN_BF16"]

@@ -168,6 +168,44 @@ gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_s
                                size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * gdn_prefill_fused_workspace_size -- bytes of device workspace gdn_prefill_fused needs
+ * for at most num_seqs sequences and total_tokens tokens (written to *bytes): the
+ * gdn_prefill_chunked workspace plus the v part of the conv output (total_tokens x Hv*d
+ * fp32).
+ */
+gdn_status gdn_prefill_fused_workspace_size(const gdn_dims* dims, int32_t num_seqs, int32_t total_tokens,
+                                            size_t* bytes);
+
+/* ---------------------------------------------------------------------------------
+ * gdn_prefill_fused -- the prefill of a layer in one call: gdn_conv_update in prefill
+ * mode followed by gdn_prefill_chunked on the q/k/v views of its output ("System
+ * Design", "GDN Kernel Dispatch Detail": conv with the per-sequence conv state, then the
+ * chunked gated delta rule and the state update), without writing the q and k part of
+ * the conv output to memory: the intra-chunk kernel convolves its chunk's q and k
+ * channels from x itself (the same per-channel arithmetic as the conv kernel), and only
+ * the v part goes through the workspace. o, the recurrent states and the conv states
+ * come out bit-identical to those two calls in sequence.
+ *
+ *  x          [total_tokens][C] in dims->in_dtype, row stride x_stride (C = (2 Hk + Hv) d,
+ *             channels ordered q | k | v as for gdn_conv_update).
+ *  conv_w     [C][conv_width], conv_b [C] or NULL, in dims->in_dtype.
+ *  g, beta, o, cu_seqlens, num_seqs, total_tokens, state_ptrs: as for gdn_prefill_chunked.
+ *  conv_state_ptrs device u64 [num_seqs]; entry s points at sequence s's conv state,
+ *             [conv_width-1][C] in dims->in_dtype: read before, and replaced by, the last
+ *             conv_width-1 rows of the sequence's conv input (as gdn_conv_update).
+ *  workspace  device scratch of at least gdn_prefill_fused_workspace_size(dims, num_seqs,
+ *             total_tokens) bytes, 256-byte aligned; contents on entry are ignored.
+ *  Alignment: x, conv_w, conv_b 16-byte aligned, x_stride a multiple of 16 bytes.
+ *  Errors: as the two calls (GDN_ERR_NULL, _SHAPE, _ALIGN, _WORKSPACE); nothing is
+ *  launched unless every check passes.
+ */
+gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stride, const void* conv_w,
+                             const void* conv_b, const float* g, const float* beta, float* o,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                             const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * gdn_decode_batched -- one token for each of m slots: L2 norm + one step of the gated
  * delta rule on each slot's state, in place ("System Design", "GDN Kernel Dispatch
  * Detail", decode branch: decay the temporal state and write the delta, then

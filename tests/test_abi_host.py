@@ -181,6 +181,35 @@ def test_prefill_workspace_and_checks():
     gdn.gdn_prefill_chunked(d, *qkv, FAKE, 0, 0, FAKE, None, 0, 0)
 
 
+def test_prefill_fused_workspace_and_checks():
+    """The fused prefill needs the chunked prefill's workspace plus the v part of the conv
+    output, and rejects what either of the two calls would."""
+    d = dims()
+    pre = gdn.gdn_prefill_workspace_size(d, 8, 15717)
+    need = gdn.gdn_prefill_fused_workspace_size(d, 8, 15717)
+    assert need >= pre + 15717 * 32 * 128 * 4
+    args = (FAKE, 8192, FAKE, None, FAKE, FAKE, FAKE, FAKE, 8, 15717, FAKE, FAKE)
+    st, msg = _status(gdn.gdn_prefill_fused, d, *args, FAKE, need - 1, 0)
+    assert st == _lib.GDN_ERR_WORKSPACE and str(need) in msg
+    assert _status(gdn.gdn_prefill_fused, d, *args, None, need, 0)[0] == _lib.GDN_ERR_WORKSPACE
+    assert _status(gdn.gdn_prefill_fused, d, *args, FAKE + 16, need, 0)[0] == _lib.GDN_ERR_ALIGN
+    # x, conv_w and the pointer arrays are required; x rows must hold every channel
+    no_x = (None,) + args[1:]
+    assert _status(gdn.gdn_prefill_fused, d, *no_x, FAKE, need, 0)[0] == _lib.GDN_ERR_NULL
+    no_cs = args[:11] + (None,)
+    assert _status(gdn.gdn_prefill_fused, d, *no_cs, FAKE, need, 0)[0] == _lib.GDN_ERR_NULL
+    short = (FAKE, 8000) + args[2:]
+    assert _status(gdn.gdn_prefill_fused, d, *short, FAKE, need, 0)[0] == _lib.GDN_ERR_SHAPE
+    odd = (FAKE, 8196) + args[2:]  # 8196 bf16 = 16392 bytes: not a multiple of 16
+    assert _status(gdn.gdn_prefill_fused, d, *odd, FAKE, need, 0)[0] == _lib.GDN_ERR_ALIGN
+    bad_b = args[:3] + (FAKE + 8,) + args[4:]
+    assert _status(gdn.gdn_prefill_fused, d, *bad_b, FAKE, need, 0)[0] == _lib.GDN_ERR_ALIGN
+    assert _status(gdn.gdn_prefill_fused, d, *args[:8], 0, 5, *args[10:], FAKE, need, 0)[0] == _lib.GDN_ERR_SHAPE
+    assert _status(gdn.gdn_prefill_fused, dims(conv_width=9), *args, FAKE, need, 0)[0] == _lib.GDN_ERR_UNSUPPORTED
+    # no sequences: no-op
+    gdn.gdn_prefill_fused(d, *args[:8], 0, 0, None, None, None, 0, 0)
+
+
 def test_prefill_form_workspace():
     """The chunk-parallel form needs room for per-segment state maps; AUTO takes it below
     256 state-row workgroups ((d / 16) * Hv * num_seqs) and matches the explicit choice."""
