@@ -207,9 +207,10 @@ Workspace carve(void* base, int hk, int hv, int d, int chunk, int num_seqs, int 
 
 // ------------------------------------------------------------------------ chunk table
 // One workgroup. Each thread reads its sequence's bounds once (all reads independent),
-// the chunk counts are scanned in LDS, and each thread writes its own sequence's chunk
-// entries; the longest-first order is ranked from lengths kept in LDS, so the kernel
-// makes a single dependent round trip to global memory.
+// the chunk counts are scanned (in LDS; by shuffles within one wave up to 64
+// sequences), and the chunk entries are written; the longest-first order is ranked from
+// lengths kept on chip, so the kernel makes a single dependent round trip to global
+// memory.
 __global__ __launch_bounds__(kMetaThreads) void chunk_table_kernel(const int* __restrict__ cu, int N, int C,
                                                                   Workspace w) {
   __shared__ int scan[kMetaThreads];
@@ -217,6 +218,63 @@ __global__ __launch_bounds__(kMetaThreads) void chunk_table_kernel(const int* __
   __shared__ int lens[kLptMaxSeqs];
   const int tid = threadIdx.x;
   const bool segmented = w.segmented != 0;
+  if (N <= 64) {
+    // Up to 64 sequences: one wave, lane s = sequence s; scans by shuffles (no LDS, no
+    // barriers), and each sequence's entries written by all 64 lanes.
+    if (tid >= 64) return;
+    const int lane = tid;
+    int start = 0, len = 0;
+    if (lane < N) {
+      start = cu[lane];
+      len = cu[lane + 1] - start;
+    }
+    const int nc = (len + C - 1) / C;
+    const int sc = segment_len(nc);
+    const int ns = segmented ? (nc + sc - 1) / sc : 0;
+    int inc = nc, inc_s = ns;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(inc, off, 64), us = __shfl_up(inc_s, off, 64);
+      if (lane >= off) {
+        inc += u;
+        inc_s += us;
+      }
+    }
+    const int first = inc - nc, first_seg = inc_s - ns;
+    if (lane < N) {
+      w.chunk_off[lane] = first;
+      if (segmented) w.seg_off[lane] = first_seg;
+    }
+    if (lane == 0) {
+      const int total = __builtin_amdgcn_readlane(inc, 63), total_s = __builtin_amdgcn_readlane(inc_s, 63);
+      w.chunk_off[N] = total;
+      *w.n_chunks = total;
+      if (segmented) {
+        w.seg_off[N] = total_s;
+        *w.n_segs = total_s;
+      }
+    }
+    for (int q = 0; q < N; ++q) {
+      const int fq = __builtin_amdgcn_readlane(first, q), nq = __builtin_amdgcn_readlane(nc, q);
+      const int sq = __builtin_amdgcn_readlane(start, q), lq = __builtin_amdgcn_readlane(len, q);
+      for (int c = lane; c < nq; c += 64) w.table[fq + c] = make_int4(q, sq + c * C, min(C, lq - c * C), c);
+      if (segmented) {
+        const int gq = __builtin_amdgcn_readlane(first_seg, q), mq = __builtin_amdgcn_readlane(ns, q);
+        const int scq = __builtin_amdgcn_readlane(sc, q);
+        for (int g = lane; g < mq; g += 64) w.seg_table[gq + g] = make_int4(q, g * scq, min(nq, (g + 1) * scq), g == mq - 1);
+      }
+    }
+    // longest sequence first (ties by index)
+    if (lane < N) {
+      int rank = 0;
+      for (int q = 0; q < N; ++q) {
+        const int lq = __builtin_amdgcn_readlane(len, q);
+        rank += (lq > len) || (lq == len && q < lane);
+      }
+      w.order[rank] = lane;
+    }
+    return;
+  }
   int carry = 0, carry_seg = 0;
   for (int base = 0; base < N; base += kMetaThreads) {
     const int s = base + tid;
