@@ -9,16 +9,20 @@ One step = one pass of the whole hot path:
     eager (one ctypes call per launch) step is timed too, and so is the same step as
     one gdn_decode_fused call per layer (conv + commit + norm + delta rule);
   * prefill: one 4096-token sequence (16 q/k heads, 32 v-heads, d = 128, bf16 input,
-    chunk 64) = gdn_conv_update (prefill mode) + gdn_prefill_chunked. The 8-sequence
-    ragged pack (T = 15717) is timed as well.
+    chunk 64) = gdn_conv_update (prefill mode) + gdn_prefill_chunked, and the same as one
+    gdn_prefill_fused call. The 8-sequence ragged pack (T = 15717) and one GPU's share
+    of an 8-way head split (2 q/k, 4 v heads) are timed as well.
 Inputs are seeded synthetic data already resident in HBM when timing starts.
 
 `value` is the decode state bandwidth: 30 * m * 4 MiB (each slot-layer reads and writes
 its 2 MiB state once) over the graph-replayed decode step. Prefill is reported as
 tokens/s and as algorithmic TFLOP/s against the bf16 MFMA peak. `roofline` is for the
 dominant kernel (the decode kernel), whose average launch time is measured with HIP
-events around back-to-back launches on the stream it runs on. `cpu_baseline` times the
-fp64 oracle on a bounded sample of the same decode workload on the host.
+events around back-to-back launches on the stream it runs on. `ceilings` are this GPU's
+measured practical rates (a 4 GiB device copy, a bf16 8192^3 matmul), next to which the
+decode and prefill rates are also stated. `cpu_baseline` times the fp64 oracle on a
+bounded sample of the same decode workload on one host thread (`cpu_baseline_all_cores`:
+one single-threaded process per usable core, at most 16).
 """
 
 from __future__ import annotations
@@ -255,6 +259,121 @@ def cpu_baseline(seconds: float) -> dict:
                       f"NumPy on 1 thread; host has {os.cpu_count()} logical CPUs"}
 
 
+def _oracle_worker(args):
+    """One host process: the oracle's decode layer on its own slot-layers for `seconds`."""
+    seconds, seed = args
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        ctx = None
+    from gen import make_decode_pool, make_decode_step
+    from oracle import decode_layer
+
+    pool = make_decode_pool(3, pool=4)
+    sh = pool["shape"]
+    done, step = 0, seed * 1000
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        inp = make_decode_step(3, step, 4)
+        decode_layer(inp["x"], pool["conv_w"], pool["conv_state"], pool["S"], inp["g"], inp["beta"],
+                     sh.num_k_heads, sh.num_v_heads, sh.head_dim, in_dtype="bf16")
+        done += 4
+        step += 1
+    return done, time.perf_counter() - t0
+
+
+def host_cpu() -> dict:
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count() or 1
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def cpu_baseline_pool(seconds: float) -> dict:
+    """The same oracle sharded over every usable host core: one process per core, each on
+    its own slot-layers (independent units), single-threaded, for `seconds`."""
+    import multiprocessing as mp
+
+    n = min(host_cpu()["usable_cpus"], 16)  # (at most 16: the GPU box's CPU share)
+    ctx = mp.get_context("spawn")  # (a fresh interpreter: nothing of this process's GPU state)
+    with ctx.Pool(n) as pool:
+        res = pool.map(_oracle_worker, [(seconds, i) for i in range(n)])
+    done = sum(r[0] for r in res)
+    dt = max(r[1] for r in res)
+    return {"value": round(done * STATE_BYTES_PER_SLOT_LAYER / dt / 1e9, 4), "unit": "GB/s", "cores": n,
+            "kind": "oracle", "sample": f"{done} slot-layers over {n} single-threaded processes, {dt:.1f} s"}
+
+
+def ceilings() -> dict:
+    """Measured practical ceilings of this GPU: a device-to-device copy of 4 GiB (read +
+    write bytes over time) and a bf16 8192 x 8192 x 8192 matmul; medians of 5."""
+    import statistics
+
+    import torch
+
+    out = {}
+    src = torch.empty(1 << 30, dtype=torch.float32, device="cuda").fill_(1.0)  # 4 GiB
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(5):
+        a, b = ev(), ev()
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    out["d2d_copy_4GiB_GBps"] = round(2 * src.numel() * 4 / (statistics.median(ts) * 1e-3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    n = 8192
+    x = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    y = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    z = torch.matmul(x, y)
+    ts = []
+    for _ in range(5):
+        a, b = ev(), ev()
+        a.record()
+        z = torch.matmul(x, y)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    out["bf16_matmul_8192_TFLOPs"] = round(2 * n ** 3 / (statistics.median(ts) * 1e-3) / 1e12, 1)
+    del x, y, z
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_graph_scrubbed(rig: DecodeRig, steps: int, scrub) -> float:
+    """Median ms of single graph-replayed decode steps, each after a 1 GiB write that
+    evicts the states from the GPU's caches (the write is outside the timed region)."""
+    import statistics
+
+    import torch
+
+    ts = []
+    for _ in range(steps):
+        scrub.fill_(0.0)
+        a, b = ev(), ev()
+        a.record()
+        rig.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return statistics.median(ts)
+
+
 def time_graph(rig: DecodeRig, steps: int, warmup: int) -> float:
     """Mean ms per graph-replayed decode step."""
     import torch
@@ -314,11 +433,19 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true", help="also run a 256 MiB device copy (counter scale)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured copy / matmul ceilings")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the GDN layer core here has no multi-GPU path (no collectives, "
               "no sharding code); run it with --gpus 1", file=sys.stderr)
         return 2
+
+    # the oracle over every host core first, in processes started before this one touches
+    # the GPU
+    cpu_pool = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on all host cores")
+        cpu_pool = cpu_baseline_pool(args.cpu_seconds / 2)
 
     import torch
 
@@ -363,6 +490,7 @@ def main() -> int:
     sweep = None
     if not args.no_sweep:
         sweep = {}
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
         for mm in (1, 4, 16):
             row = {}
             for fused in (False, True):
@@ -376,6 +504,11 @@ def main() -> int:
                 row[tag + "ms_per_step"] = round(ms, 4)
                 row[tag + "state_GBps"] = round(r.layers * mm * STATE_BYTES_PER_SLOT_LAYER / ms / 1e6, 1)
                 row[tag + "decode_kernel_us"] = round(kus, 2)
+                if mm * 60 < 256:  # state footprint fits the Infinity Cache: also from cold caches
+                    sms = time_graph_scrubbed(r, max(5, K // 2), scrub)
+                    row[tag + "scrubbed_ms_per_step"] = round(sms, 4)
+                    row[tag + "scrubbed_state_GBps"] = round(r.layers * mm * STATE_BYTES_PER_SLOT_LAYER / sms / 1e6,
+                                                             1)
                 del r
                 torch.cuda.empty_cache()
             row["note"] = (("state footprint (%d MiB over 30 layers) fits the 256 MB Infinity Cache" % (mm * 60))
@@ -428,11 +561,20 @@ def main() -> int:
             torch.cuda.empty_cache()
             log(f"prefill {name}: {ms:.3f} ms")
 
+    ceil = None
+    if not args.no_ceilings:
+        log("measuring the copy and matmul ceilings")
+        ceil = ceilings()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on host cores")
         cpu = cpu_baseline(args.cpu_seconds)
 
+    if ceil and prefill:
+        for row in prefill.values():
+            row["frac_of_measured_bf16_matmul"] = round(row["algorithmic_TFLOPs"] / ceil["bf16_matmul_8192_TFLOPs"],
+                                                        5)
     out = {
         "metric": "GDN decode state GB/s (m=64) + prefill tokens/s; % of HBM / MFMA peak",
         "value": round(value, 2),
@@ -458,6 +600,7 @@ def main() -> int:
                    "state_GBps_graph": round(value, 2),
                    "state_GBps_eager": round(state_bytes_step / (eager_ms * 1e-3) / 1e9, 2),
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                   "frac_of_measured_copy": round(value / ceil["d2d_copy_4GiB_GBps"], 4) if ceil else None,
                    "decode_kernel_us": round(kern_us, 2)},
         "decode_fused": {"note": "the same step as one gdn_decode_fused call per layer",
                          "graph_ms_per_step": round(f_graph_ms, 4),
@@ -472,8 +615,13 @@ def main() -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.m == 64 else None,
                      "bytes_per_launch": bytes_per_launch,
-                     "avg_launch_us": round(kern_us, 2)},
+                     "avg_launch_us": round(kern_us, 2),
+                     "measured_ceiling_GBps": ceil["d2d_copy_4GiB_GBps"] if ceil else None,
+                     "frac_of_measured_ceiling": round(achieved / ceil["d2d_copy_4GiB_GBps"], 4) if ceil else None},
+        "ceilings": ceil,
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_pool,
+        "host_cpu": host_cpu(),
         "wall_s": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
