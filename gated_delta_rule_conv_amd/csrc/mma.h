@@ -202,6 +202,7 @@ struct FragIO<kPolFP32> {
   __device__ __forceinline__ static void store(char* blk, int lane, const float* x) {
     *reinterpret_cast<float4*>(blk + lane * 16) = make_float4(x[0], x[1], x[2], x[3]);
   }
+  __device__ __forceinline__ static void store_frag(char* blk, int lane, const M::Frag& f) { store(blk, lane, f.v); }
 };
 
 template <>
@@ -219,6 +220,11 @@ struct FragIO<kPolBF16X3> {
     M::split(x, h, l);
     *reinterpret_cast<bf16x8*>(blk + lane * 16) = h;
     *reinterpret_cast<bf16x8*>(blk + 1024 + lane * 16) = l;
+  }
+  // an already split fragment
+  __device__ __forceinline__ static void store_frag(char* blk, int lane, const M::Frag& f) {
+    *reinterpret_cast<bf16x8*>(blk + lane * 16) = f.hi;
+    *reinterpret_cast<bf16x8*>(blk + 1024 + lane * 16) = f.lo;
   }
 };
 

@@ -426,12 +426,15 @@ __device__ __forceinline__ void conv_qk_rows(const PrefillArgs& a, int h, int t0
 
 // LDS of the intra-chunk kernel, in floats. K^ and Q^ live only until K K^T and Q K^T are
 // in registers; then G and QK take K^'s place and A and T take Q^'s, so the peak is two
-// C x (D+4) areas (70 KB at C = 64, D = 128) and two workgroups fit on a CU.
+// areas, each the largest of K^ as fp32 rows, K^ as bf16 hi and lo planes and two C x C
+// matrices (70 KB at C = 64, D = 128), and two workgroups fit on a CU.
 template <int D, int C>
 struct IntraLayout {
   static constexpr int KP = D + 4;  // padded row of K^/Q^
   static constexpr int CP = C + 4;  // padded row of C x C matrices
-  static constexpr int RS = (C * KP > 2 * C * CP) ? C * KP : 2 * C * CP;  // one area
+  static constexpr int KHF = D + 8;  // a row of K^ (or Q^) as bf16 hi and lo planes, in floats
+  static constexpr int RS0 = (C * KP > 2 * C * CP) ? C * KP : 2 * C * CP;
+  static constexpr int RS = (RS0 > C * KHF) ? RS0 : C * KHF;  // one area
   static constexpr int OFF_K = 0;        // K^   alias  G, QK
   static constexpr int OFF_G = 0;
   static constexpr int OFF_QK = C * CP;
@@ -489,8 +492,16 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     conv_qk_rows<D, C, KP>(a, h, t0, n, t0 - ent.w * C, ent.x, Kh, Qh, tid);
     __syncthreads();
   }
-  for (int row = tid / TPR; row < C; row += kThreads / TPR) {
-    const int part = tid % TPR;
+  // With bf16x3 products, K^ and Q^ are kept as bf16 hi and lo planes ([C][KH] each, the
+  // lo plane after the hi one, in the same LDS area as the fp32 rows): split once here,
+  // then read as they are by the products and the export below.
+  constexpr bool kPlanes = POL == kPolBF16X3;
+  constexpr int KH = Lo::KHF;  // plane row length (elements)
+  static_assert(kThreads / TPR >= C, "one pass over the rows");
+  auto* Khp = reinterpret_cast<__bf16*>(smem + Lo::OFF_K);
+  auto* Qhp = reinterpret_cast<__bf16*>(smem + Lo::OFF_Q);
+  {
+    const int row = tid / TPR, part = tid % TPR;
     float kv[EPT], qv[EPT];
     const bool live = row < n;
     if (live && fused) {
@@ -503,6 +514,9 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
 #pragma unroll
       for (int e = 0; e < EPT; ++e) kv[e] = qv[e] = 0.f;
     }
+    // (the planes overlap the fp32 rows the fused conv left in LDS: all of those are in
+    // registers before any plane is written)
+    if (kPlanes && fused) __syncthreads();
     float kk = 0.f, qq = 0.f;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
@@ -513,15 +527,55 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     qq = group_sum<TPR>(qq);
     const float rk = live ? 1.0f / sqrtf(kk + r.eps) : 0.f;
     const float rq = live ? r.scale / sqrtf(qq + r.eps) : 0.f;
+    if (row < C) {
 #pragma unroll
-    for (int e = 0; e < EPT; e += 4) {
-      *reinterpret_cast<float4*>(&Kh[row][part * EPT + e]) =
-          make_float4(kv[e] * rk, kv[e + 1] * rk, kv[e + 2] * rk, kv[e + 3] * rk);
-      *reinterpret_cast<float4*>(&Qh[row][part * EPT + e]) =
-          make_float4(qv[e] * rq, qv[e + 1] * rq, qv[e + 2] * rq, qv[e + 3] * rq);
+      for (int e = 0; e < EPT; ++e) {
+        kv[e] *= rk;
+        qv[e] *= rq;
+      }
+      if constexpr (kPlanes) {
+        // (4 values at a time, as EPT is 4 at d = 32; the split is Mma<>::split's)
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4) {
+          bf16x4 kh, kl4, qh, ql4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            kh[i] = static_cast<__bf16>(kv[e + i]);
+            kl4[i] = static_cast<__bf16>(kv[e + i] - static_cast<float>(kh[i]));
+            qh[i] = static_cast<__bf16>(qv[e + i]);
+            ql4[i] = static_cast<__bf16>(qv[e + i] - static_cast<float>(qh[i]));
+          }
+          const int o = row * KH + part * EPT + e;
+          *reinterpret_cast<bf16x4*>(Khp + o) = kh;
+          *reinterpret_cast<bf16x4*>(Khp + C * KH + o) = kl4;
+          *reinterpret_cast<bf16x4*>(Qhp + o) = qh;
+          *reinterpret_cast<bf16x4*>(Qhp + C * KH + o) = ql4;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4) {
+          *reinterpret_cast<float4*>(&Kh[row][part * EPT + e]) = make_float4(kv[e], kv[e + 1], kv[e + 2], kv[e + 3]);
+          *reinterpret_cast<float4*>(&Qh[row][part * EPT + e]) = make_float4(qv[e], qv[e + 1], qv[e + 2], qv[e + 3]);
+        }
+      }
     }
   }
   __syncthreads();
+  // the A-operand fragment of row t, head-dim values d0 .. d0 + KPL - 1 of K^ (or Q^)
+  auto frag_of = [&](bool isq, int t, int d0) {
+    if constexpr (kPlanes) {
+      const __bf16* base = (isq ? Qhp : Khp) + t * KH + d0;
+      typename M::Frag f;
+      f.hi = *reinterpret_cast<const bf16x8*>(base);
+      f.lo = *reinterpret_cast<const bf16x8*>(base + C * KH);
+      return f;
+    } else {
+      float x[KPL];
+      load_k<KPL>(isq ? &Qh[t][d0] : &Kh[t][d0], x);
+      return M::frag(x);
+    }
+  };
 
   // 1b. export K^ and Q^ as A operands in fragment order. Thread e writes lane e % 64 of
   // fragment block e / 64, so each wave stores whole contiguous KiBs.
@@ -531,14 +585,8 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     for (int e = tid; e < (C / 16) * NVF * 64; e += kThreads) {
       const int blk = e / 64, ln = e % 64;
       const int t = (blk / NVF) * 16 + ln % 16, d0 = (blk % NVF) * KSTEP + KPL * (ln / 16);
-      float kx[KPL], qx[KPL];
-#pragma unroll
-      for (int i = 0; i < KPL; ++i) {
-        kx[i] = Kh[t][d0 + i];
-        qx[i] = Qh[t][d0 + i];
-      }
-      FIO::store(kq + static_cast<size_t>(blk) * FIO::BYTES, ln, kx);
-      FIO::store(qq + static_cast<size_t>(blk) * FIO::BYTES, ln, qx);
+      FIO::store_frag(kq + static_cast<size_t>(blk) * FIO::BYTES, ln, frag_of(false, t, d0));
+      FIO::store_frag(qq + static_cast<size_t>(blk) * FIO::BYTES, ln, frag_of(true, t, d0));
     }
   }
 
@@ -558,16 +606,11 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
         int ti = 0;
         while ((ti + 1) * (ti + 2) / 2 <= it) ++ti;
         const int tj = it - ti * (ti + 1) / 2;
-        const float(*Aop)[KP] = isq ? Qh : Kh;
         f32x4 a3[3];
         zero3(a3);
 #pragma unroll
-        for (int v = 0; v < NVF; ++v) {
-          float av[KPL], bv[KPL];
-          load_k<KPL>(&Aop[ti * 16 + l16][kl + v * KSTEP], av);
-          load_k<KPL>(&Kh[tj * 16 + l16][kl + v * KSTEP], bv);
-          M::mma3(a3, M::frag(av), M::frag(bv));
-        }
+        for (int v = 0; v < NVF; ++v)
+          M::mma3(a3, frag_of(isq, ti * 16 + l16, kl + v * KSTEP), frag_of(false, tj * 16 + l16, kl + v * KSTEP));
         res[q] = total(a3);
       }
     }
