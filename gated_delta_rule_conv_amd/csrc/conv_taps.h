@@ -122,23 +122,21 @@ struct ConvTaps {
   }
 };
 
-// The conv of 8 adjacent channels straight from the loaded (raw) taps [8][K], bias,
-// K-1 preceding rows and current token, converting one channel at a time so that few
-// values are live at once. The operations and their order are those of ConvTaps::apply
-// (acc = b; acc = fma(w_j, z_j, acc) for j = 0 .. K-1; then the activation), so both
-// give the same bits.
+// The conv of 4 adjacent channels straight from the loaded (raw) vectors: the taps
+// [4][K] as K vectors of 4, the bias, the K-1 preceding rows and the current token. The
+// operations and their order are those of ConvTaps::apply (acc = b; acc = fma(w_j, z_j,
+// acc) for j = 0 .. K-1; then the activation), so both give the same bits.
 template <typename T, int K>
-__device__ __forceinline__ void conv8_raw(const typename Vec8<T>::Raw (&wr)[K], const typename Vec8<T>::Raw& br,
-                                          bool has_b, const typename Vec8<T>::Raw (&rows)[K - 1],
-                                          const typename Vec8<T>::Raw& cur, bool silu, float (&out)[kConvVec]) {
-  using V8 = Vec8<T>;
+__device__ __forceinline__ void conv4_raw(const typename Vec4<T>::Raw (&wr)[K], const typename Vec4<T>::Raw& br,
+                                          bool has_b, const typename Vec4<T>::Raw (&rows)[K - 1],
+                                          const typename Vec4<T>::Raw& cur, bool silu, float (&out)[4]) {
+  using V4 = Vec4<T>;
 #pragma unroll
-  for (int c = 0; c < kConvVec; ++c) {
-    float acc = has_b ? V8::elem(br, c) : 0.f;
+  for (int c = 0; c < 4; ++c) {
+    float acc = has_b ? V4::elem(br, c) : 0.f;
 #pragma unroll
-    for (int j = 0; j < K - 1; ++j)
-      acc = fmaf(V8::elem(wr[(c * K + j) / kConvVec], (c * K + j) % kConvVec), V8::elem(rows[j], c), acc);
-    acc = fmaf(V8::elem(wr[(c * K + K - 1) / kConvVec], (c * K + K - 1) % kConvVec), V8::elem(cur, c), acc);
+    for (int j = 0; j < K - 1; ++j) acc = fmaf(V4::elem(wr[(c * K + j) / 4], (c * K + j) % 4), V4::elem(rows[j], c), acc);
+    acc = fmaf(V4::elem(wr[(c * K + K - 1) / 4], (c * K + K - 1) % 4), V4::elem(cur, c), acc);
     if (silu) acc = gdn::silu(acc);
     out[c] = acc;
   }

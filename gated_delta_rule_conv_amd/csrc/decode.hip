@@ -195,10 +195,12 @@ namespace {
 // One launch for the whole decode step of a layer: the depthwise conv of the token's
 // q, k and v channels (against the slot's conv state), the conv state commit, and the
 // decode above. A workgroup is WPB units of one (slot, v-head), i.e. VR consecutive
-// state rows. Lanes of wave 0 first convolve 8 channels each -- the 2d q/k channels of
-// the head's k-head and the VR v channels of the workgroup's rows -- into LDS with the
-// conv kernels' arithmetic (conv8_raw), while every wave's state loads are in flight;
-// the waves then take k, q and v from LDS and run decode_rows unchanged.
+// state rows. Threads first convolve 4 channels each -- the 2d q/k channels of the
+// head's k-head (wave 0) and then the VR v channels of the workgroup's rows -- into LDS
+// with the conv kernels' arithmetic (conv4_raw); their conv inputs are loaded before
+// the state rows, so the conv waits only for its own (mostly cached) inputs while the
+// state is still streaming in. The waves then take k, q and v from LDS and run
+// decode_rows unchanged.
 //
 // Conv state commit. The v channels of a workgroup's rows are read by that workgroup
 // alone, so their lanes write the shifted state right after reading it. The q/k
@@ -213,9 +215,13 @@ struct FusedCfg {
   static constexpr int BPH = NPART / WPB;                                 // workgroups per (slot, v-head)
   static constexpr int NT = WPB * kWave;
   static constexpr int VR = WPB * DecodeCfg<D, P>::ROWS;                  // state rows per workgroup
-  static constexpr int GQK = 2 * D / kConvVec;                            // q/k channel groups
-  static constexpr int GV = VR / kConvVec;                                // v channel groups
-  static_assert(GQK + GV <= kWave, "one channel group per lane of wave 0");
+  static constexpr int CV = 4;                                            // channels per conv thread
+  static constexpr int GQK = 2 * D / CV;                                  // q/k channel groups
+  static constexpr int GV = VR / CV;                                      // v channel groups
+  static constexpr int NCG = GQK + GV;
+  static constexpr int NCW = (NCG + kWave - 1) / kWave;                   // waves that convolve
+  static_assert(GQK <= kWave, "the q/k groups are wave 0's");
+  static_assert(NCG <= NT, "one channel group per thread");
   // One-pass units with bf16 inputs fit 72 VGPRs, i.e. 7 waves per SIMD (one register
   // more would cost a wave); fp32 inputs need more registers for the raw conv inputs.
   template <typename T>
@@ -226,14 +232,14 @@ template <typename T, int K, int D, int P, bool SCHED_FENCE>
 __global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min_blocks<T>())) void fused_decode_kernel(FusedArgs f) {
   using Cfg = DecodeCfg<D, P>;
   using FC = FusedCfg<D, P>;
-  using V8 = Vec8<T>;
+  using V4 = Vec4<T>;
   constexpr int LPR = Cfg::LPR, RPP = Cfg::RPP, ROWS = Cfg::ROWS;
-  constexpr int WPB = FC::WPB, BPH = FC::BPH, VR = FC::VR, GQK = FC::GQK, GV = FC::GV;
-  constexpr int V = kConvVec;
+  constexpr int WPB = FC::WPB, BPH = FC::BPH, VR = FC::VR, GQK = FC::GQK, GV = FC::GV, NCG = FC::NCG;
+  constexpr int V = FC::CV;
   typedef __attribute__((address_space(1))) T GT;
   __shared__ __attribute__((aligned(16))) float yqk[2 * D];  // q then k of the k-head
   __shared__ __attribute__((aligned(16))) float yv[VR];
-  __shared__ typename Vec8<T>::Raw qk_rows[K - 1][GQK];  // new q/k conv-state rows
+  __shared__ typename V4::Raw qk_rows[K - 1][GQK];  // new q/k conv-state rows
   const RecurArgs& a = f.r;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -253,9 +259,27 @@ __global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min
   GT* cs = (GT*)reinterpret_cast<T*>(cp);
   const int C = f.channels;
 
-  // State rows first (every wave), then wave 0's conv inputs, lane l taking channel
-  // group l (q/k groups, then v groups; lanes past them repeat a group and drop it).
-  // Everything is in flight before anything waits.
+  // Conv inputs first: thread t < NCG takes channel group t (q/k groups, then v groups);
+  // other threads that load repeat a v group and drop the result. Then every wave's
+  // state rows, so that all loads are in flight before anything waits. (With two passes
+  // per wave every wave loads conv inputs: there, loads under the branch made the
+  // compiler copy their results at its end, which waits for them before the state loads
+  // can issue.)
+  const bool conv_wave = w < FC::NCW;
+  const int grp = tid < NCG ? tid : GQK + (tid - NCG) % GV;
+  const bool is_qk = grp < GQK;
+  const int ch0 = is_qk ? (grp * V < D ? h * D + grp * V : a.hk * D + h * D + (grp * V - D))
+                        : 2 * a.hk * D + j * D + bh * VR + (grp - GQK) * V;
+  typename V4::Raw xr, sr[K - 1], wr[K], br;
+  if (conv_wave || P > 1) {
+#pragma unroll
+    for (int t = 0; t < K - 1; ++t) sr[t] = V4::load_raw_g(cs + static_cast<int64_t>(t) * C + ch0);
+    xr = V4::load_raw(static_cast<const T*>(f.x) + static_cast<int64_t>(i) * f.x_stride + ch0);
+#pragma unroll
+    for (int t = 0; t < K; ++t) wr[t] = V4::load_raw(static_cast<const T*>(f.w) + static_cast<int64_t>(ch0) * K + t * V);
+    // with no bias, taps stand in for the load and are never used
+    br = V4::load_raw(static_cast<const T*>(f.b ? f.b : f.w) + ch0);
+  }
   f32x4 s[P][4];
 #pragma unroll
   for (int p = 0; p < P; ++p)
@@ -265,41 +289,27 @@ __global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min
   const int64_t gi = static_cast<int64_t>(i) * a.hv + j;
   const float gval = ((cfloat*)a.g)[gi];
   const float beta = ((cfloat*)a.beta)[gi];
-  const int grp = lane % (GQK + GV);
-  const bool is_qk = grp < GQK;
-  const int ch0 = is_qk ? (grp * V < D ? h * D + grp * V : a.hk * D + h * D + (grp * V - D))
-                        : 2 * a.hk * D + j * D + bh * VR + (grp - GQK) * V;
   if constexpr (SCHED_FENCE) __builtin_amdgcn_sched_barrier(0);
 
-  // Wave 0 alone reads conv state. Once its reads have returned (their values are
+  // Only wave 0 reads q/k conv state. Once its reads have returned (their values are
   // consumed here) it counts this workgroup in, with a relaxed atomic: no later write
   // can reach a read that is done, and the commit needs nothing from the other
   // workgroups but the count itself. (Acquire or release at device scope would write
   // back and invalidate this XCD's L2.) The count comes back while the waves compute.
   int32_t* ctr = f.counters + static_cast<int64_t>(i) * a.hk + h;
   int before = 0;
-  if (w == 0) {
-    // (loads and arithmetic in one block: no raw value lives past it)
-    typename V8::Raw xr, sr[K - 1], wr[K], br;
-#pragma unroll
-    for (int t = 0; t < K; ++t) wr[t] = V8::load_raw(static_cast<const T*>(f.w) + static_cast<int64_t>(ch0) * K + t * V);
-#pragma unroll
-    for (int t = 0; t < K - 1; ++t) sr[t] = V8::load_raw_g(cs + static_cast<int64_t>(t) * C + ch0);
-    xr = V8::load_raw(static_cast<const T*>(f.x) + static_cast<int64_t>(i) * f.x_stride + ch0);
-    // with no bias, taps stand in for the load and are never used
-    br = V8::load_raw(static_cast<const T*>(f.b ? f.b : f.w) + ch0);
+  if (conv_wave) {
     float out[V];
-    conv8_raw<T, K>(wr, br, f.b != nullptr, sr, xr, f.silu != 0, out);
-    if (lane < GQK + GV) {
+    conv4_raw<T, K>(wr, br, f.b != nullptr, sr, xr, f.silu != 0, out);
+    if (tid < NCG) {
       float* dst = is_qk ? &yqk[grp * V] : &yv[(grp - GQK) * V];
       *reinterpret_cast<f32x4*>(dst) = f32x4{out[0], out[1], out[2], out[3]};
-      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{out[4], out[5], out[6], out[7]};
       // new conv-state rows = old rows 1 .. K-2, then x
       if (!is_qk) {
-        // v channels: this lane is their only reader, so they are written now
+        // v channels: this thread is their only reader, so they are written now
 #pragma unroll
-        for (int t = 0; t < K - 2; ++t) V8::store_raw_g(cs + static_cast<int64_t>(t) * C + ch0, sr[t + 1]);
-        V8::store_raw_g(cs + static_cast<int64_t>(K - 2) * C + ch0, xr);
+        for (int t = 0; t < K - 2; ++t) V4::store_raw_g(cs + static_cast<int64_t>(t) * C + ch0, sr[t + 1]);
+        V4::store_raw_g(cs + static_cast<int64_t>(K - 2) * C + ch0, xr);
       } else {
         // q/k channels: kept in LDS for the commit, in case this workgroup is the last
 #pragma unroll
@@ -307,9 +317,13 @@ __global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min
         qk_rows[K - 2][grp] = xr;
       }
     }
-    if (lane == 0) before = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) before = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
+  // A barrier that orders LDS only: the waves' state loads (and wave 0's count) stay in
+  // flight across it, where __syncthreads() would wait for all of them.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
   f32x4 kv[4], qv[4];
 #pragma unroll
@@ -327,7 +341,7 @@ __global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min
   if (w == 0 && __builtin_amdgcn_readfirstlane(before) == (a.hv / a.hk) * BPH - 1) {
     if (lane < GQK) {
 #pragma unroll
-      for (int t = 0; t < K - 1; ++t) V8::store_raw_g(cs + static_cast<int64_t>(t) * C + ch0, qk_rows[t][lane]);
+      for (int t = 0; t < K - 1; ++t) V4::store_raw_g(cs + static_cast<int64_t>(t) * C + ch0, qk_rows[t][lane]);
     }
     if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

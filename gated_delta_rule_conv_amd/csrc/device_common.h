@@ -113,6 +113,45 @@ struct Vec8<uint16_t> {
   }
 };
 
+// 4 consecutive elements of dtype T as loaded: 8 bytes (bf16) or 16 bytes (fp32), aligned
+// to their size.
+template <typename T>
+struct Vec4;
+
+template <>
+struct Vec4<float> {
+  typedef f32x4 Raw;
+  typedef __attribute__((address_space(1))) float GT;
+  __device__ __forceinline__ static Raw load_raw(const float* p) { return *reinterpret_cast<const Raw*>(p); }
+  __device__ __forceinline__ static Raw load_raw_g(const GT* p) {
+    typedef __attribute__((address_space(1))) const Raw G4;
+    return *(G4*)p;
+  }
+  __device__ __forceinline__ static void store_raw_g(GT* p, const Raw& r) {
+    typedef __attribute__((address_space(1))) Raw G4;
+    *(G4*)p = r;
+  }
+  __device__ __forceinline__ static float elem(const Raw& r, int e) { return r[e]; }
+};
+
+template <>
+struct Vec4<uint16_t> {
+  typedef uint32_t Raw __attribute__((ext_vector_type(2)));  // 4 bf16 as loaded
+  typedef __attribute__((address_space(1))) uint16_t GT;
+  __device__ __forceinline__ static Raw load_raw(const uint16_t* p) { return *reinterpret_cast<const Raw*>(p); }
+  __device__ __forceinline__ static Raw load_raw_g(const GT* p) {
+    typedef __attribute__((address_space(1))) const Raw G2;
+    return *(G2*)p;
+  }
+  __device__ __forceinline__ static void store_raw_g(GT* p, const Raw& r) {
+    typedef __attribute__((address_space(1))) Raw G2;
+    *(G2*)p = r;
+  }
+  __device__ __forceinline__ static float elem(const Raw& a, int e) {
+    return (e & 1) ? __uint_as_float(a[e >> 1] & 0xFFFF0000u) : __uint_as_float(a[e >> 1] << 16);
+  }
+};
+
 // ---------------------------------------------------------------- DPP reductions
 // dpp_ctrl encodings (GCN/CDNA DPP): quad_perm [1,0,3,2] = 0xB1 (lane ^ 1),
 // quad_perm [2,3,0,1] = 0x4E (lane ^ 2), row_half_mirror = 0x141 (lane i <-> 7 - i
