@@ -184,22 +184,27 @@ __global__ __launch_bounds__(kThreads) void conv_commit_kernel(ConvArgs a) {
 template <typename T, int K>
 __global__ __launch_bounds__(kDecThreads) void conv_decode_kernel(ConvArgs a) {
   typedef __attribute__((address_space(4))) const uint64_t cu64;
-  const int ch0 = (blockIdx.x * kDecThreads + threadIdx.x) * kVec;
-  if (ch0 >= a.channels) return;
-  const int i = blockIdx.y;
-  const uint64_t sp = ((cu64*)a.state_ptrs)[i];
-  if (sp == 0) return;
   const int C = a.channels;
-  using GT = __attribute__((address_space(1))) T;
-  GT* cs = (GT*)reinterpret_cast<T*>(sp);
+  const int cg = (blockIdx.x * kDecThreads + threadIdx.x) * kVec;
+  const bool live = cg < C;
+  const int ch0 = live ? cg : 0;  // (threads past the channels load channel 0 and store nothing)
+  const int i = blockIdx.y;
+  // the loads that do not need the slot pointer go first, so they overlap its load
   typename Vec8<T>::Raw wr[K], sr[K - 1], xr, br;
 #pragma unroll
   for (int j = 0; j < K; ++j) wr[j] = Vec8<T>::load_raw(static_cast<const T*>(a.w) + static_cast<int64_t>(ch0) * K + j * kVec);
-#pragma unroll
-  for (int r = 0; r < K - 1; ++r) sr[r] = Vec8<T>::load_raw_g(cs + static_cast<int64_t>(r) * C + ch0);
   xr = Vec8<T>::load_raw(static_cast<const T*>(a.x) + static_cast<int64_t>(i) * a.x_stride + ch0);
   const bool has_b = a.b != nullptr;
   br = Vec8<T>::load_raw(static_cast<const T*>(has_b ? a.b : a.w) + ch0);  // (taps as a stand-in when no bias)
+  // An inactive slot (zero pointer) reads the taps in place of a state (C x K elements,
+  // so K - 1 rows are in bounds) and stores nothing: no branch on the pointer keeps the
+  // loads above free to issue before it arrives.
+  const uint64_t sp = ((cu64*)a.state_ptrs)[i];
+  const bool act = sp != 0 && live;
+  using GT = __attribute__((address_space(1))) T;
+  GT* cs = (GT*)reinterpret_cast<T*>(sp != 0 ? sp : reinterpret_cast<uint64_t>(a.w));
+#pragma unroll
+  for (int r = 0; r < K - 1; ++r) sr[r] = Vec8<T>::load_raw_g(cs + static_cast<int64_t>(r) * C + ch0);
   ConvTaps<T, K> taps;
   taps.from_raw(wr, br, has_b);
   float win[K - 1][kVec], cur[kVec], out[kVec];
@@ -207,6 +212,7 @@ __global__ __launch_bounds__(kDecThreads) void conv_decode_kernel(ConvArgs a) {
   for (int r = 0; r < K - 1; ++r) Vec8<T>::convert(sr[r], win[r]);
   Vec8<T>::convert(xr, cur);
   taps.apply(win, cur, a.silu != 0, out);
+  if (!act) return;
   Vec8<float>::store(a.y + static_cast<int64_t>(i) * a.y_stride + ch0, out);
 #pragma unroll
   for (int r = 0; r < K - 2; ++r) Vec8<T>::store_raw_g(cs + static_cast<int64_t>(r) * C + ch0, sr[r + 1]);
