@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kDecThreads) void conv_decode_kernel(ConvArgs a) {
   Vec8<T>::store_raw_g(cs + static_cast<int64_t>(K - 2) * C + ch0, xr);
 }
 
-// mode: 0 decode, 1 prefill conv + commit, 2 prefill conv only, 3 commit only
+// mode: 0 decode, 1 prefill conv + commit, 2 prefill conv only
 template <typename T>
 hipError_t launch_all(const ConvArgs& a, hipStream_t s, int mode) {
   const unsigned gx = (a.channels / kVec + kThreads - 1) / kThreads;
@@ -234,7 +234,7 @@ hipError_t launch_all(const ConvArgs& a, hipStream_t s, int mode) {
     }
     return hipGetLastError();
   }
-  if (mode != 3 && a.total_tokens > 0) {
+  if (a.total_tokens > 0) {
     dim3 grid((a.channels + 512 * (kThreads / 64) - 1) / (512 * (kThreads / 64)), (a.total_tokens + kStrip - 1) / kStrip);
     switch (a.width) {
       case 2: conv_prefill_kernel<T, 2><<<grid, kThreads, 0, s>>>(a); break;
@@ -262,10 +262,6 @@ hipError_t launch_conv_prefill(const ConvArgs& a, hipStream_t s) {
 
 hipError_t launch_conv_prefill_only(const ConvArgs& a, hipStream_t s) {
   return a.bf16 ? launch_all<uint16_t>(a, s, 2) : launch_all<float>(a, s, 2);
-}
-
-hipError_t launch_conv_commit(const ConvArgs& a, hipStream_t s) {
-  return a.bf16 ? launch_all<uint16_t>(a, s, 3) : launch_all<float>(a, s, 3);
 }
 
 hipError_t launch_conv_decode(const ConvArgs& a, hipStream_t s) {

@@ -243,7 +243,7 @@ gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stri
   const char* xb = static_cast<const char*>(x);
   const char* wb = static_cast<const char*>(conv_w);
   const char* bb = static_cast<const char*>(conv_b);
-  // 1. the v channels' conv into the workspace (the conv states are committed last)
+  // 1. the v channels' conv into the workspace (the conv states are committed in step 2)
   gdn::ConvArgs cv{xb + qk * esz, x_stride, yv, vw, wb + qk * K * esz, bb ? bb + qk * esz : nullptr, cu_seqlens,
                    conv_state_ptrs, num_seqs, total_tokens, static_cast<int32_t>(vw), K, silu, bf16, C,
                    static_cast<int32_t>(qk)};
@@ -260,11 +260,9 @@ gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stri
   a.form = dims->prefill_form;
   a.mma = resolve_mma(dims);
   a.workspace = workspace;
-  if (gdn_status st = hip_status(gdn::launch_prefill(a, s), fn)) return st;
-  // 3. every channel's conv state: the last K-1 rows of the sequence's conv input
-  gdn::ConvArgs cc{x, x_stride, nullptr, 0, conv_w, conv_b, cu_seqlens, conv_state_ptrs, num_seqs, total_tokens,
-                   static_cast<int32_t>(C), K, silu, bf16, C, 0};
-  return hip_status(gdn::launch_conv_commit(cc, s), fn);
+  // (the chunk-0 workgroups of its intra-chunk kernel also commit every channel's conv
+  // state, after the last reader of the old rows)
+  return hip_status(gdn::launch_prefill(a, s), fn);
 }
 
 gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_stride, const float* k,

@@ -31,7 +31,6 @@ struct ConvArgs {
 
 hipError_t launch_conv_prefill(const ConvArgs& a, hipStream_t s);  // conv, then the conv-state commit
 hipError_t launch_conv_prefill_only(const ConvArgs& a, hipStream_t s);
-hipError_t launch_conv_commit(const ConvArgs& a, hipStream_t s);
 hipError_t launch_conv_decode(const ConvArgs& a, hipStream_t s);
 
 struct RecurArgs {

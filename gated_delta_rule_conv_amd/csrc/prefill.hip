@@ -424,6 +424,57 @@ __device__ __forceinline__ void conv_qk_rows(const PrefillArgs& a, int h, int t0
   }
 }
 
+// The conv-state commit of the fused entry point, for one (sequence, k-head): the
+// channels of q and k of k-head h and of v of its `group` v-heads become the last K-1
+// rows of [old conv state | the sequence's x rows] (rows before the sequence come from
+// the old state, as in the conv kernels). The chunk-0 workgroup of the pair runs it after
+// its own loader, the only reader of the old q/k rows; the v rows were read by the v
+// conv, which ran before. A thread owns 8 channels.
+template <typename T, int K, int D>
+__device__ __forceinline__ void commit_conv_rows_k(const PrefillArgs& a, int h, int group, int s, int tid) {
+  constexpr int NQ = sizeof(T) / 2;  // 16-byte pieces of 8 channels
+  const int start = a.cu_seqlens[s];
+  const int L = a.cu_seqlens[s + 1] - start;
+  T* cs = reinterpret_cast<T*>(a.conv.state_ptrs[s]);
+  const T* x = static_cast<const T*>(a.conv.x);
+  const int64_t C = a.conv.channels;
+  const int ng = (2 + group) * D / kConvVec;
+  for (int e = tid; e < ng; e += kThreads) {
+    const int c8 = e * kConvVec;  // position in [q of h | k of h | v of the group]
+    const int ch = c8 < D ? h * D + c8
+                 : c8 < 2 * D ? a.r.hk * D + h * D + (c8 - D)
+                              : 2 * a.r.hk * D + h * group * D + (c8 - 2 * D);
+    // New row i is row L + i of z; in increasing i an old state row is always read before
+    // it is overwritten (L >= 1), so rows are copied one at a time.
+#pragma unroll
+    for (int i = 0; i < K - 1; ++i) {
+      const int r = L + i;
+      const T* src = r < K - 1 ? cs + static_cast<int64_t>(r) * C + ch
+                               : x + static_cast<int64_t>(start + r - (K - 1)) * a.conv.x_stride + ch;
+      T* dst = cs + static_cast<int64_t>(i) * C + ch;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) reinterpret_cast<uint4*>(dst)[q] = reinterpret_cast<const uint4*>(src)[q];
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void commit_conv_rows(const PrefillArgs& a, int h, int group, int s, int tid) {
+  if (a.conv.bf16) {
+    switch (a.conv.width) {
+      case 2: commit_conv_rows_k<uint16_t, 2, D>(a, h, group, s, tid); break;
+      case 3: commit_conv_rows_k<uint16_t, 3, D>(a, h, group, s, tid); break;
+      default: commit_conv_rows_k<uint16_t, 4, D>(a, h, group, s, tid); break;
+    }
+  } else {
+    switch (a.conv.width) {
+      case 2: commit_conv_rows_k<float, 2, D>(a, h, group, s, tid); break;
+      case 3: commit_conv_rows_k<float, 3, D>(a, h, group, s, tid); break;
+      default: commit_conv_rows_k<float, 4, D>(a, h, group, s, tid); break;
+    }
+  }
+}
+
 // LDS of the intra-chunk kernel, in floats. K^ and Q^ live only until K K^T and Q K^T are
 // in registers; then G and QK take K^'s place and A and T take Q^'s, so the peak is two
 // areas, each the largest of K^ as fp32 rows, K^ as bf16 hi and lo planes and two C x C
@@ -744,6 +795,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     }
     __syncthreads();
   }
+  if (fused && ent.w == 0) commit_conv_rows<D>(a, h, group, ent.x, tid);
 }
 
 // ------------------------------------------------------------------------ inter-chunk
