@@ -89,14 +89,14 @@ class DecodeRig:
         import torch
 
         import gated_delta_rule_conv_amd as gdn
-        from gen.inputs import CONFIGS, ST_PERM, make_decode_pool_torch, rng_for
+        from gen.inputs import DECODE_30_LAYERS, ST_PERM, WORKLOADS, make_decode_pool_torch, rng_for
 
-        sh = CONFIGS[3].shape
+        sh = WORKLOADS[DECODE_30_LAYERS].shape
         self.m, self.layers, self.sh = m, layers, sh
         self.dims = gdn.make_dims(sh.num_k_heads, sh.num_v_heads, sh.head_dim, conv_width=sh.conv_width,
                                   chunk_size=sh.chunk, in_dtype=gdn.GDN_BF16)
-        self.states, self.conv_states, self.conv_w = make_decode_pool_torch(3, pool, layers, device)
-        slots = rng_for(3, ST_PERM).permutation(pool)[:m].astype(np.int32)
+        self.states, self.conv_states, self.conv_w = make_decode_pool_torch(DECODE_30_LAYERS, pool, layers, device)
+        slots = rng_for(DECODE_30_LAYERS, ST_PERM).permutation(pool)[:m].astype(np.int32)
         idx = torch.tensor(slots, dtype=torch.int32, device=device)
         self.sptr = torch.empty((layers, m), dtype=torch.int64, device=device)
         self.cptr = torch.empty((layers, m), dtype=torch.int64, device=device)
@@ -165,14 +165,14 @@ class DecodeRig:
 
 
 class PrefillRig:
-    def __init__(self, cfg: int = 1, device="cuda", shape=None, form: int = 0, fused: bool = False):
+    def __init__(self, wid: int, device="cuda", shape=None, form: int = 0, fused: bool = False):
         import numpy as np
         import torch
 
         import gated_delta_rule_conv_amd as gdn
         from gen import make_prefill
 
-        inp = make_prefill(cfg, shape=shape)
+        inp = make_prefill(wid, shape=shape)
         sh = inp["shape"]
         self.sh = sh
         self.lens = list(inp["lens"])
@@ -232,10 +232,10 @@ def cpu_baseline(seconds: float) -> dict:
         from threadpoolctl import threadpool_limits
     except Exception:  # pragma: no cover
         threadpool_limits = None
-    from gen import make_decode_pool, make_decode_step
+    from gen import DECODE_30_LAYERS, make_decode_pool, make_decode_step
     from oracle import decode_layer
 
-    pool = make_decode_pool(3, pool=4)
+    pool = make_decode_pool(DECODE_30_LAYERS, pool=4)
     sh = pool["shape"]
     done = 0
     t0 = time.perf_counter()
@@ -243,7 +243,7 @@ def cpu_baseline(seconds: float) -> dict:
     try:
         step = 0
         while time.perf_counter() - t0 < seconds:
-            inp = make_decode_step(3, step, 4)
+            inp = make_decode_step(DECODE_30_LAYERS, step, 4)
             decode_layer(inp["x"], pool["conv_w"], pool["conv_state"], pool["S"], inp["g"], inp["beta"],
                          sh.num_k_heads, sh.num_v_heads, sh.head_dim, in_dtype="bf16")
             done += 4
@@ -267,15 +267,15 @@ def _oracle_worker(args):
         ctx = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
         ctx = None
-    from gen import make_decode_pool, make_decode_step
+    from gen import DECODE_30_LAYERS, make_decode_pool, make_decode_step
     from oracle import decode_layer
 
-    pool = make_decode_pool(3, pool=4)
+    pool = make_decode_pool(DECODE_30_LAYERS, pool=4)
     sh = pool["shape"]
     done, step = 0, seed * 1000
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
-        inp = make_decode_step(3, step, 4)
+        inp = make_decode_step(DECODE_30_LAYERS, step, 4)
         decode_layer(inp["x"], pool["conv_w"], pool["conv_state"], pool["S"], inp["g"], inp["beta"],
                      sh.num_k_heads, sh.num_v_heads, sh.head_dim, in_dtype="bf16")
         done += 4
@@ -520,7 +520,7 @@ def main() -> int:
     prefill = None
     if not args.no_prefill:
         prefill = {}
-        from gen.inputs import LayerShape
+        from gen.inputs import PREFILL_L4096, RAGGED_T15717, LayerShape
 
         # the last two: one GPU's share of an 8-way head split of the same layer (2 q/k
         # heads, 4 v-heads), as the library runs it (chunk-parallel form) and forced to
@@ -528,14 +528,15 @@ def main() -> int:
         share = LayerShape(2, 4, 128, conv_width=4, chunk=64, in_dtype="bf16")
         # "_fused": the same prefill as one gdn_prefill_fused call (q/k conv inside the
         # intra-chunk kernel; bit-identical results)
-        runs = [(1, "L4096", None, 0, False), (1, "L4096_fused", None, 0, True),
-                (4, "ragged8_T15717", None, 0, False), (4, "ragged8_T15717_fused", None, 0, True),
-                (1, "L4096_hk2_hv4", share, 0, False), (1, "L4096_hk2_hv4_fused", share, 0, True),
-                (1, "L4096_hk2_hv4_whole_sequence", share, 1, False)]
-        for cfg, name, shape, form, fused in runs:
-            if cfg == 4 and args.no_ragged:
+        L4096, RAGGED = PREFILL_L4096, RAGGED_T15717
+        runs = [(L4096, "L4096", None, 0, False), (L4096, "L4096_fused", None, 0, True),
+                (RAGGED, "ragged8_T15717", None, 0, False), (RAGGED, "ragged8_T15717_fused", None, 0, True),
+                (L4096, "L4096_hk2_hv4", share, 0, False), (L4096, "L4096_hk2_hv4_fused", share, 0, True),
+                (L4096, "L4096_hk2_hv4_whole_sequence", share, 1, False)]
+        for wid, name, shape, form, fused in runs:
+            if wid == RAGGED and args.no_ragged:
                 continue
-            pre = PrefillRig(cfg, shape=shape, form=form, fused=fused)
+            pre = PrefillRig(wid, shape=shape, form=form, fused=fused)
             for _ in range(W):
                 pre.step()
             torch.cuda.synchronize()

@@ -8,7 +8,12 @@ bits without sharing any computation.
 """
 
 from .inputs import (  # noqa: F401
-    CONFIGS,
+    DECODE_30_LAYERS,
+    DECODE_M16_POOL64,
+    PREFILL_L4096,
+    RAGGED_T15717,
+    TINY_FP32,
+    WORKLOADS,
     LayerShape,
     bf16_bits_from_f32,
     make_decode_pool,

@@ -13,14 +13,14 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 
-from gen import make_prefill  # noqa: E402
+from gen import TINY_FP32, make_prefill  # noqa: E402
 from oracle import prefill_layer  # noqa: E402
 
 TOKENS = [0, 1, 15, 16, 17, 40, 63]
 
 
 def compute():
-    inp = make_prefill(0)
+    inp = make_prefill(TINY_FP32)
     sh = inp["shape"]
     out = prefill_layer(inp["x"], inp["conv_w"], inp["cu_seqlens"], inp["conv_state"], inp["S0"], inp["g"],
                         inp["beta"], sh.num_k_heads, sh.num_v_heads, sh.head_dim, in_dtype="f32")

@@ -9,7 +9,7 @@ update in the decode branch.)
 import numpy as np
 import pytest
 
-from gen import make_decode_pool, make_decode_step, make_prefill
+from gen import DECODE_M16_POOL64, PREFILL_L4096, TINY_FP32, make_decode_pool, make_decode_step, make_prefill
 from gen.inputs import LayerShape
 from oracle import causal_conv, storage_to_f64
 from tests.gpu_helpers import announce, storage_of, to_dev
@@ -81,7 +81,7 @@ CASES = [
 def test_conv_prefill_matches_oracle(in_dtype, K, lens, bias, act):
     announce(f"conv prefill {in_dtype} K={K} lens={lens} bias={bias} act={act}")
     shape = LayerShape(2, 4, 32, conv_width=K, chunk=16, in_dtype=in_dtype)
-    inp = make_prefill(0, lens=lens, shape=shape, conv_state_std=1.0, with_bias=bias)
+    inp = make_prefill(TINY_FP32, lens=lens, shape=shape, conv_state_std=1.0, with_bias=bias)
     y_ref, cs_ref = _oracle_conv(inp, act)
     y, cs = _run_prefill_conv(inp, act, x_pad=8 if in_dtype == "f32" else 64, shuffle=True)
     np.testing.assert_allclose(y, y_ref, rtol=1e-5, atol=1e-5)
@@ -100,7 +100,7 @@ def test_conv_prefill_matches_oracle(in_dtype, K, lens, bias, act):
 def test_conv_prefill_full_size_4096():
     """The 4096-token, 8192-channel bf16 prefill shape, launched as the benchmark does."""
     announce("conv prefill L=4096 C=8192 bf16")
-    inp = make_prefill(1)
+    inp = make_prefill(PREFILL_L4096)
     y_ref, _ = _oracle_conv(inp, "none")
     y, cs = _run_prefill_conv(inp, "none")
     np.testing.assert_allclose(y, y_ref, rtol=1e-5, atol=1e-5)
@@ -116,8 +116,8 @@ def test_conv_decode_matches_oracle_and_skips_inactive(in_dtype):
 
     announce(f"conv decode {in_dtype}")
     shape = LayerShape(16, 32, 128, in_dtype=in_dtype)
-    pool_np = make_decode_pool(2, pool=12, shape=shape)
-    step = make_decode_step(2, 0, 6, shape=shape)
+    pool_np = make_decode_pool(DECODE_M16_POOL64, pool=12, shape=shape)
+    step = make_decode_step(DECODE_M16_POOL64, 0, 6, shape=shape)
     dims = _dims(shape)
     pool = gdn.SlotPool(dims, 12, conv_state=to_dev(pool_np["conv_state"], in_dtype))
     slots = [5, 0, 11, -1, 7, 3]  # -1: inactive slot (null pointer)

@@ -9,7 +9,7 @@ equal to the per-slot result; "qLLM", "What this is": fixed-size slot pool.)
 import numpy as np
 import pytest
 
-from gen import make_decode_pool, make_decode_step
+from gen import DECODE_M16_POOL64, make_decode_pool, make_decode_step
 from gen.inputs import LayerShape
 from oracle import decode_layer
 from tests.gpu_helpers import (TOL_BF16, TOL_F32, announce, bits_of, max_block_err_S, normwise_err,
@@ -29,12 +29,12 @@ def _dims(shape, act=0):
 class DecodeRig:
     """A slot pool on the device plus the oracle's copy of every slot."""
 
-    def __init__(self, cfg, shape, pool_slots, act=0):
+    def __init__(self, wid, shape, pool_slots, act=0):
         import gated_delta_rule_conv_amd as gdn
 
-        self.cfg, self.shape, self.act = cfg, shape, act
+        self.wid, self.shape, self.act = wid, shape, act
         self.dims = _dims(shape, act)
-        self.np = make_decode_pool(cfg, pool=pool_slots, shape=shape)
+        self.np = make_decode_pool(wid, pool=pool_slots, shape=shape)
         self.pool = gdn.SlotPool(self.dims, pool_slots, state=to_dev(self.np["S"], "f32"),
                                  conv_state=to_dev(self.np["conv_state"], shape.in_dtype))
         self.conv_w = to_dev(self.np["conv_w"], shape.in_dtype)
@@ -47,7 +47,7 @@ class DecodeRig:
         import gated_delta_rule_conv_amd as gdn
 
         m = len(slots)
-        inp = make_decode_step(self.cfg, step, m, shape=self.shape)
+        inp = make_decode_step(self.wid, step, m, shape=self.shape)
         sp, cp = self.pool.pointers(torch.tensor(slots, dtype=torch.int32, device="cuda"))
         x = to_dev(inp["x"], self.shape.in_dtype)
         y = torch.empty((m, self.shape.channels), dtype=torch.float32, device="cuda")
@@ -76,9 +76,9 @@ def test_decode_m16_pool64_64_steps_matches_oracle():
     bf16 inputs, fp32 state. Every step's o, the final states and conv states."""
     import torch
 
-    announce("decode cfg m=16 pool=64 steps=64")
+    announce("decode m=16 pool=64 steps=64")
     shape = LayerShape(16, 32, 128, in_dtype="bf16")
-    rig = DecodeRig(2, shape, 64)
+    rig = DecodeRig(DECODE_M16_POOL64, shape, 64)
     slots = [int(s) for s in rig.np["perm"][:16]]
     worst_o = 0.0
     for step in range(64):
@@ -105,7 +105,7 @@ def test_decode_head_dims_match_oracle(d, in_dtype, hk, hv):
     announce(f"decode d={d} {in_dtype} hk={hk} hv={hv}")
     shape = LayerShape(hk, hv, d, in_dtype=in_dtype)
     for act in (0, 1):
-        rig = DecodeRig(2, shape, 9, act=act)
+        rig = DecodeRig(DECODE_M16_POOL64, shape, 9, act=act)
         slots = [3, 8, 0, 5]
         for step in range(5):
             inp, o = rig.gpu_step(step, slots)
@@ -129,9 +129,9 @@ def test_batched_is_bit_exact_against_m1_and_routing():
     announce("decode bit-exact m=16 vs m=1 vs shuffled routing")
     shape = LayerShape(16, 32, 128, in_dtype="bf16")
     dims = _dims(shape)
-    base = make_decode_pool(2, pool=40, shape=shape)
+    base = make_decode_pool(DECODE_M16_POOL64, pool=40, shape=shape)
     slots = [int(s) for s in base["perm"][:16]]
-    inp = make_decode_step(2, 3, 16, shape=shape)
+    inp = make_decode_step(DECODE_M16_POOL64, 3, 16, shape=shape)
     conv_w = to_dev(base["conv_w"], "bf16")
     x = to_dev(inp["x"], "bf16")
     g = to_dev(inp["g"], "f32")
@@ -183,8 +183,8 @@ def test_inactive_slot_pointers_are_skipped_and_run_twice_is_deterministic():
     announce("decode inactive slots + determinism")
     shape = LayerShape(16, 32, 128, in_dtype="bf16")
     dims = _dims(shape)
-    base = make_decode_pool(2, pool=8, shape=shape)
-    inp = make_decode_step(2, 9, 5, shape=shape)
+    base = make_decode_pool(DECODE_M16_POOL64, pool=8, shape=shape)
+    inp = make_decode_step(DECODE_M16_POOL64, 9, 5, shape=shape)
     slots = [2, -1, 6, 99, 0]  # -1 and 99 fall outside the pool -> null pointers
     outs = []
     for _ in range(2):
@@ -213,9 +213,9 @@ def test_large_batch_unit_size_is_bit_exact_against_m1():
     announce("decode bit-exact m=40 (one-pass units) vs m=1 (two-pass units)")
     shape = LayerShape(16, 32, 128, in_dtype="bf16")
     dims = _dims(shape)
-    base = make_decode_pool(2, pool=48, shape=shape)
+    base = make_decode_pool(DECODE_M16_POOL64, pool=48, shape=shape)
     slots = [int(s) for s in base["perm"][:40]]
-    inp = make_decode_step(2, 5, 40, shape=shape)
+    inp = make_decode_step(DECODE_M16_POOL64, 5, 40, shape=shape)
     conv_w = to_dev(base["conv_w"], "bf16")
     x, g, beta = to_dev(inp["x"], "bf16"), to_dev(inp["g"], "f32"), to_dev(inp["beta"], "f32")
 
@@ -262,10 +262,10 @@ def test_graph_replay_matches_eager_every_replay():
     shape = LayerShape(16, 32, 128, in_dtype="bf16")
     dims = _dims(shape)
     layers, pool_slots, m = 2, 24, 20
-    base = [make_decode_pool(2, pool=pool_slots, shape=shape) for _ in range(layers)]
+    base = [make_decode_pool(DECODE_M16_POOL64, pool=pool_slots, shape=shape) for _ in range(layers)]
     slots = [int(s) for s in base[0]["perm"][:m]]
     idx = torch.tensor(slots, dtype=torch.int32, device="cuda")
-    inp = make_decode_step(2, 7, m, shape=shape)
+    inp = make_decode_step(DECODE_M16_POOL64, 7, m, shape=shape)
     x, g, beta = to_dev(inp["x"], "bf16"), to_dev(inp["g"], "f32"), to_dev(inp["beta"], "f32")
 
     def rig():

@@ -8,7 +8,7 @@ and two layers rerun through gdn_decode_fused for the same bits."""
 import numpy as np
 import pytest
 
-from gen.inputs import CONFIGS, ST_PERM, make_decode_pool_torch, rng_for
+from gen.inputs import DECODE_30_LAYERS, ST_PERM, WORKLOADS, make_decode_pool_torch, rng_for
 from oracle import decode_layer
 from tests.gpu_helpers import TOL_BF16, announce, bits_of, max_block_err_S, normwise_err, storage_of
 
@@ -25,11 +25,11 @@ def test_decode_step_full_size_30_layers_sampled():
     import gated_delta_rule_conv_amd as gdn
 
     announce(f"decode step full size: {LAYERS} layers, pool {POOL}, m={M}")
-    sh = CONFIGS[3].shape
+    sh = WORKLOADS[DECODE_30_LAYERS].shape
     Hk, Hv, d, C = sh.num_k_heads, sh.num_v_heads, sh.head_dim, sh.channels
     dims = gdn.make_dims(Hk, Hv, d, conv_width=sh.conv_width, chunk_size=sh.chunk, in_dtype=gdn.GDN_BF16)
-    states, conv_states, conv_w = make_decode_pool_torch(3, POOL, LAYERS, "cuda")
-    slots = rng_for(3, ST_PERM).permutation(POOL)[:M].astype(np.int32)
+    states, conv_states, conv_w = make_decode_pool_torch(DECODE_30_LAYERS, POOL, LAYERS, "cuda")
+    slots = rng_for(DECODE_30_LAYERS, ST_PERM).permutation(POOL)[:M].astype(np.int32)
     idle = [s for s in range(POOL) if s not in set(slots.tolist())][:3]
     idx = torch.tensor(slots, dtype=torch.int32, device="cuda")
     sptr = torch.empty((LAYERS, M), dtype=torch.int64, device="cuda")

@@ -10,7 +10,7 @@ decode over a device u64[m] pointer array.)
 import numpy as np
 import pytest
 
-from gen import make_decode_pool, make_decode_step
+from gen import DECODE_30_LAYERS, make_decode_pool, make_decode_step
 from gen.inputs import LayerShape
 from oracle import decode_layer
 from tests.gpu_helpers import TOL_BF16, TOL_F32, announce, bits_of, max_block_err_S, normwise_err, to_dev
@@ -58,7 +58,7 @@ def test_fused_equals_conv_then_decode_bit_for_bit(hk, hv, d, dt, K, act, bias, 
     shape = LayerShape(hk, hv, d, conv_width=K, in_dtype=dt)
     dims = _dims(shape, act)
     pool_slots = m + 5
-    base = make_decode_pool(3, pool=pool_slots, shape=shape, with_bias=bias)
+    base = make_decode_pool(DECODE_30_LAYERS, pool=pool_slots, shape=shape, with_bias=bias)
     slots = [int(s) for s in base["perm"][:m]]
     idx = torch.tensor(slots, dtype=torch.int32, device="cuda")
     conv_w = to_dev(base["conv_w"], dt)
@@ -70,7 +70,7 @@ def test_fused_equals_conv_then_decode_bit_for_bit(hk, hv, d, dt, K, act, bias, 
     ref_S = base["S"].astype(np.float64)[slots]
     ref_cs = base["conv_state"][slots]
     for step in range(3):
-        inp = make_decode_step(3, step, m, shape=shape)
+        inp = make_decode_step(DECODE_30_LAYERS, step, m, shape=shape)
         x, g, beta = to_dev(inp["x"], dt), to_dev(inp["g"], "f32"), to_dev(inp["beta"], "f32")
         y = torch.empty((m, shape.channels), dtype=torch.float32, device="cuda")
         oa = torch.empty((m, hv, d), dtype=torch.float32, device="cuda")
@@ -111,8 +111,8 @@ def test_fused_inactive_slots_are_untouched():
     announce("decode_fused inactive slots")
     shape = LayerShape(16, 32, 128, in_dtype="bf16")
     dims = _dims(shape)
-    base = make_decode_pool(3, pool=10, shape=shape)
-    inp = make_decode_step(3, 4, 6, shape=shape)
+    base = make_decode_pool(DECODE_30_LAYERS, pool=10, shape=shape)
+    inp = make_decode_step(DECODE_30_LAYERS, 4, 6, shape=shape)
     slots = [3, 8, 1, 5, 0, 9]
     x, g, beta = to_dev(inp["x"], "bf16"), to_dev(inp["g"], "f32"), to_dev(inp["beta"], "f32")
     conv_w = to_dev(base["conv_w"], "bf16")
@@ -156,9 +156,9 @@ def test_fused_graph_replay_matches_eager():
     shape = LayerShape(16, 32, 128, in_dtype="bf16")
     dims = _dims(shape)
     layers, pool_slots, m = 2, 40, 36
-    base = [make_decode_pool(3, pool=pool_slots, shape=shape) for _ in range(layers)]
+    base = [make_decode_pool(DECODE_30_LAYERS, pool=pool_slots, shape=shape) for _ in range(layers)]
     idx = torch.tensor([int(s) for s in base[0]["perm"][:m]], dtype=torch.int32, device="cuda")
-    inp = make_decode_step(3, 11, m, shape=shape)
+    inp = make_decode_step(DECODE_30_LAYERS, 11, m, shape=shape)
     x, g, beta = to_dev(inp["x"], "bf16"), to_dev(inp["g"], "f32"), to_dev(inp["beta"], "f32")
 
     def rig():

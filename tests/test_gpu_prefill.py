@@ -9,7 +9,7 @@ gated delta rule on (q, k, v, g, beta, state), temporal state updated; aprender 
 import numpy as np
 import pytest
 
-from gen import make_prefill
+from gen import PREFILL_L4096, RAGGED_T15717, TINY_FP32, make_prefill
 from gen.inputs import LayerShape
 from oracle import prefill_layer
 from tests.gpu_helpers import (TOL_BF16, TOL_F32, announce, bits_of, max_block_err_o, max_block_err_S, storage_of,
@@ -84,7 +84,7 @@ def _check(o, S, ref, cu, tol, heads=None, label=""):
 def test_tiny_fp32_chunk16(act):
     """1 sequence, L = 64, 2 heads, d = 32, chunk 16, fp32 inputs, zero states: 1e-5."""
     announce(f"prefill tiny fp32 act={act}")
-    inp = make_prefill(0)
+    inp = make_prefill(TINY_FP32)
     run = PrefillRun(inp, act=act)
     o, S = run.run()
     ref = _oracle(inp, "silu" if act else "none")
@@ -100,7 +100,7 @@ def test_ragged_small_shapes(d, chunk, mma, in_dtype):
     announce(f"prefill ragged d={d} chunk={chunk} mma={mma} {in_dtype}")
     shape = LayerShape(2, 4, d, conv_width=4, chunk=chunk, in_dtype=in_dtype)
     lens = (1, 17, 64, 0, 33, 100, 2)
-    inp = make_prefill(4, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
+    inp = make_prefill(RAGGED_T15717, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
     o, S = PrefillRun(inp, mma=mma).run()
     ref = _oracle(inp)
     tol = TOL_F32 if in_dtype == "f32" else TOL_BF16
@@ -113,7 +113,7 @@ def test_prefill_L4096_full_size_sampled_heads():
     """One 4096-token sequence, 16/32 heads, d = 128, bf16, chunk 64 (the benchmark's
     launch); the oracle runs a sample of v-heads over the whole sequence."""
     announce("prefill L=4096 full size")
-    inp = make_prefill(1)
+    inp = make_prefill(PREFILL_L4096)
     o, S = PrefillRun(inp).run()
     heads = [0, 1, 17, 31]
     ref = _oracle(inp, v_heads=heads)
@@ -125,7 +125,7 @@ def test_ragged_T15717_full_size_sampled_heads():
     """8 packed sequences {1,17,64,300,1000,2048,4095,8192}, nonzero initial conv and
     recurrent states, bf16, chunk 64; oracle on sampled v-heads of every sequence."""
     announce("prefill ragged T=15717 full size")
-    inp = make_prefill(4)
+    inp = make_prefill(RAGGED_T15717)
     o, S = PrefillRun(inp).run()
     heads = [5, 30]
     ref = _oracle(inp, v_heads=heads)
@@ -139,7 +139,7 @@ def test_packed_equals_solo_bit_exact():
     announce("prefill packed vs solo bit-exact")
     shape = LayerShape(2, 4, 128, conv_width=4, chunk=64, in_dtype="bf16")
     lens = (5, 130, 64, 1, 77)
-    inp = make_prefill(4, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
+    inp = make_prefill(RAGGED_T15717, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
     o, S = PrefillRun(inp).run()
     cu = inp["cu_seqlens"]
     for s in (1, 4, 3):
@@ -160,7 +160,7 @@ def test_one_and_two_workgroups_per_cu_variants_bit_exact():
     sequence's o and state must agree bit for bit."""
     announce("prefill inter variants (prefetch vs two per CU) bit-exact")
     lens = (300, 130)
-    inp = make_prefill(1, lens=lens, s0_std=0.02, conv_state_std=1.0)
+    inp = make_prefill(PREFILL_L4096, lens=lens, s0_std=0.02, conv_state_std=1.0)
     o, S = PrefillRun(inp).run()
     solo = dict(inp, x=inp["x"][:300], cu_seqlens=np.array([0, 300], dtype=np.int32),
                 conv_state=inp["conv_state"][:1], S0=inp["S0"][:1], g=inp["g"][:300], beta=inp["beta"][:300],
@@ -181,7 +181,7 @@ def test_split_and_decode_continuation():
 
     announce("prefill split + decode continuation")
     shape = LayerShape(2, 4, 128, conv_width=4, chunk=64, in_dtype="bf16")
-    inp = make_prefill(4, lens=(150,), shape=shape, s0_std=0.05, conv_state_std=1.0)
+    inp = make_prefill(RAGGED_T15717, lens=(150,), shape=shape, s0_std=0.05, conv_state_std=1.0)
     ref = _oracle(inp)
     L1 = 70
     first = dict(inp, x=inp["x"][:L1], cu_seqlens=np.array([0, L1], dtype=np.int32), g=inp["g"][:L1],
@@ -210,7 +210,7 @@ def test_strong_decay_stays_finite():
     nothing overflows; the state forgets its past within a token."""
     announce("prefill strong decay")
     shape = LayerShape(2, 4, 64, conv_width=4, chunk=64, in_dtype="bf16")
-    inp = make_prefill(4, lens=(130, 7), shape=shape, s0_std=0.05, conv_state_std=1.0)
+    inp = make_prefill(RAGGED_T15717, lens=(130, 7), shape=shape, s0_std=0.05, conv_state_std=1.0)
     g = np.full_like(inp["g"], -50.0)
     o, S = PrefillRun(inp, g=g).run()
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
@@ -221,7 +221,7 @@ def test_strong_decay_stays_finite():
 def test_run_twice_is_deterministic():
     announce("prefill determinism")
     shape = LayerShape(2, 4, 128, conv_width=4, chunk=64, in_dtype="bf16")
-    inp = make_prefill(4, lens=(3, 200, 64), shape=shape, s0_std=0.05, conv_state_std=1.0)
+    inp = make_prefill(RAGGED_T15717, lens=(3, 200, 64), shape=shape, s0_std=0.05, conv_state_std=1.0)
     a = PrefillRun(inp).run()
     b = PrefillRun(inp).run()
     for x, y in zip(a, b):
@@ -241,7 +241,7 @@ def test_many_short_sequences():
     rng = np.random.default_rng(77)
     lens = tuple(int(v) for v in rng.integers(0, 6, size=1100))
     shape = LayerShape(2, 2, 32, conv_width=4, chunk=16, in_dtype="f32")
-    inp = make_prefill(0, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
+    inp = make_prefill(TINY_FP32, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
     run = PrefillRun(inp)
     o, S = run.run()
     ref = _oracle(inp)

@@ -11,7 +11,7 @@ give the per-slot result.)
 import numpy as np
 import pytest
 
-from gen import make_prefill
+from gen import PREFILL_L4096, RAGGED_T15717, make_prefill
 from gen.inputs import LayerShape
 from oracle import prefill_layer
 from tests.gpu_helpers import TOL_BF16, TOL_F32, announce, bits_of, max_block_err_o, max_block_err_S, to_dev
@@ -82,7 +82,7 @@ def test_fused_equals_conv_then_prefill_bit_for_bit(hk, hv, d, dt, K, act, bias,
     announce(f"prefill_fused vs conv+prefill hk={hk} hv={hv} d={d} {dt} K={K} act={act} bias={bias} C={chunk} "
              f"lens={lens} form={form}")
     shape = LayerShape(hk, hv, d, conv_width=K, chunk=chunk, in_dtype=dt)
-    inp = make_prefill(4, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0, with_bias=bias)
+    inp = make_prefill(RAGGED_T15717, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0, with_bias=bias)
     (oa, Sa, ca), (ob, Sb, cb) = _run_both(inp, act, form)
     np.testing.assert_array_equal(oa.view(np.int32), ob.view(np.int32))
     np.testing.assert_array_equal(Sa.view(np.int32), Sb.view(np.int32))
@@ -101,7 +101,7 @@ def test_fused_full_size_L4096_bit_for_bit():
     """The benchmark's launch (one 4096-token sequence, 16/32 heads, d = 128, bf16, chunk
     64): fused and two-call results agree bit for bit."""
     announce("prefill_fused vs conv+prefill L=4096")
-    inp = make_prefill(1)
+    inp = make_prefill(PREFILL_L4096)
     (oa, Sa, ca), (ob, Sb, cb) = _run_both(inp, 0, 0)
     np.testing.assert_array_equal(oa.view(np.int32), ob.view(np.int32))
     np.testing.assert_array_equal(Sa.view(np.int32), Sb.view(np.int32))

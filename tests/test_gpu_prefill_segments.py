@@ -13,7 +13,7 @@ run of chunks.)
 import numpy as np
 import pytest
 
-from gen import make_prefill
+from gen import PREFILL_L4096, RAGGED_T15717, make_prefill
 from gen.inputs import LayerShape
 from tests.gpu_helpers import TOL_BF16, TOL_F32, announce
 from tests.test_gpu_prefill import PrefillRun, _check, _oracle
@@ -26,7 +26,7 @@ def test_long_sequence_few_heads_matches_oracle():
     the 16/32-head layer), d = 128, bf16, chunk 64: 64 chunks in 22 segments of 3."""
     announce("prefill chunk-parallel L=4096 hk=2 hv=4 d=128 bf16")
     shape = LayerShape(2, 4, 128, conv_width=4, chunk=64, in_dtype="bf16")
-    inp = make_prefill(1, lens=(4096,), shape=shape, s0_std=0.02, conv_state_std=1.0)
+    inp = make_prefill(PREFILL_L4096, lens=(4096,), shape=shape, s0_std=0.02, conv_state_std=1.0)
     o, S = PrefillRun(inp).run()
     heads = [0, 3]
     ref = _oracle(inp, v_heads=heads)
@@ -47,7 +47,7 @@ def test_ragged_segments_match_oracle(d, chunk, mma, in_dtype, lens, form):
     counts) and forced to whole sequences, both against the oracle."""
     announce(f"prefill form={form} d={d} chunk={chunk} mma={mma} {in_dtype} lens={lens}")
     shape = LayerShape(2, 4, d, conv_width=4, chunk=chunk, in_dtype=in_dtype)
-    inp = make_prefill(4, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
+    inp = make_prefill(RAGGED_T15717, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
     o, S = PrefillRun(inp, mma=mma, form=form).run()
     ref = _oracle(inp)
     tol = TOL_F32 if in_dtype == "f32" else TOL_BF16
@@ -63,7 +63,7 @@ def test_segments_forced_at_full_head_count():
     import gated_delta_rule_conv_amd as gdn
 
     announce("prefill segments forced, 16/32 heads")
-    inp = make_prefill(1, lens=(1000, 2100), s0_std=0.02, conv_state_std=1.0)
+    inp = make_prefill(PREFILL_L4096, lens=(1000, 2100), s0_std=0.02, conv_state_std=1.0)
     o, S = PrefillRun(inp, form=gdn.GDN_PREFILL_SEGMENTS).run()
     heads = [2, 29]
     ref = _oracle(inp, v_heads=heads)
@@ -76,7 +76,7 @@ def test_segments_depend_on_the_sequence_only():
     announce("prefill chunk-parallel packed vs solo bit-exact")
     shape = LayerShape(2, 4, 128, conv_width=4, chunk=64, in_dtype="bf16")
     lens = (900, 40, 1500)
-    inp = make_prefill(4, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
+    inp = make_prefill(RAGGED_T15717, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
     o, S = PrefillRun(inp).run()
     cu = inp["cu_seqlens"]
     for s in (0, 2):
@@ -103,7 +103,7 @@ def test_slow_decay_few_heads_L4096(form):
     form (AUTO = segments here)."""
     announce(f"prefill slow decay L=4096 hk=2 hv=4 form={form}")
     shape = LayerShape(2, 4, 128, conv_width=4, chunk=64, in_dtype="bf16")
-    inp = make_prefill(1, lens=(4096,), shape=shape, s0_std=0.02, conv_state_std=1.0)
+    inp = make_prefill(PREFILL_L4096, lens=(4096,), shape=shape, s0_std=0.02, conv_state_std=1.0)
     g = (inp["g"] * SLOW).astype(np.float32)
     o, S = PrefillRun(inp, g=g, form=form).run()
     heads = [1, 2]
@@ -121,7 +121,7 @@ def test_slow_decay_few_heads_L4096(form):
 def test_slow_decay_ragged(d, chunk, mma, in_dtype, lens, form):
     announce(f"prefill slow decay form={form} d={d} chunk={chunk} mma={mma} {in_dtype} lens={lens}")
     shape = LayerShape(2, 4, d, conv_width=4, chunk=chunk, in_dtype=in_dtype)
-    inp = make_prefill(4, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
+    inp = make_prefill(RAGGED_T15717, lens=lens, shape=shape, s0_std=0.05, conv_state_std=1.0)
     g = (inp["g"] * SLOW).astype(np.float32)
     o, S = PrefillRun(inp, mma=mma, g=g, form=form).run()
     ref = _oracle(inp, g=g)
@@ -134,7 +134,7 @@ def test_slow_decay_full_heads_L4096(form):
     """The 16/32-head L = 4096 layer with slowly decaying state, whole sequences (AUTO)
     and segments forced."""
     announce(f"prefill slow decay L=4096 16/32 heads form={form}")
-    inp = make_prefill(1)
+    inp = make_prefill(PREFILL_L4096)
     g = (inp["g"] * SLOW).astype(np.float32)
     o, S = PrefillRun(inp, g=g, form=form).run()
     heads = [7, 24]

@@ -9,7 +9,7 @@ slot must continue exactly like its source: these checks are bit-exact.
 import numpy as np
 import pytest
 
-from gen import make_decode_pool, make_decode_step, make_prefill
+from gen import DECODE_M16_POOL64, PREFILL_L4096, RAGGED_T15717, make_decode_pool, make_decode_step, make_prefill
 from gen.inputs import LayerShape
 from tests.gpu_helpers import announce, bits_of, to_dev
 
@@ -32,7 +32,7 @@ def test_fork_copies_state_and_conv_state_bit_exact():
     announce("slot copy: fork 3 slots, bf16, d=128")
     shape = LayerShape(16, 32, 128, in_dtype="bf16")
     dims = _dims(shape)
-    base = make_decode_pool(2, pool=12, shape=shape)
+    base = make_decode_pool(DECODE_M16_POOL64, pool=12, shape=shape)
     pool = gdn.SlotPool(dims, 12, state=to_dev(base["S"], "f32"), conv_state=to_dev(base["conv_state"], "bf16"))
     src, dst = [2, 2, 5], [7, 9, 0]
     pool.copy_slots(torch.tensor(src, dtype=torch.int32, device="cuda"),
@@ -65,7 +65,7 @@ def test_forked_slot_decodes_like_its_source():
     announce("slot copy: fork then decode 4 steps")
     shape = LayerShape(16, 32, 128, in_dtype="bf16")
     dims = _dims(shape)
-    base = make_decode_pool(2, pool=6, shape=shape)
+    base = make_decode_pool(DECODE_M16_POOL64, pool=6, shape=shape)
     pool = gdn.SlotPool(dims, 6, state=to_dev(base["S"], "f32"), conv_state=to_dev(base["conv_state"], "bf16"))
     pool.copy_slots(torch.tensor([1], dtype=torch.int32, device="cuda"),
                     torch.tensor([4], dtype=torch.int32, device="cuda"))
@@ -73,7 +73,7 @@ def test_forked_slot_decodes_like_its_source():
     sp, cp = pool.pointers(idx)
     conv_w = to_dev(base["conv_w"], "bf16")
     for step in range(4):
-        inp = make_decode_step(2, 20 + step, 1, shape=shape)
+        inp = make_decode_step(DECODE_M16_POOL64, 20 + step, 1, shape=shape)
         x = to_dev(inp["x"], "bf16").repeat(2, 1)  # the same token for both slots
         g = to_dev(inp["g"], "f32").repeat(2, 1)
         beta = to_dev(inp["beta"], "f32").repeat(2, 1)
@@ -99,8 +99,8 @@ def test_prefix_reuse_equals_one_long_prefill():
     shape = LayerShape(4, 8, 128, conv_width=4, chunk=64, in_dtype="bf16")
     dims = _dims(shape)
     P, Lc = 128, 100
-    full = [make_prefill(1, lens=(P + Lc,), shape=shape, s0_std=0.02, conv_state_std=1.0) for _ in range(1)][0]
-    other = make_prefill(4, lens=(P + Lc,), shape=shape, s0_std=0.02, conv_state_std=1.0)
+    full = [make_prefill(PREFILL_L4096, lens=(P + Lc,), shape=shape, s0_std=0.02, conv_state_std=1.0) for _ in range(1)][0]
+    other = make_prefill(RAGGED_T15717, lens=(P + Lc,), shape=shape, s0_std=0.02, conv_state_std=1.0)
     x_a = full["x"]
     x_b = np.concatenate([full["x"][:P], other["x"][P:]], axis=0)  # same prefix, another continuation
     g_a, b_a = full["g"], full["beta"]

@@ -9,7 +9,7 @@ per-slot result.)
 import numpy as np
 import pytest
 
-from gen import make_prefill
+from gen import TINY_FP32, make_prefill
 from gen.inputs import LayerShape
 from oracle import decode_layer, gated_delta_chunked, gated_delta_recurrent, l2norm, prefill_layer
 
@@ -63,7 +63,7 @@ def test_strong_decay_stays_finite_and_forgets():
 
 def _layer_inputs(lens, Hk=1, Hv=2, d=8, in_dtype="f32"):
     shape = LayerShape(Hk, Hv, d, conv_width=4, chunk=16, in_dtype=in_dtype)
-    return make_prefill(0, lens=lens, shape=shape, s0_std=0.1, conv_state_std=1.0)
+    return make_prefill(TINY_FP32, lens=lens, shape=shape, s0_std=0.1, conv_state_std=1.0)
 
 
 def _run(inp, cu=None, **kw):
