@@ -106,3 +106,15 @@ def test_fused_full_size_L4096_bit_for_bit():
     np.testing.assert_array_equal(oa.view(np.int32), ob.view(np.int32))
     np.testing.assert_array_equal(Sa.view(np.int32), Sb.view(np.int32))
     np.testing.assert_array_equal(ca, cb)
+
+
+def test_fused_full_size_ragged_T15717_bit_for_bit():
+    """The benchmark's ragged launch (8 packed sequences of 1 .. 8192 tokens, T = 15717,
+    nonzero initial and conv states): fused and two-call results agree bit for bit, so the
+    fused path inherits the two-call path's full-size checks against the oracle."""
+    announce("prefill_fused vs conv+prefill ragged T=15717")
+    inp = make_prefill(RAGGED_T15717)
+    (oa, Sa, ca), (ob, Sb, cb) = _run_both(inp, 0, 0)
+    np.testing.assert_array_equal(oa.view(np.int32), ob.view(np.int32))
+    np.testing.assert_array_equal(Sa.view(np.int32), Sb.view(np.int32))
+    np.testing.assert_array_equal(ca, cb)
