@@ -16,7 +16,8 @@ Inputs are seeded synthetic data already resident in HBM when timing starts.
 
 `value` is the decode state bandwidth: 30 * m * 4 MiB (each slot-layer reads and writes
 its 2 MiB state once) over the graph-replayed decode step. Prefill is reported as
-tokens/s and as algorithmic TFLOP/s against the bf16 MFMA peak. `roofline` is for the
+tokens/s (eager calls, and the same calls replayed from a HIP graph) and as algorithmic
+TFLOP/s against the bf16 MFMA peak. `roofline` is for the
 dominant kernel (the decode kernel), whose average launch time is measured with HIP
 events around back-to-back launches on the stream it runs on. `ceilings` are this GPU's
 measured practical rates (a 4 GiB device copy, a bf16 8192^3 matmul), next to which the
@@ -213,6 +214,22 @@ class PrefillRig:
                 n = min(C, L - c0)
                 tot += 5 * 2 * n * n * d + 3 * 2 * n * d * d + (2.0 / 3.0) * n ** 3
         return tot * Hv
+
+    def capture(self):
+        """One prefill call (or the two calls) captured in a HIP graph."""
+        import torch
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step()
+        torch.cuda.synchronize()
+        return graph
 
     def step(self) -> None:
         import gated_delta_rule_conv_amd as gdn
@@ -547,9 +564,23 @@ def main() -> int:
             b.record()
             torch.cuda.synchronize()
             ms = a.elapsed_time(b) / K
+            # the same call(s) replayed from a HIP graph (the launches without host overhead)
+            graph = pre.capture()
+            for _ in range(W):
+                graph.replay()
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record()
+            for _ in range(K):
+                graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            gms = a.elapsed_time(b) / K
+            del graph
             fl = pre.flops()
             prefill[name] = {
                 "ms": round(ms, 4), "tokens": pre.T, "tokens_per_s": round(pre.T / (ms * 1e-3), 1),
+                "graph_ms": round(gms, 4), "graph_tokens_per_s": round(pre.T / (gms * 1e-3), 1),
                 "algorithmic_TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2),
                 "frac_of_bf16_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
                 "gflop": round(fl / 1e9, 3),
@@ -560,7 +591,7 @@ def main() -> int:
                                                  if shape is not None else "")}
             del pre
             torch.cuda.empty_cache()
-            log(f"prefill {name}: {ms:.3f} ms")
+            log(f"prefill {name}: {ms:.3f} ms (graph {gms:.3f} ms)")
 
     ceil = None
     if not args.no_ceilings:
