@@ -43,10 +43,18 @@ typedef __attribute__((address_space(1))) float gfloat;
 typedef __attribute__((address_space(1))) const float cgfloat;
 typedef __attribute__((address_space(4))) const uint64_t cu64;
 typedef __attribute__((address_space(4))) const float cfloat;
+typedef __attribute__((address_space(1))) uint16_t gu16;
 // (Generic -> global/constant pointer conversions are address-space casts, which C++
 // spells only as C-style casts.)
 
 constexpr int kDecodeWaves = 4;  // waves per workgroup
+
+// element `off` of o, in o's dtype: OB 0 fp32, 1 bf16, 2 as the o_bf16 flag says
+template <int OB>
+__device__ __forceinline__ void* o_row(const RecurArgs& a, int64_t off) {
+  const bool b16 = OB == 1 || (OB == 2 && a.o_bf16);
+  return b16 ? static_cast<void*>(static_cast<uint16_t*>(a.o) + off) : static_cast<void*>(static_cast<float*>(a.o) + off);
+}
 
 template <int D, int P>
 struct DecodeCfg {
@@ -61,10 +69,11 @@ struct DecodeCfg {
 // lane holds 16 columns of each), then for each of the P row passes the two row dots,
 // the delta-rule update of the rows and their outputs. Both decode kernels call this, so
 // the fused kernel's bits equal the separate conv + decode launches.
-template <int D, int P>
+// OB: how o is stored -- 0 fp32, 1 bf16 (rounded to nearest even), 2 as the o_bf16 flag says.
+template <int D, int P, int OB>
 __device__ __forceinline__ void decode_rows(const f32x4 (&s)[P][4], f32x4 (&kv)[4], f32x4 (&qv)[4], const float (&vr)[P],
-                                            float gval, float beta, float eps, float scale, gf32x4* S, gfloat* orow,
-                                            int row0, int c) {
+                                            float gval, float beta, float eps, float scale, gf32x4* S, void* orow,
+                                            bool o_bf16, int row0, int c) {
   using Cfg = DecodeCfg<D, P>;
   constexpr int LPR = Cfg::LPR, RPP = Cfg::RPP;
   // k^ and q^ at this lane's 16 columns, and k^ . q^
@@ -115,12 +124,18 @@ __device__ __forceinline__ void decode_rows(const f32x4 (&s)[P][4], f32x4 (&kv)[
       n.w = fmaf(ur, kv[e].w, alpha * s[p][e].w);
       __builtin_nontemporal_store(n, rowp + c + LPR * e);
     }
-    if (c == 0) orow[r] = fmaf(ur, kq, alpha * sq);
+    if (c == 0) {
+      const float ov = fmaf(ur, kq, alpha * sq);
+      if (OB == 1 || (OB == 2 && o_bf16))
+        ((gu16*)orow)[r] = f32_to_bf16_rne(ov);
+      else
+        ((gfloat*)orow)[r] = ov;
+    }
   }
 }
 
 
-template <int D, int P, bool SCHED_FENCE>
+template <int D, int P, bool SCHED_FENCE, int OB>
 __global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(RecurArgs a, int32_t total_units) {
   using Cfg = DecodeCfg<D, P>;
   constexpr int LPR = Cfg::LPR, RPP = Cfg::RPP, NPART = Cfg::NPART;
@@ -164,14 +179,17 @@ __global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(RecurArgs a
   const float beta = ((cfloat*)a.beta)[gi];
   if constexpr (SCHED_FENCE) __builtin_amdgcn_sched_barrier(0);
 
-  decode_rows<D, P>(s, kv, qv, vr, gval, beta, a.eps, a.scale, S, (gfloat*)(a.o + gi * D), row0, c);
+  decode_rows<D, P, OB>(s, kv, qv, vr, gval, beta, a.eps, a.scale, S, o_row<OB>(a, gi * D), OB == 1, row0, c);
 }
 
 template <int D, int P, bool F>
 hipError_t launch_units(const RecurArgs& a, int32_t m, hipStream_t s) {
   const int64_t units = static_cast<int64_t>(m) * a.hv * DecodeCfg<D, P>::NPART;
   const unsigned blocks = static_cast<unsigned>((units + kDecodeWaves - 1) / kDecodeWaves);
-  decode_kernel<D, P, F><<<blocks, kDecodeWaves * kWave, 0, s>>>(a, static_cast<int32_t>(units));
+  if (a.o_bf16)
+    decode_kernel<D, P, F, 1><<<blocks, kDecodeWaves * kWave, 0, s>>>(a, static_cast<int32_t>(units));
+  else
+    decode_kernel<D, P, F, 0><<<blocks, kDecodeWaves * kWave, 0, s>>>(a, static_cast<int32_t>(units));
   return hipGetLastError();
 }
 
@@ -334,7 +352,7 @@ __global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min
   float vr[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) vr[p] = yv[w * ROWS + rl + p * RPP];
-  decode_rows<D, P>(s, kv, qv, vr, gval, beta, a.eps, a.scale, S, (gfloat*)(a.o + gi * D), row0, c);
+  decode_rows<D, P, 2>(s, kv, qv, vr, gval, beta, a.eps, a.scale, S, o_row<2>(a, gi * D), a.o_bf16 != 0, row0, c);
 
   // the last workgroup of (slot, k-head) writes the q/k conv state (wave 0, from the
   // rows it put in LDS itself) and leaves the counter at zero

@@ -58,6 +58,8 @@ gdn_status check_dims(const gdn_dims* d, const char* fn) {
   if (d->prefill_form != GDN_PREFILL_AUTO && d->prefill_form != GDN_PREFILL_WHOLE &&
       d->prefill_form != GDN_PREFILL_SEGMENTS)
     return fail(GDN_ERR_SHAPE, "%s: unknown prefill_form %d", fn, d->prefill_form);
+  if (d->out_dtype != GDN_F32 && d->out_dtype != GDN_BF16)
+    return fail(GDN_ERR_DTYPE, "%s: unknown out_dtype %d", fn, d->out_dtype);
   if (!(d->l2_eps >= 0.0f) || !(d->l2_eps < 1e30f))
     return fail(GDN_ERR_SHAPE, "%s: l2_eps must be finite and >= 0", fn);
   if (!(d->scale == d->scale) || d->scale > 1e30f || d->scale < -1e30f)
@@ -73,7 +75,7 @@ int64_t channels(const gdn_dims* d) {
 
 // q/k/v of the recurrence entry points.
 gdn_status check_qkv(const gdn_dims* d, const char* fn, const float* q, int64_t qs, const float* k, int64_t ks,
-                     const float* v, int64_t vs, const float* g, const float* beta, float* o, int32_t rows) {
+                     const float* v, int64_t vs, const float* g, const float* beta, const void* o, int32_t rows) {
   if (!q || !k || !v || !g || !beta || !o) return fail(GDN_ERR_NULL, "%s: q, k, v, g, beta and o are required", fn);
   const int64_t qk_w = static_cast<int64_t>(d->num_k_heads) * d->head_dim;
   const int64_t v_w = static_cast<int64_t>(d->num_v_heads) * d->head_dim;
@@ -152,7 +154,7 @@ gdn_status gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, in
 
 gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_stride, const float* k,
                                int64_t k_stride, const float* v, int64_t v_stride, const float* g,
-                               const float* beta, float* o, const int32_t* cu_seqlens, int32_t num_seqs,
+                               const float* beta, void* o, const int32_t* cu_seqlens, int32_t num_seqs,
                                int32_t total_tokens, const uint64_t* state_ptrs, void* workspace,
                                size_t workspace_bytes, void* stream) {
   const char* fn = "gdn_prefill_chunked";
@@ -177,7 +179,8 @@ gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_s
     return fail(GDN_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
   gdn::PrefillArgs a{};
   a.r = gdn::RecurArgs{q, q_stride, k, k_stride, v, v_stride, g, beta, o, state_ptrs, dims->num_k_heads,
-                       dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale};
+                       dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
+                       dims->out_dtype == GDN_BF16};
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
   a.total_tokens = total_tokens;
@@ -199,7 +202,7 @@ gdn_status gdn_prefill_fused_workspace_size(const gdn_dims* dims, int32_t num_se
 }
 
 gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stride, const void* conv_w,
-                             const void* conv_b, const float* g, const float* beta, float* o,
+                             const void* conv_b, const float* g, const float* beta, void* o,
                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
                              const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, void* workspace,
                              size_t workspace_bytes, void* stream) {
@@ -251,7 +254,8 @@ gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stri
   // 2. the chunked prefill, the q/k conv inside its intra-chunk kernel
   gdn::PrefillArgs a{};
   a.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, yv, vw, g, beta, o, state_ptrs, dims->num_k_heads,
-                       dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale};
+                       dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
+                       dims->out_dtype == GDN_BF16};
   a.conv = gdn::ConvIn{x, x_stride, conv_w, conv_b, conv_state_ptrs, static_cast<int32_t>(C), K, silu, bf16};
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
@@ -267,7 +271,7 @@ gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stri
 
 gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_stride, const float* k,
                               int64_t k_stride, const float* v, int64_t v_stride, const float* g,
-                              const float* beta, float* o, const uint64_t* state_ptrs, int32_t m, void* stream) {
+                              const float* beta, void* o, const uint64_t* state_ptrs, int32_t m, void* stream) {
   const char* fn = "gdn_decode_batched";
   if (gdn_status st = check_dims(dims, fn)) return st;
   if (m < 0) return fail(GDN_ERR_SHAPE, "%s: negative m", fn);
@@ -276,7 +280,8 @@ gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_st
   if (!state_ptrs) return fail(GDN_ERR_NULL, "%s: state_ptrs is required", fn);
   if (gdn_status st = check_qkv(dims, fn, q, q_stride, k, k_stride, v, v_stride, g, beta, o, m)) return st;
   gdn::RecurArgs a{q, q_stride, k, k_stride, v, v_stride, g, beta, o, state_ptrs, dims->num_k_heads,
-                   dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale};
+                   dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
+                       dims->out_dtype == GDN_BF16};
   return hip_status(gdn::launch_decode(a, m, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -290,7 +295,7 @@ gdn_status gdn_decode_fused_workspace_size(const gdn_dims* dims, int32_t m, size
 }
 
 gdn_status gdn_decode_fused(const gdn_dims* dims, const void* x, int64_t x_stride, const void* conv_w,
-                            const void* conv_b, const float* g, const float* beta, float* o,
+                            const void* conv_b, const float* g, const float* beta, void* o,
                             const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, int32_t m,
                             void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "gdn_decode_fused";
@@ -314,7 +319,8 @@ gdn_status gdn_decode_fused(const gdn_dims* dims, const void* x, int64_t x_strid
   if (blocks > 0x7fffffff) return fail(GDN_ERR_SHAPE, "%s: m = %d too large for one launch", fn, m);
   gdn::FusedArgs f{};
   f.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, nullptr, 0, g, beta, o, state_ptrs, dims->num_k_heads,
-                       dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale};
+                       dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
+                       dims->out_dtype == GDN_BF16};
   f.x = x;
   f.x_stride = x_stride;
   f.w = conv_w;

@@ -42,13 +42,14 @@ struct RecurArgs {
   int64_t v_stride;
   const float* g;
   const float* beta;
-  float* o;
+  void* o;  // fp32, or bf16 when o_bf16
   const uint64_t* state_ptrs;
   int32_t hk;
   int32_t hv;
   int32_t d;
   float eps;
   float scale;
+  int32_t o_bf16;  // o holds the fp32 results rounded to bf16 (nearest even)
 };
 
 hipError_t launch_decode(const RecurArgs& a, int32_t m, hipStream_t s);

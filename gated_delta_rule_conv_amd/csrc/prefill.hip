@@ -1114,7 +1114,13 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int t = tt * 16 + 4 * lg + rr;
-      if (kOut && t < n) r.o[(static_cast<int64_t>(t0 + t) * r.hv + j) * D + blk * kDVB + l16] = o[rr];
+      if (kOut && t < n) {
+        const int64_t e = (static_cast<int64_t>(t0 + t) * r.hv + j) * D + blk * kDVB + l16;
+        if (r.o_bf16)
+          static_cast<uint16_t*>(r.o)[e] = f32_to_bf16_rne(o[rr]);
+        else
+          static_cast<float*>(r.o)[e] = o[rr];
+      }
     }
   };
   // phase 3, Q side: O = e^gam Y + P U

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -98,6 +98,8 @@ typedef struct gdn_dims {
   float l2_eps;        /* k^ = k / sqrt(|k|^2 + l2_eps); q^ likewise, then times scale */
   float scale;         /* multiplies q^ (1.0 = no scaling) */
   int32_t prefill_form; /* gdn_prefill_form */
+  int32_t out_dtype;    /* gdn_dtype of o: GDN_F32, or GDN_BF16 = the fp32 result rounded to
+                           nearest even (the conv output y is fp32 either way) */
 } gdn_dims;
 
 /* Conv channel count C = 2*Hk*d + Hv*d, channels ordered [q heads | k heads | v heads]. */
@@ -152,7 +154,7 @@ gdn_status gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, in
  *  q, k       [total_tokens][Hk*d] fp32 (raw conv output; normalised inside), row
  *             strides q_stride, k_stride.   v: [total_tokens][Hv*d] fp32, stride v_stride.
  *  g, beta    [total_tokens][Hv] fp32 contiguous: log-decay (<= 0) and write strength.
- *  o          [total_tokens][Hv][d] fp32 contiguous output.
+ *  o          [total_tokens][Hv][d] contiguous output in dims->out_dtype.
  *  cu_seqlens device int32 [num_seqs+1].
  *  state_ptrs device u64 [num_seqs]; entry s points at sequence s's state, fp32
  *             [Hv][d_v][d_k] (d_k contiguous), 16-byte aligned; read as the initial
@@ -163,7 +165,7 @@ gdn_status gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, in
  */
 gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_stride, const float* k,
                                int64_t k_stride, const float* v, int64_t v_stride, const float* g,
-                               const float* beta, float* o, const int32_t* cu_seqlens, int32_t num_seqs,
+                               const float* beta, void* o, const int32_t* cu_seqlens, int32_t num_seqs,
                                int32_t total_tokens, const uint64_t* state_ptrs, void* workspace,
                                size_t workspace_bytes, void* stream);
 
@@ -200,7 +202,7 @@ gdn_status gdn_prefill_fused_workspace_size(const gdn_dims* dims, int32_t num_se
  *  launched unless every check passes.
  */
 gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stride, const void* conv_w,
-                             const void* conv_b, const float* g, const float* beta, float* o,
+                             const void* conv_b, const float* g, const float* beta, void* o,
                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
                              const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, void* workspace,
                              size_t workspace_bytes, void* stream);
@@ -218,7 +220,7 @@ gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stri
  *  q, k       [m][Hk*d] fp32, row strides q_stride, k_stride (raw; normalised inside).
  *  v          [m][Hv*d] fp32, row stride v_stride.
  *  g, beta    [m][Hv] fp32 contiguous.
- *  o          [m][Hv][d] fp32 contiguous output.
+ *  o          [m][Hv][d] contiguous output in dims->out_dtype.
  *  state_ptrs device u64 [m]; entry i points at slot i's fp32 [Hv][d_v][d_k] state
  *             (16-byte aligned), updated in place. An entry of 0 marks an inactive
  *             slot: nothing is read or written for it (its o rows are left untouched).
@@ -226,7 +228,7 @@ gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stri
  */
 gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_stride, const float* k,
                               int64_t k_stride, const float* v, int64_t v_stride, const float* g,
-                              const float* beta, float* o, const uint64_t* state_ptrs, int32_t m,
+                              const float* beta, void* o, const uint64_t* state_ptrs, int32_t m,
                               void* stream);
 
 /* ---------------------------------------------------------------------------------
@@ -256,7 +258,7 @@ gdn_status gdn_decode_fused_workspace_size(const gdn_dims* dims, int32_t m, size
  *  Alignment: x, conv_w, conv_b 16-byte aligned, x_stride a multiple of 16 bytes.
  */
 gdn_status gdn_decode_fused(const gdn_dims* dims, const void* x, int64_t x_stride, const void* conv_w,
-                            const void* conv_b, const float* g, const float* beta, float* o,
+                            const void* conv_b, const float* g, const float* beta, void* o,
                             const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, int32_t m,
                             void* workspace, size_t workspace_bytes, void* stream);
 
