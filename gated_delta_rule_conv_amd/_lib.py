@@ -43,14 +43,16 @@ class gdn_dims(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("prefill_form", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
+        ("qk_l2norm", ctypes.c_int32),
     ]
 
 
 def make_dims(num_k_heads: int, num_v_heads: int, head_dim: int, conv_width: int = 4, chunk_size: int = 64,
               activation: int = GDN_ACT_NONE, in_dtype: int = GDN_BF16, mma: int = GDN_MMA_AUTO,
-              l2_eps: float = 1e-6, scale: float = 1.0, prefill_form: int = 0, out_dtype: int = GDN_F32) -> gdn_dims:
+              l2_eps: float = 1e-6, scale: float = 1.0, prefill_form: int = 0, out_dtype: int = GDN_F32,
+              qk_l2norm: int = 1) -> gdn_dims:
     return gdn_dims(ctypes.sizeof(gdn_dims), num_k_heads, num_v_heads, head_dim, conv_width, chunk_size,
-                    activation, in_dtype, mma, l2_eps, scale, prefill_form, out_dtype)
+                    activation, in_dtype, mma, l2_eps, scale, prefill_form, out_dtype, qk_l2norm)
 
 
 class GDNError(RuntimeError):

@@ -72,8 +72,8 @@ struct DecodeCfg {
 // OB: how o is stored -- 0 fp32, 1 bf16 (rounded to nearest even), 2 as the o_bf16 flag says.
 template <int D, int P, int OB>
 __device__ __forceinline__ void decode_rows(const f32x4 (&s)[P][4], f32x4 (&kv)[4], f32x4 (&qv)[4], const float (&vr)[P],
-                                            float gval, float beta, float eps, float scale, gf32x4* S, void* orow,
-                                            bool o_bf16, int row0, int c) {
+                                            float gval, float beta, float eps, float scale, bool qk_norm, gf32x4* S,
+                                            void* orow, bool o_bf16, int row0, int c) {
   using Cfg = DecodeCfg<D, P>;
   constexpr int LPR = Cfg::LPR, RPP = Cfg::RPP;
   // k^ and q^ at this lane's 16 columns, and k^ . q^
@@ -87,8 +87,8 @@ __device__ __forceinline__ void decode_rows(const f32x4 (&s)[P][4], f32x4 (&kv)[
   }
   kk = group_sum<LPR>(kk);
   qq = group_sum<LPR>(qq);
-  const float rk = 1.0f / sqrtf(kk + eps);
-  const float rq = scale / sqrtf(qq + eps);
+  const float rk = qk_norm ? 1.0f / sqrtf(kk + eps) : 1.0f;
+  const float rq = qk_norm ? scale / sqrtf(qq + eps) : scale;
   float kq = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(RecurArgs a
   const float beta = ((cfloat*)a.beta)[gi];
   if constexpr (SCHED_FENCE) __builtin_amdgcn_sched_barrier(0);
 
-  decode_rows<D, P, OB>(s, kv, qv, vr, gval, beta, a.eps, a.scale, S, o_row<OB>(a, gi * D), OB == 1, row0, c);
+  decode_rows<D, P, OB>(s, kv, qv, vr, gval, beta, a.eps, a.scale, a.qk_norm != 0, S, o_row<OB>(a, gi * D), OB == 1, row0, c);
 }
 
 template <int D, int P, bool F>
@@ -352,7 +352,7 @@ __global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min
   float vr[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) vr[p] = yv[w * ROWS + rl + p * RPP];
-  decode_rows<D, P, 2>(s, kv, qv, vr, gval, beta, a.eps, a.scale, S, o_row<2>(a, gi * D), a.o_bf16 != 0, row0, c);
+  decode_rows<D, P, 2>(s, kv, qv, vr, gval, beta, a.eps, a.scale, a.qk_norm != 0, S, o_row<2>(a, gi * D), a.o_bf16 != 0, row0, c);
 
   // the last workgroup of (slot, k-head) writes the q/k conv state (wave 0, from the
   // rows it put in LDS itself) and leaves the counter at zero

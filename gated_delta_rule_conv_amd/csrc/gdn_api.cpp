@@ -60,6 +60,8 @@ gdn_status check_dims(const gdn_dims* d, const char* fn) {
     return fail(GDN_ERR_SHAPE, "%s: unknown prefill_form %d", fn, d->prefill_form);
   if (d->out_dtype != GDN_F32 && d->out_dtype != GDN_BF16)
     return fail(GDN_ERR_DTYPE, "%s: unknown out_dtype %d", fn, d->out_dtype);
+  if (d->qk_l2norm != 0 && d->qk_l2norm != 1)
+    return fail(GDN_ERR_SHAPE, "%s: qk_l2norm must be 0 or 1 (got %d)", fn, d->qk_l2norm);
   if (!(d->l2_eps >= 0.0f) || !(d->l2_eps < 1e30f))
     return fail(GDN_ERR_SHAPE, "%s: l2_eps must be finite and >= 0", fn);
   if (!(d->scale == d->scale) || d->scale > 1e30f || d->scale < -1e30f)
@@ -180,7 +182,7 @@ gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_s
   gdn::PrefillArgs a{};
   a.r = gdn::RecurArgs{q, q_stride, k, k_stride, v, v_stride, g, beta, o, state_ptrs, dims->num_k_heads,
                        dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16};
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm};
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
   a.total_tokens = total_tokens;
@@ -255,7 +257,7 @@ gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stri
   gdn::PrefillArgs a{};
   a.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, yv, vw, g, beta, o, state_ptrs, dims->num_k_heads,
                        dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16};
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm};
   a.conv = gdn::ConvIn{x, x_stride, conv_w, conv_b, conv_state_ptrs, static_cast<int32_t>(C), K, silu, bf16};
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
@@ -281,7 +283,7 @@ gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_st
   if (gdn_status st = check_qkv(dims, fn, q, q_stride, k, k_stride, v, v_stride, g, beta, o, m)) return st;
   gdn::RecurArgs a{q, q_stride, k, k_stride, v, v_stride, g, beta, o, state_ptrs, dims->num_k_heads,
                    dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16};
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm};
   return hip_status(gdn::launch_decode(a, m, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -320,7 +322,7 @@ gdn_status gdn_decode_fused(const gdn_dims* dims, const void* x, int64_t x_strid
   gdn::FusedArgs f{};
   f.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, nullptr, 0, g, beta, o, state_ptrs, dims->num_k_heads,
                        dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16};
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm};
   f.x = x;
   f.x_stride = x_stride;
   f.w = conv_w;

@@ -49,7 +49,8 @@ struct RecurArgs {
   int32_t d;
   float eps;
   float scale;
-  int32_t o_bf16;  // o holds the fp32 results rounded to bf16 (nearest even)
+  int32_t o_bf16;   // o holds the fp32 results rounded to bf16 (nearest even)
+  int32_t qk_norm;  // q and k L2-normalised (else used as given; q still times scale)
 };
 
 hipError_t launch_decode(const RecurArgs& a, int32_t m, hipStream_t s);

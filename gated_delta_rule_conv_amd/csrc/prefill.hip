@@ -576,8 +576,8 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     }
     kk = group_sum<TPR>(kk);
     qq = group_sum<TPR>(qq);
-    const float rk = live ? 1.0f / sqrtf(kk + r.eps) : 0.f;
-    const float rq = live ? r.scale / sqrtf(qq + r.eps) : 0.f;
+    const float rk = live ? (r.qk_norm ? 1.0f / sqrtf(kk + r.eps) : 1.0f) : 0.f;
+    const float rq = live ? (r.qk_norm ? r.scale / sqrtf(qq + r.eps) : r.scale) : 0.f;
     if (row < C) {
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {

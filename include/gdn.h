@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -100,6 +100,9 @@ typedef struct gdn_dims {
   int32_t prefill_form; /* gdn_prefill_form */
   int32_t out_dtype;    /* gdn_dtype of o: GDN_F32, or GDN_BF16 = the fp32 result rounded to
                            nearest even (the conv output y is fp32 either way) */
+  int32_t qk_l2norm;    /* 1: q and k L2-normalised in the kernels (the layer's step 2);
+                           0: used as given (q still times scale). Set it explicitly: a
+                           zero-filled struct turns the normalisation off. */
 } gdn_dims;
 
 /* Conv channel count C = 2*Hk*d + Hv*d, channels ordered [q heads | k heads | v heads]. */

@@ -181,7 +181,8 @@ def gated_delta_chunked(q, k, v, g, beta, S0, chunk: int, kmap=None):
 
 def prefill_layer(x, conv_w, cu_seqlens, conv_state, S0, g, beta, Hk: int, Hv: int, d: int,
                   conv_b=None, in_dtype: str = "f32", activation: str = "none",
-                  eps: float = 1e-6, scale: float = 1.0, v_heads=None, chunk: int | None = None):
+                  eps: float = 1e-6, scale: float = 1.0, v_heads=None, chunk: int | None = None,
+                  qk_l2norm: bool = True):
     """The whole layer core over packed ragged sequences.
 
     x [T, C] (storage dtype), conv_w [C, K], conv_b [C] or None, cu_seqlens [N+1],
@@ -189,7 +190,9 @@ def prefill_layer(x, conv_w, cu_seqlens, conv_state, S0, g, beta, Hk: int, Hv: i
     Per sequence: conv (from its own conv state) -> split -> L2 norm (q also scaled)
     -> gated delta rule from its own recurrent state. Sequences never see each other.
     ``v_heads`` restricts the recurrence to a subset of v-heads (o and S come back for
-    those heads only); ``chunk`` switches the recurrence to the chunked form.
+    those heads only); ``chunk`` switches the recurrence to the chunked form;
+    ``qk_l2norm=False`` skips the L2 norm (q and k used as the conv gives them, q still
+    times ``scale``).
 
     Returns dict y [T, C], o [T, H, d], S [N, H, d, d], conv_state [N, K-1, C].
     """
@@ -214,8 +217,8 @@ def prefill_layer(x, conv_w, cu_seqlens, conv_state, S0, g, beta, Hk: int, Hv: i
         ys, cs_out[s] = causal_conv(xf[a:b], wf, bf, csf[s], activation)
         y[a:b] = ys
         q, k, v = split_qkv(ys, Hk, Hv, d, d)
-        qn = l2norm(q, eps) * scale
-        kn = l2norm(k, eps)
+        qn = (l2norm(q, eps) if qk_l2norm else q) * scale
+        kn = l2norm(k, eps) if qk_l2norm else k
         args = (qn, kn, v[:, heads], g[a:b][:, heads], beta[a:b][:, heads], S0[s][heads])
         if chunk is None:
             o[a:b], S_out[s] = gated_delta_recurrent(*args, kmap=kmap)

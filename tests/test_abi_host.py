@@ -34,8 +34,8 @@ def test_header_symbols_are_exported():
 
 
 def test_abi_version_and_struct_size():
-    assert gdn.gdn_abi_version() == 3
-    assert ctypes.sizeof(_lib.gdn_dims) == 13 * 4
+    assert gdn.gdn_abi_version() == 4
+    assert ctypes.sizeof(_lib.gdn_dims) == 14 * 4
 
 
 def dims(**kw):
@@ -59,6 +59,7 @@ def _status(fn, *args):
     (dict(num_k_heads=0), _lib.GDN_ERR_SHAPE),
     (dict(in_dtype=7), _lib.GDN_ERR_DTYPE),
     (dict(out_dtype=2), _lib.GDN_ERR_DTYPE),
+    (dict(qk_l2norm=2), _lib.GDN_ERR_SHAPE),
     (dict(activation=3), _lib.GDN_ERR_DTYPE),
     (dict(mma=9), _lib.GDN_ERR_DTYPE),
     (dict(l2_eps=-1.0), _lib.GDN_ERR_SHAPE),

@@ -149,3 +149,32 @@ def test_bf16_inputs_decode_exactly():
     assert inp["x"].dtype == np.uint16
     out = _run(inp)
     assert np.all(np.isfinite(out["o"]))
+
+
+def test_qk_l2norm_off_skips_only_the_norm():
+    """With identity conv taps (w = e_{K-1}, so y = x) and q, k head vectors of x that are
+    unit vectors already, the layer without the L2 norm equals the layer with it at eps = 0
+    (to fp32 rounding of the inputs); and without the norm o is linear in q (the norm would
+    cancel a scale of q's channels), while the state does not depend on q at all."""
+    inp = _layer_inputs([19, 5])
+    sh = inp["shape"]
+    d, Hk = sh.head_dim, sh.num_k_heads
+    C = sh.channels
+    w = np.zeros((C, sh.conv_width), dtype=np.float32)
+    w[:, -1] = 1.0
+    x = np.array(inp["x"], dtype=np.float64)
+    qk = x[:, :2 * Hk * d].reshape(len(x), 2 * Hk, d)
+    x[:, :2 * Hk * d] = (qk / np.linalg.norm(qk, axis=-1, keepdims=True)).reshape(len(x), -1)
+    x = x.astype(np.float32)
+    base = dict(inp, x=x, conv_w=w)
+    on = _run(base, eps=0.0)
+    off = _run(base, eps=0.0, qk_l2norm=False)
+    np.testing.assert_allclose(off["o"], on["o"], rtol=0, atol=1e-5 * np.abs(on["o"]).max())
+    np.testing.assert_allclose(off["S"], on["S"], rtol=0, atol=1e-5 * np.abs(on["S"]).max())
+    x2 = x.copy()
+    x2[:, :Hk * d] *= 2.0  # q channels only (exact in fp32)
+    off2 = _run(dict(base, x=x2), eps=0.0, qk_l2norm=False)
+    on2 = _run(dict(base, x=x2), eps=0.0)
+    np.testing.assert_allclose(off2["o"], 2.0 * off["o"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(off2["S"], off["S"])
+    np.testing.assert_allclose(on2["o"], on["o"], rtol=1e-12, atol=1e-14)
