@@ -22,9 +22,12 @@
 //                        chunk offsets, a longest-first sequence order and (chunk-parallel
 //                        form) the segment table, on the device.
 //   intra_chunk_kernel : one workgroup per (chunk, k-head), all chunks in parallel:
-//                        normalised K, Q in LDS; K K^T and Q K^T on MFMA; for each v-head
+//                        K, Q in LDS (L2-normalised unless that is switched off); K K^T and Q K^T on MFMA; for each v-head
 //                        sharing the k-head: the decay mask, A, T by blocked (16x16)
 //                        forward substitution, and P. K^, Q^, T and P go to the workspace.
+//                        Through the fused entry point it also convolves its chunk's q and
+//                        k channels from x, and a sequence's first chunk commits the conv
+//                        state of its k-head's q, k and v channels.
 //   inter_chunk_kernel : one workgroup per (sequence, v-head, 16 state rows), walking the
 //                        chunks of its sequence in order with its 16 x d slice of the
 //                        state resident in registers/LDS; the contractions K S^T, Q S^T,
