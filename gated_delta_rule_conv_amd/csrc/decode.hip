@@ -246,7 +246,7 @@ struct FusedCfg {
   static constexpr int min_blocks() { return (P == 1 && sizeof(T) == 2 && WPB == 4) ? 7 : 1; }
 };
 
-template <typename T, int K, int D, int P, bool SCHED_FENCE>
+template <typename T, int K, int D, int P, bool SCHED_FENCE, bool CONV_FIRST>
 __global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min_blocks<T>())) void fused_decode_kernel(FusedArgs f) {
   using Cfg = DecodeCfg<D, P>;
   using FC = FusedCfg<D, P>;
@@ -277,19 +277,22 @@ __global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min
   GT* cs = (GT*)reinterpret_cast<T*>(cp);
   const int C = f.channels;
 
-  // Conv inputs first: thread t < NCG takes channel group t (q/k groups, then v groups);
-  // other threads that load repeat a v group and drop the result. Then every wave's
-  // state rows, so that all loads are in flight before anything waits. (With two passes
-  // per wave every wave loads conv inputs: there, loads under the branch made the
-  // compiler copy their results at its end, which waits for them before the state loads
-  // can issue.)
+  // Thread t < NCG takes channel group t (q/k groups, then v groups); other threads that
+  // load repeat a v group and drop the result. Everything is in flight before anything
+  // waits. CONV_FIRST: the conv inputs are loaded before the state rows, so the conv
+  // waits only for its own (mostly cached) inputs -- best where the launch is short and
+  // latency-bound; with two passes per wave every wave then loads conv inputs (loads
+  // under a branch made the compiler copy their results at its end, which waits for them
+  // before the state loads can issue). Otherwise the state rows go first and only the
+  // convolving waves load conv inputs, which issues fewer loads where the launch fills
+  // the chip.
   const bool conv_wave = w < FC::NCW;
   const int grp = tid < NCG ? tid : GQK + (tid - NCG) % GV;
   const bool is_qk = grp < GQK;
   const int ch0 = is_qk ? (grp * V < D ? h * D + grp * V : a.hk * D + h * D + (grp * V - D))
                         : 2 * a.hk * D + j * D + bh * VR + (grp - GQK) * V;
   typename V4::Raw xr, sr[K - 1], wr[K], br;
-  if (conv_wave || P > 1) {
+  auto load_conv = [&]() {
 #pragma unroll
     for (int t = 0; t < K - 1; ++t) sr[t] = V4::load_raw_g(cs + static_cast<int64_t>(t) * C + ch0);
     xr = V4::load_raw(static_cast<const T*>(f.x) + static_cast<int64_t>(i) * f.x_stride + ch0);
@@ -297,13 +300,22 @@ __global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min
     for (int t = 0; t < K; ++t) wr[t] = V4::load_raw(static_cast<const T*>(f.w) + static_cast<int64_t>(ch0) * K + t * V);
     // with no bias, taps stand in for the load and are never used
     br = V4::load_raw(static_cast<const T*>(f.b ? f.b : f.w) + ch0);
-  }
+  };
   f32x4 s[P][4];
+  auto load_state = [&]() {
 #pragma unroll
-  for (int p = 0; p < P; ++p)
+    for (int p = 0; p < P; ++p)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      s[p][e] = __builtin_nontemporal_load(S + static_cast<int64_t>(row0 + p * RPP) * (D / 4) + c + LPR * e);
+      for (int e = 0; e < 4; ++e)
+        s[p][e] = __builtin_nontemporal_load(S + static_cast<int64_t>(row0 + p * RPP) * (D / 4) + c + LPR * e);
+  };
+  if constexpr (!CONV_FIRST) {
+    load_state();
+    if (conv_wave) load_conv();
+  } else {
+    if (conv_wave || P > 1) load_conv();
+    load_state();
+  }
   const int64_t gi = static_cast<int64_t>(i) * a.hv + j;
   const float gval = ((cfloat*)a.g)[gi];
   const float beta = ((cfloat*)a.beta)[gi];
@@ -365,22 +377,29 @@ __global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min
   }
 }
 
-template <typename T, int K, int D, int P, bool F>
+template <typename T, int K, int D, int P, bool F, bool CF>
 hipError_t launch_fused_units(const FusedArgs& f, int32_t m, hipStream_t s) {
   using FC = FusedCfg<D, P>;
   const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(m) * f.r.hv * FC::BPH);
-  fused_decode_kernel<T, K, D, P, F><<<blocks, FC::NT, 0, s>>>(f);
+  fused_decode_kernel<T, K, D, P, F, CF><<<blocks, FC::NT, 0, s>>>(f);
   return hipGetLastError();
 }
 
 template <typename T, int K>
 hipError_t launch_fused_k(const FusedArgs& f, int32_t m, hipStream_t s) {
-  const bool big = static_cast<int64_t>(m) * f.r.hv >= 1024;
+  // unit size as launch_decode; below m * Hv = 256 (a launch of a few hundred
+  // workgroups) the two-pass units load the conv inputs first
+  const int64_t mh = static_cast<int64_t>(m) * f.r.hv;
   switch (f.r.d) {
-    case 32: return launch_fused_units<T, K, 32, 1, false>(f, m, s);
-    case 64: return big ? launch_fused_units<T, K, 64, 1, false>(f, m, s) : launch_fused_units<T, K, 64, 2, true>(f, m, s);
+    case 32: return launch_fused_units<T, K, 32, 1, false, true>(f, m, s);
+    case 64:
+      if (mh >= 1024) return launch_fused_units<T, K, 64, 1, false, true>(f, m, s);
+      return mh >= 256 ? launch_fused_units<T, K, 64, 2, true, false>(f, m, s)
+                       : launch_fused_units<T, K, 64, 2, true, true>(f, m, s);
     default:
-      return big ? launch_fused_units<T, K, 128, 1, false>(f, m, s) : launch_fused_units<T, K, 128, 2, true>(f, m, s);
+      if (mh >= 1024) return launch_fused_units<T, K, 128, 1, false, true>(f, m, s);
+      return mh >= 256 ? launch_fused_units<T, K, 128, 2, true, false>(f, m, s)
+                       : launch_fused_units<T, K, 128, 2, true, true>(f, m, s);
   }
 }
 

@@ -32,9 +32,12 @@ def _pool(gdn, dims, base, shape):
 
 
 # (Hk, Hv, d, in_dtype, K, activation, bias, m): both unit sizes (m * Hv >= 1024 takes
-# one-pass units), all head dims, both input dtypes, every conv width, SiLU and bias
+# one-pass units) and both load orders of the two-pass units (conv inputs first below
+# m * Hv = 256), all head dims, both input dtypes, every conv width, SiLU and bias
 CASES = [
     (16, 32, 128, "bf16", 4, 0, False, 40),
+    (16, 32, 128, "bf16", 4, 1, True, 16),
+    (2, 4, 64, "bf16", 3, 0, False, 100),
     (16, 32, 128, "bf16", 4, 0, False, 7),
     (4, 8, 128, "f32", 3, 1, True, 5),
     (2, 4, 64, "bf16", 2, 0, True, 300),
