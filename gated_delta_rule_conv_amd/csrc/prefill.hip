@@ -363,11 +363,17 @@ template <typename T, int K, int D, int C, int KP>
 __device__ __forceinline__ void conv_qk_rows_k(const PrefillArgs& a, int h, int t0, int n, int seq_start, int s,
                                                float (*Kh)[KP], float (*Qh)[KP], int tid) {
   using V8 = Vec8<T>;
+  using GT = const typename V8::GT;
   constexpr int G = 2 * D / kConvVec;                                 // 8-channel groups
   constexpr int RPT = (G * C >= kThreads) ? G * C / kThreads : 1;    // rows per thread
   constexpr int NS = C / RPT;                                          // row strips
-  const T* __restrict__ x = static_cast<const T*>(a.conv.x);
-  const T* cs = reinterpret_cast<const T*>(a.conv.state_ptrs[s]);
+  // (global-address-space pointers: every load below is issued before any is used, in
+  // one memory round trip)
+  GT* x = (GT*)static_cast<const T*>(a.conv.x);
+  GT* cs = (GT*)reinterpret_cast<const T*>(a.conv.state_ptrs[s]);
+  GT* wt = (GT*)static_cast<const T*>(a.conv.w);
+  const bool has_b = a.conv.b != nullptr;
+  GT* bs = (GT*)static_cast<const T*>(has_b ? a.conv.b : a.conv.w);  // (taps stand in when there is no bias)
   const int64_t cstride = a.conv.channels;
   const int pos0 = t0 - seq_start;  // position of the chunk's first row in its sequence
   const bool silu = a.conv.silu != 0;
@@ -376,18 +382,22 @@ __device__ __forceinline__ void conv_qk_rows_k(const PrefillArgs& a, int h, int 
     const bool isq = grp < G / 2;
     const int col = (isq ? grp : grp - G / 2) * kConvVec;  // column within the head
     const int ch = (isq ? 0 : a.r.hk * D) + h * D + col;    // channel of x, the taps and the conv state
-    ConvTaps<T, K> taps;
-    taps.load(static_cast<const T*>(a.conv.w), static_cast<const T*>(a.conv.b), ch);
+    typename V8::Raw wr[K], br;
+#pragma unroll
+    for (int t = 0; t < K; ++t) wr[t] = V8::load_raw_g(wt + static_cast<int64_t>(ch) * K + t * kConvVec);
+    br = V8::load_raw_g(bs + ch);
     const int r0 = strip * RPT;
     typename V8::Raw z[RPT + K - 1];  // z rows r0 - (K-1) .. r0 + RPT - 1 (chunk coordinates)
 #pragma unroll
     for (int i = 0; i < RPT + K - 1; ++i) {
       const int rr = min(r0 - (K - 1) + i, n - 1);  // rows past the chunk's end repeat its last
       const int p = pos0 + rr;                       // position in the sequence
-      const T* src = p >= 0 ? x + static_cast<int64_t>(seq_start + p) * a.conv.x_stride + ch
-                            : cs + static_cast<int64_t>(p + K - 1) * cstride + ch;
-      z[i] = V8::load_raw(src);
+      GT* src = p >= 0 ? x + static_cast<int64_t>(seq_start + p) * a.conv.x_stride + ch
+                       : cs + static_cast<int64_t>(p + K - 1) * cstride + ch;
+      z[i] = V8::load_raw_g(src);
     }
+    ConvTaps<T, K> taps;
+    taps.from_raw(wr, br, has_b);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = r0 + i;
