@@ -643,7 +643,7 @@ def main() -> int:
                          "fused_kernel_GBps": round(f_bytes_per_launch / (f_kern_us * 1e-6) / 1e9, 2)},
         "decode_sweep": sweep,
         "prefill": prefill,
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,1,false>", "achieved": round(achieved, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,1,false,0>", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.m == 64 else None,
                      "bytes_per_launch": bytes_per_launch,
