@@ -729,9 +729,12 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
 
     // A (strictly lower) into LDS and P (lower incl. diagonal) to the workspace, one
     // fragment lane per thread; the k range runs to the padded NKF * KSTEP so the zero
-    // padding of the P fragments is written too
+    // padding of the P fragments is written too. Fragments wholly above the diagonal are
+    // neither written nor read: the inter-chunk kernel skips their products (the same
+    // test, kk * KSTEP >= 16 (row tile + 1)), and A's upper triangle is never read.
     for (int e = tid; e < (C / 16) * NKF * 64; e += kThreads) {
       const int blk = e / 64, ln = e % 64;
+      if ((blk % NKF) * KSTEP >= (blk / NKF + 1) * 16) continue;
       const int t = (blk / NKF) * 16 + ln % 16, s0 = (blk % NKF) * KSTEP + KPL * (ln / 16);
       float pv[KPL];
 #pragma unroll
@@ -800,6 +803,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
 
     for (int e = tid; e < (C / 16) * NKF * 64; e += kThreads) {
       const int blk = e / 64, ln = e % 64;
+      if ((blk % NKF) * KSTEP >= (blk / NKF + 1) * 16) continue;  // (above the diagonal, as P)
       const int t = (blk / NKF) * 16 + ln % 16, s0 = (blk % NKF) * KSTEP + KPL * (ln / 16);
       float tv[KPL];
 #pragma unroll
