@@ -215,10 +215,11 @@ namespace {
 // decode above. A workgroup is WPB units of one (slot, v-head), i.e. VR consecutive
 // state rows. Threads first convolve 4 channels each -- the 2d q/k channels of the
 // head's k-head (wave 0) and then the VR v channels of the workgroup's rows -- into LDS
-// with the conv kernels' arithmetic (conv4_raw); their conv inputs are loaded before
-// the state rows, so the conv waits only for its own (mostly cached) inputs while the
-// state is still streaming in. The waves then take k, q and v from LDS and run
-// decode_rows unchanged.
+// with the conv kernels' arithmetic (conv4_raw). In one-pass units and short launches
+// the conv inputs are loaded before the state rows, so the conv waits only for its own
+// (mostly cached) inputs while the state is still streaming in; otherwise after them
+// (see CONV_FIRST). The waves then take k, q and v from LDS and run decode_rows
+// unchanged.
 //
 // Conv state commit. The v channels of a workgroup's rows are read by that workgroup
 // alone, so their lanes write the shifted state right after reading it. The q/k
@@ -240,8 +241,8 @@ struct FusedCfg {
   static constexpr int NCW = (NCG + kWave - 1) / kWave;                   // waves that convolve
   static_assert(GQK <= kWave, "the q/k groups are wave 0's");
   static_assert(NCG <= NT, "one channel group per thread");
-  // One-pass units with bf16 inputs fit 72 VGPRs, i.e. 7 waves per SIMD (one register
-  // more would cost a wave); fp32 inputs need more registers for the raw conv inputs.
+  // One-pass units with bf16 inputs are held to 72 VGPRs, at least 7 waves per SIMD
+  // (they take 64: 8 waves); fp32 inputs need more registers for the raw conv inputs.
   template <typename T>
   static constexpr int min_blocks() { return (P == 1 && sizeof(T) == 2 && WPB == 4) ? 7 : 1; }
 };
