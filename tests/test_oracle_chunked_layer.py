@@ -178,3 +178,21 @@ def test_qk_l2norm_off_skips_only_the_norm():
     np.testing.assert_allclose(off2["o"], 2.0 * off["o"], rtol=1e-12, atol=1e-14)
     np.testing.assert_array_equal(off2["S"], off["S"])
     np.testing.assert_allclose(on2["o"], on["o"], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("c", [0.25, 3.0])
+def test_scale_multiplies_output_only_with_norm_on(c):
+    """q^ = scale * q / sqrt(|q|^2 + eps): with the norm on, o is linear in q^ and the
+    state never sees q, so scale = c gives o(c) = c * o(1) and the same final states.
+    A reading that scales q before the norm (where the factor cancels) gives o(c) = o(1)
+    and fails the first check; one that scales k changes the states and fails the second."""
+    inp = _layer_inputs([5, 37, 1], Hk=2, Hv=4, d=8)
+    base = _run(inp)
+    scaled = _run(inp, scale=c)
+    if c == 0.25:  # a power of two: every product is exact, so the bits agree
+        np.testing.assert_array_equal(scaled["o"], c * base["o"])
+    else:
+        np.testing.assert_allclose(scaled["o"], c * base["o"], rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(scaled["S"], base["S"])
+    np.testing.assert_array_equal(scaled["conv_state"], base["conv_state"])
+    assert np.abs(base["o"]).max() > 0.1  # (the check is not vacuous)

@@ -121,3 +121,20 @@ def test_packed_sequences_do_not_see_each_other():
         z = np.concatenate([cs[s], x[cu[s]:cu[s + 1]]])
         np.testing.assert_array_equal(out["y"][cu[s]:cu[s + 1]], z[:L])
         np.testing.assert_array_equal(out["conv_state"][s], z[-(K - 1):])
+
+
+def test_conv_bias_is_added_before_silu():
+    """With identity taps (w = e_{K-1}) and a bias b the conv output is silu(x + b): the
+    bias sits inside the activation (y = act(b + sum_j w_j z_j)). The reverse order,
+    silu(x) + b, differs for every nonzero b, so it fails this pin."""
+    C, K, L = 6, 4, 9
+    x = rng.standard_normal((L, C))
+    st = rng.standard_normal((K - 1, C))
+    b = rng.uniform(-1.0, 1.0, C)
+    w = np.zeros((C, K))
+    w[:, K - 1] = 1.0
+    y, _ = causal_conv(x, w, b, st, activation="silu")
+    pre = x + b[None, :]
+    np.testing.assert_allclose(y, pre * expit(pre), rtol=1e-14, atol=1e-15)
+    swapped = x * expit(x) + b[None, :]
+    assert np.abs(y - swapped).min() > 1e-6

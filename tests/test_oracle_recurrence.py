@@ -185,3 +185,70 @@ def test_gqa_head_map_is_consecutive_grouping():
         ref = np.zeros((d, d))
         ref[:, j // 2] = v[0, j]
         np.testing.assert_array_equal(S[j], ref)
+
+
+# Unit keys with rational coordinates (Pythagorean triples and quadruples), so that
+# k k^T, and with it every step of the rule, is exact in rational arithmetic.
+_RATIONAL_UNIT_KEYS = {
+    2: [(3, 4, 5), (5, 12, 13), (8, 15, 17), (1, 0, 1), (0, 1, 1), (-12, 5, 13)],
+    3: [(1, 2, 2, 3), (2, 3, 6, 7), (2, -6, 9, 11), (0, 0, 1, 1), (4, 4, 7, 9)],
+    4: [(1, 1, 1, 1, 2), (1, 2, 2, 4, 5), (2, 4, 5, 6, 9), (-1, 1, -1, 1, 2), (0, 3, 0, 4, 5)],
+}
+
+
+def _exact_kronecker_run(keys, vals, qs, alphas, betas, S0):
+    """The whole sequence in exact rational arithmetic (fractions.Fraction), through the
+    Kronecker form with column-major vec: vec(S_t) = (alpha (I - beta k k^T) kron I_dv)
+    vec(S_{t-1}) + beta (k kron v), each (dk dv) x (dk dv) matrix materialised. Returns the
+    outputs S_t q_t and the final state, as Fractions."""
+    from fractions import Fraction as Fr
+
+    dv, dk = len(S0), len(S0[0])
+    n = dk * dv
+    vec = [S0[r][c] for c in range(dk) for r in range(dv)]  # column-major
+    outs = []
+    for k, v, q, a, b in zip(keys, vals, qs, alphas, betas):
+        proj = [[(Fr(1) if i == j else Fr(0)) - b * k[i] * k[j] for j in range(dk)] for i in range(dk)]
+        # (A kron I_dv)[(i, r), (j, s)] = A[i][j] * [r == s], index (i, r) -> i * dv + r
+        big = [[a * proj[i // dv][j // dv] * (1 if i % dv == j % dv else 0) for j in range(n)] for i in range(n)]
+        kv = [b * k[i // dv] * v[i % dv] for i in range(n)]
+        vec = [sum(big[i][j] * vec[j] for j in range(n)) + kv[i] for i in range(n)]
+        S = [[vec[c * dv + r] for c in range(dk)] for r in range(dv)]
+        outs.append([sum(S[r][c] * q[c] for c in range(dk)) for r in range(dv)])
+    return outs, [[vec[c * dv + r] for c in range(dk)] for r in range(dv)]
+
+
+@pytest.mark.parametrize("dk,dv,L", [(2, 2, 6), (2, 3, 8), (3, 2, 5), (4, 3, 5), (4, 4, 4)])
+def test_brute_force_kronecker_form_exact_rational(dk, dv, L):
+    """The oracle (float64) against the exact rational result of the Kronecker form:
+    rational decays alpha = exp(g) and strengths beta, Pythagorean unit keys, rational v,
+    q and S0. The only rounding on the oracle's side is float64 (and g = log alpha), so the
+    two agree to a few ulp of the largest value."""
+    from fractions import Fraction as Fr
+
+    r = np.random.default_rng(100 + 10 * dk + dv)
+    table = _RATIONAL_UNIT_KEYS[dk]
+    keys = []
+    for t in range(L):
+        *num, den = table[int(r.integers(len(table)))]
+        keys.append([Fr(c, den) for c in num])
+    vals = [[Fr(int(r.integers(-9, 10)), int(r.integers(1, 5))) for _ in range(dv)] for _ in range(L)]
+    qs = [[Fr(int(r.integers(-6, 7)), 4) for _ in range(dk)] for _ in range(L)]
+    alphas = [Fr(int(r.integers(1, 9)), 8) for _ in range(L)]
+    betas = [Fr(int(r.integers(0, 5)), 4) for _ in range(L)]  # includes beta = 0 and beta = 1
+    S0 = [[Fr(int(r.integers(-5, 6)), 8) for _ in range(dk)] for _ in range(dv)]
+    outs, S_exact = _exact_kronecker_run(keys, vals, qs, alphas, betas, S0)
+
+    def f(a):
+        return np.array([[float(x) for x in row] for row in a])
+
+    q = f(qs)[:, None, :]
+    k = f(keys)[:, None, :]
+    v = f(vals)[:, None, :]
+    g = np.log(np.array([float(a) for a in alphas]))[:, None]
+    beta = np.array([float(b) for b in betas])[:, None]
+    o, S = gated_delta_recurrent(q, k, v, g, beta, f(S0)[None])
+    o_ref, S_ref = f(outs), f(S_exact)
+    scale = max(np.abs(o_ref).max(), np.abs(S_ref).max(), 1.0)
+    np.testing.assert_allclose(o[:, 0], o_ref, rtol=0, atol=1e-13 * scale)
+    np.testing.assert_allclose(S[0], S_ref, rtol=0, atol=1e-13 * scale)
