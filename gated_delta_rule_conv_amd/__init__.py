@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     gdn_decode_fused,
     gdn_decode_fused_workspace_size,
     gdn_dims,
+    gdn_dims_init,
     gdn_last_error,
     gdn_prefill_chunked,
     gdn_prefill_fused,

@@ -23,7 +23,7 @@ GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 GDN_MMA_AUTO, GDN_MMA_FP32, GDN_MMA_BF16X3 = 0, 1, 2
 GDN_PREFILL_AUTO, GDN_PREFILL_WHOLE, GDN_PREFILL_SEGMENTS = 0, 1, 2
 
-EXPORTED = ("gdn_conv_update", "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_fused_workspace_size",
+EXPORTED = ("gdn_dims_init", "gdn_conv_update", "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_fused_workspace_size",
             "gdn_prefill_fused", "gdn_decode_batched", "gdn_decode_fused_workspace_size", "gdn_decode_fused",
             "gdn_slot_copy", "gdn_slot_pointers", "gdn_last_error", "gdn_abi_version")
 
@@ -43,16 +43,17 @@ class gdn_dims(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("prefill_form", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
-        ("qk_l2norm", ctypes.c_int32),
+        ("qk_l2norm_off", ctypes.c_int32),
     ]
 
 
 def make_dims(num_k_heads: int, num_v_heads: int, head_dim: int, conv_width: int = 4, chunk_size: int = 64,
               activation: int = GDN_ACT_NONE, in_dtype: int = GDN_BF16, mma: int = GDN_MMA_AUTO,
               l2_eps: float = 1e-6, scale: float = 1.0, prefill_form: int = 0, out_dtype: int = GDN_F32,
-              qk_l2norm: int = 1) -> gdn_dims:
+              qk_l2norm: bool = True) -> gdn_dims:
+    """gdn_dims with struct_size set; ``qk_l2norm=False`` sets the struct's qk_l2norm_off."""
     return gdn_dims(ctypes.sizeof(gdn_dims), num_k_heads, num_v_heads, head_dim, conv_width, chunk_size,
-                    activation, in_dtype, mma, l2_eps, scale, prefill_form, out_dtype, qk_l2norm)
+                    activation, in_dtype, mma, l2_eps, scale, prefill_form, out_dtype, 0 if qk_l2norm else 1)
 
 
 class GDNError(RuntimeError):
@@ -87,6 +88,7 @@ def _load() -> ctypes.CDLL:
                           "share torch's runtime")
     P, I32, I64, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
     D = ctypes.POINTER(gdn_dims)
+    lib.gdn_dims_init.argtypes = [D, I32, I32, I32]
     lib.gdn_conv_update.argtypes = [D, P, I64, P, I64, P, P, P, P, I32, I32, P]
     lib.gdn_prefill_workspace_size.argtypes = [D, I32, I32, ctypes.POINTER(SZ)]
     lib.gdn_prefill_chunked.argtypes = [D, P, I64, P, I64, P, I64, P, P, P, P, I32, I32, P, P, SZ, P]
@@ -97,7 +99,7 @@ def _load() -> ctypes.CDLL:
     lib.gdn_decode_fused.argtypes = [D, P, I64, P, P, P, P, P, P, P, I32, P, SZ, P]
     lib.gdn_slot_copy.argtypes = [D, P, P, P, P, I32, P]
     lib.gdn_slot_pointers.argtypes = [U64, I64, I32, P, I32, P, P]
-    for fn in ("gdn_conv_update", "gdn_prefill_workspace_size", "gdn_prefill_chunked",
+    for fn in ("gdn_dims_init", "gdn_conv_update", "gdn_prefill_workspace_size", "gdn_prefill_chunked",
                "gdn_prefill_fused_workspace_size", "gdn_prefill_fused", "gdn_decode_batched",
                "gdn_decode_fused_workspace_size", "gdn_decode_fused", "gdn_slot_copy", "gdn_slot_pointers"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -146,6 +148,13 @@ def gdn_last_error() -> str:
 
 def gdn_abi_version() -> int:
     return int(_LIB.gdn_abi_version())
+
+
+def gdn_dims_init(num_k_heads: int, num_v_heads: int, head_dim: int) -> gdn_dims:
+    """The library's default-filled gdn_dims for these sizes."""
+    d = gdn_dims()
+    _check("gdn_dims_init", _LIB.gdn_dims_init(ctypes.byref(d), num_k_heads, num_v_heads, head_dim))
+    return d
 
 
 def gdn_conv_update(dims: gdn_dims, x, x_stride: int, y, y_stride: int, conv_w, conv_b, cu_seqlens,

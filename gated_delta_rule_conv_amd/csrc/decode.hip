@@ -5,8 +5,8 @@
 //     S_new = alpha S (I - beta k^ k^T) + beta v k^T   and   o = S_new q^.
 // ("System Design" (project_6), "GDN Kernel Dispatch Detail", decode branch: decay of
 // the temporal state with the delta write, then the query against the state;
-// aprender #5279, "Phase plan", P5: the slot index on the grid and a device u64[m]
-// array of per-slot state pointers.)
+// aprender #5279, "Phase plan", phase P5: the slot index on the launch grid and one
+// 64-bit state address per slot in a device array.)
 //
 // Row r of the update only needs row r of S:
 //     a_r = S_r . k^,  p_r = S_r . q^,  u_r = beta (v_r - alpha a_r)

@@ -57,15 +57,15 @@ gdn_status check_dims(const gdn_dims* d, const char* fn) {
     return fail(GDN_ERR_DTYPE, "%s: unknown mma policy %d", fn, d->mma);
   if (d->prefill_form != GDN_PREFILL_AUTO && d->prefill_form != GDN_PREFILL_WHOLE &&
       d->prefill_form != GDN_PREFILL_SEGMENTS)
-    return fail(GDN_ERR_SHAPE, "%s: unknown prefill_form %d", fn, d->prefill_form);
+    return fail(GDN_ERR_DTYPE, "%s: unknown prefill_form %d", fn, d->prefill_form);
   if (d->out_dtype != GDN_F32 && d->out_dtype != GDN_BF16)
     return fail(GDN_ERR_DTYPE, "%s: unknown out_dtype %d", fn, d->out_dtype);
-  if (d->qk_l2norm != 0 && d->qk_l2norm != 1)
-    return fail(GDN_ERR_SHAPE, "%s: qk_l2norm must be 0 or 1 (got %d)", fn, d->qk_l2norm);
+  if (d->qk_l2norm_off != 0 && d->qk_l2norm_off != 1)
+    return fail(GDN_ERR_DTYPE, "%s: qk_l2norm_off must be 0 or 1 (got %d)", fn, d->qk_l2norm_off);
   if (!(d->l2_eps >= 0.0f) || !(d->l2_eps < 1e30f))
     return fail(GDN_ERR_SHAPE, "%s: l2_eps must be finite and >= 0", fn);
-  if (!(d->scale == d->scale) || d->scale > 1e30f || d->scale < -1e30f)
-    return fail(GDN_ERR_SHAPE, "%s: scale must be finite", fn);
+  if (!(d->scale == d->scale) || d->scale > 1e30f || d->scale < -1e30f || d->scale == 0.0f)
+    return fail(GDN_ERR_SHAPE, "%s: scale must be finite and nonzero (1.0 = no scaling)", fn);
   const int64_t C = static_cast<int64_t>(d->head_dim) * (2 * d->num_k_heads + d->num_v_heads);
   if (C > (1 << 24)) return fail(GDN_ERR_SHAPE, "%s: channel count %lld too large", fn, static_cast<long long>(C));
   return GDN_OK;
@@ -111,6 +111,27 @@ extern "C" {
 const char* gdn_last_error(void) { return g_last_error.c_str(); }
 
 int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+gdn_status gdn_dims_init(gdn_dims* dims, int32_t num_k_heads, int32_t num_v_heads, int32_t head_dim) {
+  if (!dims) return fail(GDN_ERR_NULL, "gdn_dims_init: dims is NULL");
+  gdn_dims d{};
+  d.struct_size = static_cast<int32_t>(sizeof(gdn_dims));
+  d.num_k_heads = num_k_heads;
+  d.num_v_heads = num_v_heads;
+  d.head_dim = head_dim;
+  d.conv_width = 4;
+  d.chunk_size = 64;
+  d.activation = GDN_ACT_NONE;
+  d.in_dtype = GDN_F32;
+  d.mma = GDN_MMA_AUTO;
+  d.l2_eps = 1e-6f;
+  d.scale = 1.0f;
+  d.prefill_form = GDN_PREFILL_AUTO;
+  d.out_dtype = GDN_F32;
+  d.qk_l2norm_off = 0;
+  *dims = d;
+  return GDN_OK;
+}
 
 gdn_status gdn_conv_update(const gdn_dims* dims, const void* x, int64_t x_stride, float* y, int64_t y_stride,
                            const void* conv_w, const void* conv_b, const int32_t* cu_seqlens,
@@ -182,7 +203,7 @@ gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_s
   gdn::PrefillArgs a{};
   a.r = gdn::RecurArgs{q, q_stride, k, k_stride, v, v_stride, g, beta, o, state_ptrs, dims->num_k_heads,
                        dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16, dims->qk_l2norm};
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0};
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
   a.total_tokens = total_tokens;
@@ -257,7 +278,7 @@ gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stri
   gdn::PrefillArgs a{};
   a.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, yv, vw, g, beta, o, state_ptrs, dims->num_k_heads,
                        dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16, dims->qk_l2norm};
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0};
   a.conv = gdn::ConvIn{x, x_stride, conv_w, conv_b, conv_state_ptrs, static_cast<int32_t>(C), K, silu, bf16};
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
@@ -283,7 +304,7 @@ gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_st
   if (gdn_status st = check_qkv(dims, fn, q, q_stride, k, k_stride, v, v_stride, g, beta, o, m)) return st;
   gdn::RecurArgs a{q, q_stride, k, k_stride, v, v_stride, g, beta, o, state_ptrs, dims->num_k_heads,
                    dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16, dims->qk_l2norm};
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0};
   return hip_status(gdn::launch_decode(a, m, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -322,7 +343,7 @@ gdn_status gdn_decode_fused(const gdn_dims* dims, const void* x, int64_t x_strid
   gdn::FusedArgs f{};
   f.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, nullptr, 0, g, beta, o, state_ptrs, dims->num_k_heads,
                        dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16, dims->qk_l2norm};
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0};
   f.x = x;
   f.x_stride = x_stride;
   f.w = conv_w;

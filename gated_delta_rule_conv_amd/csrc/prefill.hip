@@ -154,12 +154,16 @@ __device__ __forceinline__ int segment_len(int nc) {
   return k;
 }
 
+// The size covers every call with at most num_seqs sequences and total_tokens tokens:
+// each term grows with both, and under AUTO the segment maps are counted whenever some
+// call of this layer could take the chunk-parallel form (a single sequence would, i.e.
+// (d / 16) * Hv < 256), not only when a call of exactly num_seqs sequences would.
 size_t workspace_bytes(int hk, int hv, int d, int chunk, int num_seqs, int total_tokens, int form) {
   const size_t mc = max_chunks_of(chunk, num_seqs, total_tokens);
   size_t b = 256 + up256(mc * sizeof(int4)) + up256((static_cast<size_t>(num_seqs) + 1) * sizeof(int)) +
              up256(static_cast<size_t>(num_seqs) * sizeof(int) + 4) + up256(mc * hk * kq_stride(d, chunk)) +
              up256(mc * hv * tp_stride(chunk));
-  if (use_segments(hv, d, num_seqs, form)) {
+  if (use_segments(hv, d, form == 0 ? 1 : num_seqs, form)) {
     const size_t ns = max_segments_of(chunk, num_seqs, total_tokens);
     b += 256 + up256((static_cast<size_t>(num_seqs) + 1) * sizeof(int)) + up256(ns * sizeof(int4)) +
          3 * up256(ns * hv * static_cast<size_t>(d) * d * sizeof(float));

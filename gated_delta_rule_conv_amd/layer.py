@@ -1,10 +1,11 @@
 """Tensor-level helpers over the C ABI (argument marshalling only).
 
-``SlotPool`` is the caller-owned slot pool: one device allocation of fixed-size
-fp32 recurrent states and one of conv states, addressed per call through device
-u64 pointer arrays built on the device by gdn_slot_pointers ("qLLM", "What this
-is": a fixed-size recurrent-state / conv-buffer slot pool; aprender #5279,
-"Phase plan", P5: a device u64[m] array of per-slot state pointers).
+``SlotPool`` is the caller-owned slot pool: one device allocation of equal-sized
+fp32 recurrent-state blocks and one of conv-state blocks, addressed per call through
+device arrays of 64-bit block addresses that gdn_slot_pointers builds on the device.
+(The "qLLM" page, section "What this is", keeps the linear-attention layers' recurrent
+and conv state in such a pool of slots; aprender #5279, "Phase plan", phase P5, puts
+the slot index on the launch grid and hands the kernels one address per slot.)
 
 ``conv_update``, ``prefill``, ``decode`` and ``decode_fused`` derive pointers, strides and views from
 torch tensors and call the library; all arithmetic happens in the HIP kernels.

@@ -42,13 +42,14 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum gdn_status {
   GDN_OK = 0,
   GDN_ERR_NULL = 1,        /* a required pointer is NULL */
   GDN_ERR_SHAPE = 2,       /* a count, size or stride is out of range or inconsistent */
-  GDN_ERR_DTYPE = 3,       /* unknown dtype / activation / precision-policy value */
+  GDN_ERR_DTYPE = 3,       /* an enumerated field holds an unknown value (dtype, activation,
+                              precision policy, prefill form, or a 0/1 switch) */
   GDN_ERR_ALIGN = 4,       /* a pointer or stride breaks the 16-byte alignment rule */
   GDN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than gdn_prefill_workspace_size */
   GDN_ERR_UNSUPPORTED = 6, /* valid but not built: head dim, chunk size or conv width */
@@ -84,7 +85,12 @@ typedef enum gdn_mma { GDN_MMA_AUTO = 0, GDN_MMA_FP32 = 1, GDN_MMA_BF16X3 = 2 } 
 typedef enum gdn_prefill_form { GDN_PREFILL_AUTO = 0, GDN_PREFILL_WHOLE = 1, GDN_PREFILL_SEGMENTS = 2 } gdn_prefill_form;
 
 /* Layer dimensions and options, passed by pointer. struct_size must be
- * sizeof(gdn_dims) as compiled by the caller (lets the struct grow later). */
+ * sizeof(gdn_dims) as compiled by the caller (lets the struct grow later).
+ * Every enumerated field and switch reads 0 as its default, so a zero-filled struct
+ * (plus struct_size and the sizes) asks for the layer as defined: identity activation,
+ * fp32 input, the automatic precision policy and prefill form, fp32 output and the q/k
+ * L2 norm on. Only `scale` has no usable zero (it would zero every output) and is
+ * rejected there; gdn_dims_init() fills every field with its default. */
 typedef struct gdn_dims {
   int32_t struct_size;
   int32_t num_k_heads; /* Hk >= 1 (q and k heads) */
@@ -95,15 +101,24 @@ typedef struct gdn_dims {
   int32_t activation;  /* gdn_activation */
   int32_t in_dtype;    /* gdn_dtype of x, conv weight, conv bias and conv state */
   int32_t mma;         /* gdn_mma */
-  float l2_eps;        /* k^ = k / sqrt(|k|^2 + l2_eps); q^ likewise, then times scale */
-  float scale;         /* multiplies q^ (1.0 = no scaling) */
+  float l2_eps;        /* k^ = k / sqrt(|k|^2 + l2_eps); q^ likewise, then times scale; >= 0 */
+  float scale;         /* multiplies q^ (1.0 = no scaling); finite and nonzero */
   int32_t prefill_form; /* gdn_prefill_form */
   int32_t out_dtype;    /* gdn_dtype of o: GDN_F32, or GDN_BF16 = the fp32 result rounded to
                            nearest even (the conv output y is fp32 either way) */
-  int32_t qk_l2norm;    /* 1: q and k L2-normalised in the kernels (the layer's step 2);
-                           0: used as given (q still times scale). Set it explicitly: a
-                           zero-filled struct turns the normalisation off. */
+  int32_t qk_l2norm_off; /* 0 (default): q and k L2-normalised in the kernels (the layer's
+                            step 2); 1: used as the conv gives them (q still times scale) */
 } gdn_dims;
+
+/* ---------------------------------------------------------------------------------
+ * gdn_dims_init -- fill *dims with the given head counts and head dim and every other
+ * field at its default: struct_size = sizeof(gdn_dims), conv_width 4, chunk_size 64,
+ * GDN_ACT_NONE, in_dtype GDN_F32, GDN_MMA_AUTO, l2_eps 1e-6, scale 1.0,
+ * GDN_PREFILL_AUTO, out_dtype GDN_F32, qk_l2norm_off 0 (the enumerated fields as a
+ * zero-filled struct has them). Host only; checks nothing but dims != NULL (the entry
+ * points check the values).
+ */
+gdn_status gdn_dims_init(gdn_dims* dims, int32_t num_k_heads, int32_t num_v_heads, int32_t head_dim);
 
 /* Conv channel count C = 2*Hk*d + Hv*d, channels ordered [q heads | k heads | v heads]. */
 
@@ -214,8 +229,8 @@ gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stri
  * gdn_decode_batched -- one token for each of m slots: L2 norm + one step of the gated
  * delta rule on each slot's state, in place ("System Design", "GDN Kernel Dispatch
  * Detail", decode branch: decay the temporal state and write the delta, then
- * multiply the query by the state; aprender #5279, "Phase plan", P5: slot index on
- * the grid, device u64[m] array of per-slot state pointers).
+ * multiply the query by the state; aprender #5279, "Phase plan", phase P5: the
+ * slot index on the launch grid, one 64-bit state address per slot in a device array).
  *
  * Each slot's result is the same bits whatever m is and whatever other slots are in
  * the call: no reduction crosses slots and every reduction has a fixed order.
@@ -269,9 +284,10 @@ gdn_status gdn_decode_fused(const gdn_dims* dims, const void* x, int64_t x_strid
  * gdn_slot_pointers -- build a device u64 pointer array from slot indices, on the
  * device: out_ptrs[i] = pool_base + slot_idx[i] * slot_bytes, or 0 when slot_idx[i]
  * is outside [0, pool_slots) (an inactive slot). The slot pool is one caller-owned
- * allocation of pool_slots fixed-size blocks ("qLLM", section "What this is": a
- * fixed-size recurrent-state / conv-buffer slot pool; aprender #5279, "Phase plan",
- * P5: a device u64[m] array of per-layer state pointers).
+ * allocation of pool_slots equal-sized blocks (the "qLLM" page, section "What this is",
+ * holds the linear-attention layers' recurrent and conv state in a pool of slots;
+ * aprender #5279, "Phase plan", phase P5, gives each layer's kernels one address per
+ * slot in a device array).
  *
  *  pool_base  device address of slot 0 (16-byte aligned); slot_bytes: multiple of 16.
  *  slot_idx   device int32 [m].   out_ptrs: device u64 [m].

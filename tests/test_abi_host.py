@@ -34,7 +34,7 @@ def test_header_symbols_are_exported():
 
 
 def test_abi_version_and_struct_size():
-    assert gdn.gdn_abi_version() == 4
+    assert gdn.gdn_abi_version() == 5
     assert ctypes.sizeof(_lib.gdn_dims) == 14 * 4
 
 
@@ -59,14 +59,21 @@ def _status(fn, *args):
     (dict(num_k_heads=0), _lib.GDN_ERR_SHAPE),
     (dict(in_dtype=7), _lib.GDN_ERR_DTYPE),
     (dict(out_dtype=2), _lib.GDN_ERR_DTYPE),
-    (dict(qk_l2norm=2), _lib.GDN_ERR_SHAPE),
+    (dict(qk_l2norm_off=2), _lib.GDN_ERR_DTYPE),
     (dict(activation=3), _lib.GDN_ERR_DTYPE),
     (dict(mma=9), _lib.GDN_ERR_DTYPE),
     (dict(l2_eps=-1.0), _lib.GDN_ERR_SHAPE),
-    (dict(prefill_form=3), _lib.GDN_ERR_SHAPE),
+    (dict(scale=0.0), _lib.GDN_ERR_SHAPE),
+    (dict(scale=float("inf")), _lib.GDN_ERR_SHAPE),
+    (dict(prefill_form=3), _lib.GDN_ERR_DTYPE),
 ])
 def test_bad_dims_rejected_everywhere(kw, status):
+    """Every enumerated field or switch with an unknown value gives GDN_ERR_DTYPE; an
+    out-of-range number gives GDN_ERR_SHAPE; a size that is not built, _UNSUPPORTED."""
+    raw = {k: kw.pop(k) for k in list(kw) if k == "qk_l2norm_off"}
     d = dims(**kw)
+    for k, val in raw.items():
+        setattr(d, k, val)
     st, _ = _status(gdn.gdn_prefill_workspace_size, d, 1, 10)
     assert st == status
     st, _ = _status(gdn.gdn_decode_batched, d, FAKE, 4096, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, 4, 0)
@@ -214,15 +221,17 @@ def test_prefill_fused_workspace_and_checks():
 
 def test_prefill_form_workspace():
     """The chunk-parallel form needs room for per-segment state maps; AUTO takes it below
-    256 state-row workgroups ((d / 16) * Hv * num_seqs) and matches the explicit choice."""
+    256 state-row workgroups ((d / 16) * Hv * num_seqs), so its size counts the maps
+    whenever a single sequence would take that form."""
     few = dict(num_k_heads=2, num_v_heads=4)  # 8 * 4 = 32 workgroups per sequence
     whole = gdn.gdn_prefill_workspace_size(dims(**few, prefill_form=_lib.GDN_PREFILL_WHOLE), 1, 4096)
     segs = gdn.gdn_prefill_workspace_size(dims(**few, prefill_form=_lib.GDN_PREFILL_SEGMENTS), 1, 4096)
     auto = gdn.gdn_prefill_workspace_size(dims(**few), 1, 4096)
     assert segs > whole and auto == segs
-    # 8 sequences of 32 workgroups fill 256 CUs: AUTO keeps whole sequences
+    # 8 sequences of 32 workgroups fill 256 CUs, so such a call walks whole sequences, but
+    # the size for 8 sequences must also cover a call with one: the maps are counted
     assert gdn.gdn_prefill_workspace_size(dims(**few), 8, 4096) == \
-        gdn.gdn_prefill_workspace_size(dims(**few, prefill_form=_lib.GDN_PREFILL_WHOLE), 8, 4096)
+        gdn.gdn_prefill_workspace_size(dims(**few, prefill_form=_lib.GDN_PREFILL_SEGMENTS), 8, 4096)
     # the 16/32-head layer has 256 workgroups per sequence: whole sequences
     assert gdn.gdn_prefill_workspace_size(dims(), 1, 4096) == \
         gdn.gdn_prefill_workspace_size(dims(prefill_form=_lib.GDN_PREFILL_WHOLE), 1, 4096)
@@ -259,3 +268,86 @@ def test_slot_copy_checks():
     bad = gdn.make_dims(16, 30, 128)  # Hv % Hk != 0
     assert _status(gdn.gdn_slot_copy, bad, FAKE, FAKE, None, None, 4)[0] == _lib.GDN_ERR_SHAPE
     gdn.gdn_slot_copy(dims, FAKE, FAKE, FAKE, FAKE, 0)  # n = 0: nothing to do, nothing launched
+
+
+@pytest.mark.parametrize("form", [_lib.GDN_PREFILL_AUTO, _lib.GDN_PREFILL_WHOLE, _lib.GDN_PREFILL_SEGMENTS])
+@pytest.mark.parametrize("heads", [(2, 4, 128), (16, 32, 128), (1, 1, 32), (4, 8, 64), (16, 16, 64)])
+def test_workspace_size_covers_every_smaller_call(form, heads):
+    """A workspace sized for (N, T) is enough for every call with N' <= N sequences and
+    T' <= T tokens: the size each such call needs is at most the size for (N, T)."""
+    hk, hv, d = heads
+    dm = dims(num_k_heads=hk, num_v_heads=hv, head_dim=d, prefill_form=form)
+    for fn in (gdn.gdn_prefill_workspace_size, gdn.gdn_prefill_fused_workspace_size):
+        for N, T in [(8, 15717), (3, 4096), (64, 1000), (300, 20000)]:
+            big = fn(dm, N, T)
+            for n2 in sorted({1, 2, N // 2, N - 1, N}):
+                for t2 in sorted({n2, T // 3, T}):
+                    if n2 < 1 or t2 < n2:
+                        continue
+                    assert fn(dm, n2, t2) <= big, (fn.__name__, N, T, n2, t2)
+
+
+def test_dims_init_fills_defaults():
+    d = gdn.gdn_dims_init(16, 32, 128)
+    assert (d.struct_size, d.num_k_heads, d.num_v_heads, d.head_dim) == (ctypes.sizeof(_lib.gdn_dims), 16, 32, 128)
+    assert (d.conv_width, d.chunk_size, d.activation, d.in_dtype, d.mma) == (4, 64, 0, _lib.GDN_F32, 0)
+    assert (d.prefill_form, d.out_dtype, d.qk_l2norm_off) == (0, _lib.GDN_F32, 0)
+    assert d.scale == 1.0 and abs(d.l2_eps - 1e-6) < 1e-12
+    assert gdn.gdn_prefill_workspace_size(d, 1, 64) > 0  # accepted by the entry points
+    assert gdn.make_dims(16, 32, 128).qk_l2norm_off == 0
+    assert gdn.make_dims(16, 32, 128, qk_l2norm=False).qk_l2norm_off == 1
+
+
+_C99_PROBE = r"""
+#include <stdio.h>
+#include <string.h>
+#include "gdn.h"
+
+int main(void) {
+  gdn_dims z = {0};  /* zero-filled: every enumerated field at its default */
+  size_t bytes = 0;
+  gdn_dims d;
+  z.struct_size = (int32_t)sizeof z;
+  z.num_k_heads = 16;
+  z.num_v_heads = 32;
+  z.head_dim = 128;
+  z.conv_width = 4;
+  z.chunk_size = 64;
+  if (z.qk_l2norm_off != 0) return 10;  /* the q/k L2 norm is on */
+  /* scale has no usable zero: rejected instead of silently zeroing every output */
+  if (gdn_prefill_workspace_size(&z, 1, 64, &bytes) != GDN_ERR_SHAPE) return 11;
+  if (strstr(gdn_last_error(), "scale") == NULL) return 12;
+  z.scale = 1.0f;
+  if (gdn_prefill_workspace_size(&z, 1, 64, &bytes) != GDN_OK || bytes == 0) return 13;
+  if (gdn_dims_init(&d, 16, 32, 128) != GDN_OK) return 14;
+  if (d.struct_size != (int32_t)sizeof d || d.qk_l2norm_off != 0 || d.scale != 1.0f || d.conv_width != 4 ||
+      d.chunk_size != 64 || d.activation != GDN_ACT_NONE || d.mma != GDN_MMA_AUTO ||
+      d.prefill_form != GDN_PREFILL_AUTO || d.out_dtype != GDN_F32 || d.in_dtype != GDN_F32)
+    return 15;
+  if (gdn_dims_init(NULL, 1, 1, 32) != GDN_ERR_NULL) return 16;
+  if (gdn_abi_version() != GDN_ABI_VERSION) return 17;
+  printf("c99 ok\n");
+  return 0;
+}
+"""
+
+
+def test_header_compiles_as_c99_and_zero_filled_dims_normalise(tmp_path):
+    """include/gdn.h is plain C99 (no C++ in the declarations); a C caller that zero-fills
+    gdn_dims gets the q/k L2 norm on, and the library's host checks behave as declared."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "probe.c"
+    src.write_text(_C99_PROBE)
+    exe = tmp_path / "probe"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{os.path.join(ROOT, 'include')}",
+                        str(src), "-o", str(exe), f"-L{libdir}", "-lgdn", f"-Wl,-rpath,{libdir}"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "c99 ok" in r.stdout, (r.returncode, r.stdout, r.stderr)
