@@ -1,9 +1,10 @@
 """The decode step at its full size: 30 layers, each a 256-slot pool of 32 v-heads x
 128 x 128 fp32 states, m = 64 active slots through a shuffled pointer array, bf16
 inputs -- the launches a 30-GDN-layer hybrid makes per generated token. Every layer
-runs gdn_conv_update + gdn_decode_batched as the benchmark's step does; sampled
-(layer, slot) pairs are checked against the oracle, inactive slots for untouched bits,
-and two layers rerun through gdn_decode_fused for the same bits."""
+runs gdn_conv_update + gdn_decode_batched as the benchmark's step does; every one of the
+64 slots of three layers (first, middle, last) is checked against the oracle, inactive
+slots for untouched bits, and two layers rerun through gdn_decode_fused for the same
+bits."""
 
 import numpy as np
 import pytest
@@ -16,10 +17,10 @@ pytestmark = pytest.mark.gpu
 
 LAYERS, POOL, M = 30, 256, 64
 SAMPLE_LAYERS = (0, 13, 29)
-SAMPLE_ROWS = (0, 17, 40, 63)  # positions in the pointer array
+SAMPLE_ROWS = tuple(range(M))  # positions in the pointer array: all of them
 
 
-def test_decode_step_full_size_30_layers_sampled():
+def test_decode_step_full_size_30_layers_every_slot():
     import torch
 
     import gated_delta_rule_conv_amd as gdn

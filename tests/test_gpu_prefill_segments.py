@@ -28,10 +28,8 @@ def test_long_sequence_few_heads_matches_oracle():
     shape = LayerShape(2, 4, 128, conv_width=4, chunk=64, in_dtype="bf16")
     inp = make_prefill(PREFILL_L4096, lens=(4096,), shape=shape, s0_std=0.02, conv_state_std=1.0)
     o, S = PrefillRun(inp).run()
-    heads = [0, 3]
-    ref = _oracle(inp, v_heads=heads)
-    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16, heads=heads, label="segments L4096")
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    ref = _oracle(inp)
+    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16, label="segments L4096")
 
 
 @pytest.mark.parametrize("form", [0, 1])
@@ -59,15 +57,14 @@ def test_ragged_segments_match_oracle(d, chunk, mma, in_dtype, lens, form):
 
 def test_segments_forced_at_full_head_count():
     """The chunk-parallel form forced on the 16/32-head layer (where AUTO keeps whole
-    sequences): two sequences of 1000 and 2100 tokens against sampled oracle heads."""
+    sequences): two sequences of 1000 and 2100 tokens, every head against the oracle."""
     import gated_delta_rule_conv_amd as gdn
 
     announce("prefill segments forced, 16/32 heads")
     inp = make_prefill(PREFILL_L4096, lens=(1000, 2100), s0_std=0.02, conv_state_std=1.0)
     o, S = PrefillRun(inp, form=gdn.GDN_PREFILL_SEGMENTS).run()
-    heads = [2, 29]
-    ref = _oracle(inp, v_heads=heads)
-    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16, heads=heads, label="segments 16/32 heads")
+    ref = _oracle(inp)
+    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16, label="segments 16/32 heads")
 
 
 def test_segments_depend_on_the_sequence_only():
@@ -106,9 +103,8 @@ def test_slow_decay_few_heads_L4096(form):
     inp = make_prefill(PREFILL_L4096, lens=(4096,), shape=shape, s0_std=0.02, conv_state_std=1.0)
     g = (inp["g"] * SLOW).astype(np.float32)
     o, S = PrefillRun(inp, g=g, form=form).run()
-    heads = [1, 2]
-    ref = _oracle(inp, v_heads=heads, g=g)
-    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16, heads=heads, label=f"slow L4096 hk2 form={form}")
+    ref = _oracle(inp, g=g)
+    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16, label=f"slow L4096 hk2 form={form}")
 
 
 @pytest.mark.parametrize("form", [1, 2])
@@ -137,6 +133,5 @@ def test_slow_decay_full_heads_L4096(form):
     inp = make_prefill(PREFILL_L4096)
     g = (inp["g"] * SLOW).astype(np.float32)
     o, S = PrefillRun(inp, g=g, form=form).run()
-    heads = [7, 24]
-    ref = _oracle(inp, v_heads=heads, g=g)
-    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16, heads=heads, label=f"slow L4096 form={form}")
+    ref = _oracle(inp, g=g)
+    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16, label=f"slow L4096 form={form}")

@@ -144,3 +144,75 @@ def test_prefix_reuse_equals_one_long_prefill():
     np.testing.assert_array_equal(bits_of(pool.state[2]), bits_of(ref.state[1]))
     np.testing.assert_array_equal(bits_of(pool.conv_state[1]), bits_of(ref.conv_state[0]))
     np.testing.assert_array_equal(bits_of(pool.conv_state[2]), bits_of(ref.conv_state[1]))
+
+
+def test_reused_slot_equals_never_used_slot():
+    """A slot that served one sequence, was freed and re-zeroed, then serves a new one,
+    gives the same bits as a slot never used: nothing of the old sequence survives the
+    reset ("qLLM", "Results": no decode-time contamination when slots are reused). The
+    new sequence runs in both slots through prefill and then decode, both entry points."""
+    import torch
+
+    import gated_delta_rule_conv_amd as gdn
+
+    announce("slot reuse: freed + re-zeroed slot == never-used slot")
+    shape = LayerShape(4, 8, 128, conv_width=4, chunk=64, in_dtype="bf16")
+    dims = _dims(shape)
+    C, Hv, d = shape.channels, shape.num_v_heads, shape.head_dim
+    old = make_prefill(RAGGED_T15717, lens=(150,), shape=shape, s0_std=0.0, conv_state_std=0.0)
+    new = make_prefill(PREFILL_L4096, lens=(90,), shape=shape, s0_std=0.0, conv_state_std=0.0)
+    conv_w = to_dev(new["conv_w"], "bf16")
+    pool = gdn.SlotPool(dims, 4)  # zero states: fresh slots
+    counters = gdn.decode_counters(dims, 2)
+
+    def prefill(slots, inp):
+        T = inp["x"].shape[0]
+        n = len(slots)
+        sp, cp = pool.pointers(torch.tensor(slots, dtype=torch.int32, device="cuda"))
+        cu = torch.tensor([i * T for i in range(n + 1)], dtype=torch.int32, device="cuda")
+        x = to_dev(np.concatenate([inp["x"]] * n), "bf16")
+        g = to_dev(np.concatenate([inp["g"]] * n), "f32")
+        beta = to_dev(np.concatenate([inp["beta"]] * n), "f32")
+        y = torch.empty((n * T, C), dtype=torch.float32, device="cuda")
+        o = torch.empty((n * T, Hv, d), dtype=torch.float32, device="cuda")
+        gdn.conv_update(dims, x, y, conv_w, None, cp, cu)
+        gdn.prefill(dims, y, g, beta, o, cu, sp, gdn.prefill_workspace(dims, n, n * T))
+        return o
+
+    def decode(slots, step, fused):
+        inp = make_decode_step(DECODE_M16_POOL64, 40 + step, 1, shape=shape)
+        n = len(slots)
+        sp, cp = pool.pointers(torch.tensor(slots, dtype=torch.int32, device="cuda"))
+        x = to_dev(inp["x"], "bf16").repeat(n, 1)
+        g = to_dev(inp["g"], "f32").repeat(n, 1)
+        beta = to_dev(inp["beta"], "f32").repeat(n, 1)
+        o = torch.empty((n, Hv, d), dtype=torch.float32, device="cuda")
+        if fused:
+            gdn.decode_fused(dims, x, conv_w, None, g, beta, o, sp, cp, counters)
+        else:
+            y = torch.empty((n, C), dtype=torch.float32, device="cuda")
+            gdn.conv_update(dims, x, y, conv_w, None, cp)
+            gdn.decode(dims, y, g, beta, o, sp)
+        return o
+
+    # slot 1 serves an old sequence (prefill and three decode steps), then is freed
+    prefill([1], old)
+    for step in range(3):
+        decode([1], step, fused=step % 2 == 1)
+    torch.cuda.synchronize()
+    assert pool.state[1].abs().max().item() > 0 and pool.conv_state[1].float().abs().max().item() > 0
+    pool.state[1].zero_()
+    pool.conv_state[1].zero_()
+    # the new sequence in the reused slot 1 and in the never-used slot 3, side by side
+    o = prefill([1, 3], new)
+    T = new["x"].shape[0]
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits_of(o[:T]), bits_of(o[T:]))
+    for step in range(4):
+        od = decode([1, 3], 10 + step, fused=step >= 2)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits_of(od[0]), bits_of(od[1]), err_msg=f"decode step {step}")
+    np.testing.assert_array_equal(bits_of(pool.state[1]), bits_of(pool.state[3]))
+    np.testing.assert_array_equal(bits_of(pool.conv_state[1]), bits_of(pool.conv_state[3]))
+    # slots 0 and 2 were never touched
+    assert pool.state[[0, 2]].abs().max().item() == 0 and pool.conv_state[[0, 2]].float().abs().max().item() == 0
