@@ -2,12 +2,15 @@
 """Benchmark of the Gated DeltaNet layer core on one MI355X.
 
 One step = one pass of the whole hot path:
-  * decode: a 30-layer decode step at m slots (default 64) of a 256-slot pool, each
-    layer = gdn_conv_update (decode mode) + gdn_decode_batched over 32 v-heads x
-    128x128 fp32 states addressed through per-layer device u64 pointer arrays. The
-    step is captured once in a HIP graph and replayed (the serving-loop form); the
-    eager (one ctypes call per launch) step is timed too, and so is the same step as
-    one gdn_decode_fused call per layer (conv + commit + norm + delta rule);
+  * decode: a 30-layer decode step at m slots (default 64) of a 256-slot pool, over 32
+    v-heads x 128x128 fp32 states addressed through per-layer device u64 pointer arrays.
+    Three forms of a layer are timed, each captured in a HIP graph and replayed (the
+    serving-loop form), and eagerly (one ctypes call per launch):
+      - fused_stream (the headline): one gdn_decode_fused call per layer (conv, conv-state
+        commit, q/k L2 norm, delta rule), the conv states read from one pool and written to
+        a second, the two pools alternating from step to step (one replay = two steps);
+      - fused: the same call with the conv states updated in place;
+      - two_calls: gdn_conv_update (decode mode) + gdn_decode_batched;
   * prefill: one 4096-token sequence (16 q/k heads, 32 v-heads, d = 128, bf16 input,
     chunk 64) = gdn_conv_update (prefill mode) + gdn_prefill_chunked, and the same as one
     gdn_prefill_fused call. The 8-sequence ragged pack (T = 15717) and one GPU's share
@@ -15,15 +18,17 @@ One step = one pass of the whole hot path:
 Inputs are seeded synthetic data already resident in HBM when timing starts.
 
 `value` is the decode state bandwidth: 30 * m * 4 MiB (each slot-layer reads and writes
-its 2 MiB state once) over the graph-replayed decode step. Prefill is reported as
+its 2 MiB state once) over the graph-replayed fused_stream step. Prefill is reported as
 tokens/s (eager calls, and the same calls replayed from a HIP graph) and as algorithmic
-TFLOP/s against the bf16 MFMA peak. `roofline` is for the
-dominant kernel (the decode kernel), whose average launch time is measured with HIP
+TFLOP/s against the bf16 MFMA peak. `roofline` is for the dominant kernel (the fused
+decode kernel of the headline step), whose average launch time is measured with HIP
 events around back-to-back launches on the stream it runs on. `ceilings` are this GPU's
-measured practical rates (a 4 GiB device copy, a bf16 8192^3 matmul), next to which the
-decode and prefill rates are also stated. `cpu_baseline` times the fp64 oracle on a
-bounded sample of the same decode workload on one host thread (`cpu_baseline_all_cores`:
-one single-threaded process per usable core, at most 16).
+measured practical rates: the library's in-place streaming pass (gdn_hbm_probe) over
+4 GiB, in one launch and as 32 launches of 128 MiB (the decode step's shape; the better
+of the two is the practical HBM ceiling), a torch device copy of 4 GiB and a bf16
+8192^3 matmul. `cpu_baseline` times the
+fp64 oracle on a bounded sample of the same decode workload on one host thread
+(`cpu_baseline_all_cores`: one single-threaded process per usable core, at most 16).
 """
 
 from __future__ import annotations
@@ -48,23 +53,34 @@ FUSED_BYTES_PER_SLOT_LAYER = STATE_BYTES_PER_SLOT_LAYER + 2 * 3 * 8192 * 2 + 819
 CONV_TAP_BYTES = 8192 * 4 * 2
 
 
-def measured_traffic():
-    """HBM bytes per decode-kernel launch (m = 64) from the committed counter summary, or
-    None when csrc/decode.hip has changed since those counters were taken."""
+def source_key(path: str) -> str:
+    """sha256 of a source file with its comments and whitespace removed: the key under
+    which counter figures are filed, unchanged by an edit to comments or layout."""
     import hashlib
+    import re
 
-    prof = os.path.join(ROOT, "profiles", "hbm_counters_decode_kernel_m64.md")
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline step's fused decode kernel (m = 64) from the
+    committed counter summary, or None when csrc/decode.hip's code has changed since those
+    counters were taken (its comment-free key differs from the one recorded there)."""
+    prof = os.path.join(ROOT, "profiles", "hbm_counters_decode_kernels_m64.md")
     src = os.path.join(ROOT, "gated_delta_rule_conv_amd", "csrc", "decode.hip")
     try:
         fields = {}
         with open(prof) as f:
             for line in f:
-                if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_launch", "decode_source_sha256"):
+                if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_launch", "decode_source_key"):
                     k, v = line.split(":", 1)
                     fields[k] = v.strip()
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if fields.get("decode_source_sha256") != sha:
+        if fields.get("decode_source_key") != source_key(src):
             return None
         return int(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -81,19 +97,23 @@ def ev():
     return torch.cuda.Event(enable_timing=True)
 
 
-class DecodeRig:
-    """30 layers of slot pools (256 slots each) and m active slots per layer."""
+FORMS = ("fused_stream", "fused", "two_calls")
 
-    def __init__(self, m: int, layers: int = 30, pool: int = 256, n_inputs: int = 8, device="cuda",
-                 fused: bool = False):
+
+class DecodeRig:
+    """30 layers of slot pools (256 slots each) and m active slots per layer, stepped in
+    one of the FORMS."""
+
+    def __init__(self, m: int, form: str, layers: int = 30, pool: int = 256, n_inputs: int = 8, device="cuda"):
         import numpy as np
         import torch
 
         import gated_delta_rule_conv_amd as gdn
         from gen.inputs import DECODE_30_LAYERS, ST_PERM, WORKLOADS, make_decode_pool_torch, rng_for
 
+        assert form in FORMS
         sh = WORKLOADS[DECODE_30_LAYERS].shape
-        self.m, self.layers, self.sh = m, layers, sh
+        self.m, self.layers, self.sh, self.form = m, layers, sh, form
         self.dims = gdn.make_dims(sh.num_k_heads, sh.num_v_heads, sh.head_dim, conv_width=sh.conv_width,
                                   chunk_size=sh.chunk, in_dtype=gdn.GDN_BF16)
         self.states, self.conv_states, self.conv_w = make_decode_pool_torch(DECODE_30_LAYERS, pool, layers, device)
@@ -106,6 +126,13 @@ class DecodeRig:
         for layer in range(layers):
             gdn.gdn_slot_pointers(self.states[layer].data_ptr(), s_bytes, pool, idx, m, self.sptr[layer])
             gdn.gdn_slot_pointers(self.conv_states[layer].data_ptr(), c_bytes, pool, idx, m, self.cptr[layer])
+        if form == "fused_stream":
+            # the second conv pool: step n reads pool n % 2 and writes the other
+            self.conv_states2 = self.conv_states.clone()
+            self.cptr2 = torch.empty((layers, m), dtype=torch.int64, device=device)
+            for layer in range(layers):
+                gdn.gdn_slot_pointers(self.conv_states2[layer].data_ptr(), c_bytes, pool, idx, m, self.cptr2[layer])
+        self.direction = 0
         gen = torch.Generator(device=device)
         gen.manual_seed(3100 + m)
         C, Hv = sh.channels, sh.num_v_heads
@@ -116,49 +143,53 @@ class DecodeRig:
         self.y = torch.empty((m, C), dtype=torch.float32, device=device)
         self.o = torch.empty((m, Hv, sh.head_dim), dtype=torch.float32, device=device)
         self.q, self.k, self.v = gdn.qkv_views(self.dims, self.y)
-        self.fused = fused
-        self.counters = gdn.decode_counters(self.dims, m, device=device)
         self.graph = None
+        self.steps_per_replay = 2 if form == "fused_stream" else 1
+
+    def kernel(self, layer: int, s: int) -> None:
+        """The launch whose time is the roofline's: the fused kernel, or the decode kernel
+        of the two-call form."""
+        import gated_delta_rule_conv_amd as gdn
+
+        if self.form == "two_calls":
+            q, k, v = self.q, self.k, self.v
+            gdn.gdn_decode_batched(self.dims, q, q.stride(0), k, k.stride(0), v, v.stride(0), self.g[s],
+                                   self.beta[s], self.o, self.sptr[layer], self.m)
+            return
+        cin, cout = self.cptr[layer], None
+        if self.form == "fused_stream":
+            cin, cout = (self.cptr[layer], self.cptr2[layer]) if self.direction == 0 else \
+                (self.cptr2[layer], self.cptr[layer])
+        gdn.decode_fused(self.dims, self.x[s], self.conv_w[layer], None, self.g[s], self.beta[s], self.o,
+                         self.sptr[layer], cin, cout)
 
     def layer(self, layer: int, s: int) -> None:
         import gated_delta_rule_conv_amd as gdn
 
-        if self.fused:
-            self.fused_only(layer, s)
-            return
-        gdn.conv_update(self.dims, self.x[s], self.y, self.conv_w[layer], None, self.cptr[layer])
-        self.decode_only(layer, s)
-
-    def fused_only(self, layer: int, s: int) -> None:
-        import gated_delta_rule_conv_amd as gdn
-
-        gdn.decode_fused(self.dims, self.x[s], self.conv_w[layer], None, self.g[s], self.beta[s], self.o,
-                         self.sptr[layer], self.cptr[layer], self.counters)
-
-    def decode_only(self, layer: int, s: int) -> None:
-        import gated_delta_rule_conv_amd as gdn
-
-        q, k, v = self.q, self.k, self.v
-        gdn.gdn_decode_batched(self.dims, q, q.stride(0), k, k.stride(0), v, v.stride(0), self.g[s], self.beta[s],
-                               self.o, self.sptr[layer], self.m)
+        if self.form == "two_calls":
+            gdn.conv_update(self.dims, self.x[s], self.y, self.conv_w[layer], None, self.cptr[layer])
+        self.kernel(layer, s)
 
     def step(self) -> None:
         for layer in range(self.layers):
             self.layer(layer, layer % self.n_inputs)
+        self.direction ^= 1
 
     def capture(self) -> None:
-        """Capture one whole step (30 layers) in a HIP graph."""
+        """Capture steps_per_replay whole steps (30 layers each) in one HIP graph."""
         import torch
 
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            self.step()
+            for _ in range(self.steps_per_replay):
+                self.step()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
-            self.step()
+            for _ in range(self.steps_per_replay):
+                self.step()
         torch.cuda.synchronize()
 
     def replay(self) -> None:
@@ -333,26 +364,58 @@ def cpu_baseline_pool(seconds: float) -> dict:
 
 
 def ceilings() -> dict:
-    """Measured practical ceilings of this GPU: a device-to-device copy of 4 GiB (read +
-    write bytes over time) and a bf16 8192 x 8192 x 8192 matmul; medians of 5."""
+    """Measured practical ceilings of this GPU, medians of 5: the library's in-place
+    streaming pass (gdn_hbm_probe: the decode kernel's state access pattern without its
+    arithmetic) over 4 GiB, a torch device-to-device copy of 4 GiB (read + write bytes over
+    time) and a bf16 8192 x 8192 x 8192 matmul."""
     import statistics
 
     import torch
 
+    import gated_delta_rule_conv_amd as gdn
+
     out = {}
-    src = torch.empty(1 << 30, dtype=torch.float32, device="cuda").fill_(1.0)  # 4 GiB
-    dst = torch.empty_like(src)
-    dst.copy_(src)
+    buf = torch.empty(1 << 30, dtype=torch.float32, device="cuda").fill_(1.0)  # 4 GiB
+    nbytes = buf.numel() * 4
+    gdn.gdn_hbm_probe(buf, nbytes)
     ts = []
     for _ in range(5):
         a, b = ev(), ev()
         a.record()
-        dst.copy_(src)
+        gdn.gdn_hbm_probe(buf, nbytes)
         b.record()
         torch.cuda.synchronize()
         ts.append(a.elapsed_time(b))
-    out["d2d_copy_4GiB_GBps"] = round(2 * src.numel() * 4 / (statistics.median(ts) * 1e-3) / 1e9, 1)
-    del src, dst
+    out["inplace_stream_4GiB_GBps"] = round(2 * nbytes / (statistics.median(ts) * 1e-3) / 1e9, 1)
+    # the same 4 GiB as 32 back-to-back launches of 128 MiB each: the decode step's shape
+    # (30 launches, each streaming 64 slots x 2 MiB = 128 MiB in place) without its
+    # arithmetic, over a footprint the 256 MB Infinity Cache cannot hold
+    chunk = 128 << 20
+    base = buf.data_ptr()
+    ts = []
+    for _ in range(5):
+        a, b = ev(), ev()
+        a.record()
+        for c in range(nbytes // chunk):
+            gdn.gdn_hbm_probe(base + c * chunk, chunk, 0, torch.cuda.current_stream().cuda_stream)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    out["inplace_stream_32x128MiB_GBps"] = round(2 * nbytes / (statistics.median(ts) * 1e-3) / 1e9, 1)
+    # the practical HBM ceiling: the better of the two streaming rates
+    out["practical_hbm_GBps"] = max(out["inplace_stream_4GiB_GBps"], out["inplace_stream_32x128MiB_GBps"])
+    dst = torch.empty_like(buf)
+    dst.copy_(buf)
+    ts = []
+    for _ in range(5):
+        a, b = ev(), ev()
+        a.record()
+        dst.copy_(buf)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    out["d2d_copy_4GiB_GBps"] = round(2 * nbytes / (statistics.median(ts) * 1e-3) / 1e9, 1)
+    del buf, dst
     torch.cuda.empty_cache()
     n = 8192
     x = torch.randn(n, n, device="cuda").to(torch.bfloat16)
@@ -373,7 +436,7 @@ def ceilings() -> dict:
 
 
 def time_graph_scrubbed(rig: DecodeRig, steps: int, scrub) -> float:
-    """Median ms of single graph-replayed decode steps, each after a 1 GiB write that
+    """Median ms per decode step of single graph replays, each after a 1 GiB write that
     evicts the states from the GPU's caches (the write is outside the timed region)."""
     import statistics
 
@@ -387,12 +450,13 @@ def time_graph_scrubbed(rig: DecodeRig, steps: int, scrub) -> float:
         rig.replay()
         b.record()
         torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
+        ts.append(a.elapsed_time(b) / rig.steps_per_replay)
     return statistics.median(ts)
 
 
 def time_graph(rig: DecodeRig, steps: int, warmup: int) -> float:
-    """Mean ms per graph-replayed decode step."""
+    """Mean ms per decode step over `steps` graph replays (a replay holds
+    rig.steps_per_replay steps)."""
     import torch
 
     for _ in range(warmup):
@@ -404,22 +468,22 @@ def time_graph(rig: DecodeRig, steps: int, warmup: int) -> float:
         rig.replay()
     b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / steps
+    return a.elapsed_time(b) / (steps * rig.steps_per_replay)
 
 
 def time_decode_kernel(rig: DecodeRig, rounds: int) -> float:
-    """Mean us per launch of the rig's decode kernel (fused, or the plain decode kernel
-    of the two-call form): the 30 layers' launches back to back (no conv launches in
-    between), `rounds` times, events on the launching stream."""
+    """Mean us per launch of the rig's roofline kernel (rig.kernel: the fused kernel, or
+    the decode kernel of the two-call form): the 30 layers' launches back to back (no conv
+    launches in between), `rounds` times, events on the launching stream."""
     import torch
 
-    one = rig.fused_only if rig.fused else rig.decode_only
     a, b = ev(), ev()
     torch.cuda.synchronize()
     a.record()
     for _ in range(rounds):
         for layer in range(rig.layers):
-            one(layer, layer % rig.n_inputs)
+            rig.kernel(layer, layer % rig.n_inputs)
+        rig.direction ^= 1
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e3 / (rounds * rig.layers)
@@ -473,8 +537,8 @@ def main() -> int:
     K, W = args.steps, args.warmup
 
     # ---------------------------------------------------------------- decode, m = 64
-    def run_decode(fused: bool):
-        rig = DecodeRig(args.m, fused=fused)
+    def run_decode(form: str):
+        rig = DecodeRig(args.m, form)
         for _ in range(W):
             rig.step()
         torch.cuda.synchronize()
@@ -490,19 +554,43 @@ def main() -> int:
         graph_ms = time_graph(rig, K, W)
         wall = time.perf_counter() - t_start
         kern_us = time_decode_kernel(rig, max(2, K // 4))
-        log(f"decode ({'fused' if fused else 'conv + decode'}): eager {eager_ms:.3f} ms/step, graph "
-            f"{graph_ms:.3f} ms/step, kernel {kern_us:.2f} us")
+        log(f"decode {form}: eager {eager_ms:.3f} ms/step, graph {graph_ms:.3f} ms/step, kernel {kern_us:.2f} us")
         del rig
         torch.cuda.empty_cache()
-        return eager_ms, graph_ms, wall, kern_us
+        return {"eager_ms": eager_ms, "graph_ms": graph_ms, "wall": wall, "kernel_us": kern_us}
 
-    eager_ms, graph_ms, wall, kern_us = run_decode(False)
-    f_eager_ms, f_graph_ms, _, f_kern_us = run_decode(True)
+    runs = {form: run_decode(form) for form in FORMS}
     state_bytes_step = 30 * args.m * STATE_BYTES_PER_SLOT_LAYER
+    head = runs["fused_stream"]
+    graph_ms = head["graph_ms"]
     value = state_bytes_step / (graph_ms * 1e-3) / 1e9
-    bytes_per_launch = args.m * STATE_BYTES_PER_SLOT_LAYER
+    # algorithmic bytes of one fused launch: the state, the conv state (read from one pool,
+    # written to another), x, o, g and beta of every slot-layer, and the taps once
+    bytes_per_launch = args.m * FUSED_BYTES_PER_SLOT_LAYER + CONV_TAP_BYTES
+    kern_us = head["kernel_us"]
     achieved = bytes_per_launch / (kern_us * 1e-6) / 1e9
-    f_bytes_per_launch = args.m * FUSED_BYTES_PER_SLOT_LAYER + CONV_TAP_BYTES
+    plain_bytes = args.m * STATE_BYTES_PER_SLOT_LAYER
+
+    def form_row(form, note):
+        r = runs[form]
+        row = {"note": note, "graph_ms_per_step": round(r["graph_ms"], 4), "eager_ms_per_step": round(r["eager_ms"], 4),
+               "state_GBps_graph": round(state_bytes_step / (r["graph_ms"] * 1e-3) / 1e9, 2),
+               "state_GBps_eager": round(state_bytes_step / (r["eager_ms"] * 1e-3) / 1e9, 2),
+               "frac_of_hbm_peak": round(state_bytes_step / (r["graph_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if form == "two_calls":
+            row["decode_kernel_us"] = round(r["kernel_us"], 2)
+            row["decode_kernel_GBps"] = round(plain_bytes / (r["kernel_us"] * 1e-6) / 1e9, 2)
+        else:
+            row["fused_kernel_us"] = round(r["kernel_us"], 2)
+            row["fused_kernel_GBps"] = round(bytes_per_launch / (r["kernel_us"] * 1e-6) / 1e9, 2)
+        return row
+
+    decode_forms = {
+        "fused_stream": form_row("fused_stream", "one gdn_decode_fused call per layer, conv states read from one "
+                                                 "pool and written to another (alternating every step)"),
+        "fused": form_row("fused", "one gdn_decode_fused call per layer, conv states updated in place"),
+        "two_calls": form_row("two_calls", "gdn_conv_update (decode mode) + gdn_decode_batched per layer"),
+    }
 
     sweep = None
     if not args.no_sweep:
@@ -510,22 +598,19 @@ def main() -> int:
         scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
         for mm in (1, 4, 16):
             row = {}
-            for fused in (False, True):
-                r = DecodeRig(mm, fused=fused)
+            for form in FORMS:
+                r = DecodeRig(mm, form)
                 for _ in range(2):
                     r.step()
                 r.capture()
                 ms = time_graph(r, K, W)
-                kus = time_decode_kernel(r, max(2, K // 4))
-                tag = "fused_" if fused else ""
-                row[tag + "ms_per_step"] = round(ms, 4)
-                row[tag + "state_GBps"] = round(r.layers * mm * STATE_BYTES_PER_SLOT_LAYER / ms / 1e6, 1)
-                row[tag + "decode_kernel_us"] = round(kus, 2)
+                row[form + "_ms_per_step"] = round(ms, 4)
+                row[form + "_state_GBps"] = round(r.layers * mm * STATE_BYTES_PER_SLOT_LAYER / ms / 1e6, 1)
                 if mm * 60 < 256:  # state footprint fits the Infinity Cache: also from cold caches
                     sms = time_graph_scrubbed(r, max(5, K // 2), scrub)
-                    row[tag + "scrubbed_ms_per_step"] = round(sms, 4)
-                    row[tag + "scrubbed_state_GBps"] = round(r.layers * mm * STATE_BYTES_PER_SLOT_LAYER / sms / 1e6,
-                                                             1)
+                    row[form + "_scrubbed_ms_per_step"] = round(sms, 4)
+                    row[form + "_scrubbed_state_GBps"] = round(
+                        r.layers * mm * STATE_BYTES_PER_SLOT_LAYER / sms / 1e6, 1)
                 del r
                 torch.cuda.empty_cache()
             row["note"] = (("state footprint (%d MiB over 30 layers) fits the 256 MB Infinity Cache" % (mm * 60))
@@ -607,6 +692,7 @@ def main() -> int:
         for row in prefill.values():
             row["frac_of_measured_bf16_matmul"] = round(row["algorithmic_TFLOPs"] / ceil["bf16_matmul_8192_TFLOPs"],
                                                         5)
+    stream_ceiling = ceil["practical_hbm_GBps"] if ceil else None
     out = {
         "metric": "GDN decode state GB/s (m=64) + prefill tokens/s; % of HBM / MFMA peak",
         "value": round(value, 2),
@@ -624,37 +710,31 @@ def main() -> int:
             "workload": f"decode step of a 30-GDN-layer hybrid: m={args.m} active slots of a 256-slot pool per "
                         f"layer, 32 v-heads / 16 k-heads, d=128, fp32 128x128 state per head, bf16 conv input "
                         f"(8192 channels, conv width 4), random per-slot state pointers; step = 30 x "
-                        f"(gdn_conv_update + gdn_decode_batched) replayed as one HIP graph",
+                        f"gdn_decode_fused (conv + conv-state commit + q/k L2 norm + delta rule), the conv states "
+                        f"alternating between two pools, replayed as a HIP graph",
             "m": args.m, "layers": 30, "pool_slots": 256, "num_v_heads": 32, "num_k_heads": 16,
             "head_dim": 128, "parallelism": "none (1 GPU)",
         },
-        "decode": {"graph_ms_per_step": round(graph_ms, 4), "eager_ms_per_step": round(eager_ms, 4),
-                   "state_GBps_graph": round(value, 2),
-                   "state_GBps_eager": round(state_bytes_step / (eager_ms * 1e-3) / 1e9, 2),
-                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-                   "frac_of_measured_copy": round(value / ceil["d2d_copy_4GiB_GBps"], 4) if ceil else None,
-                   "decode_kernel_us": round(kern_us, 2)},
-        "decode_fused": {"note": "the same step as one gdn_decode_fused call per layer",
-                         "graph_ms_per_step": round(f_graph_ms, 4),
-                         "eager_ms_per_step": round(f_eager_ms, 4),
-                         "state_GBps_graph": round(state_bytes_step / (f_graph_ms * 1e-3) / 1e9, 2),
-                         "fused_kernel_us": round(f_kern_us, 2),
-                         "fused_kernel_bytes_per_launch": f_bytes_per_launch,
-                         "fused_kernel_GBps": round(f_bytes_per_launch / (f_kern_us * 1e-6) / 1e9, 2)},
+        "decode": {"graph_ms_per_step": round(graph_ms, 4), "eager_ms_per_step": round(head["eager_ms"], 4),
+                   "state_GBps_graph": round(value, 2), "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                   "frac_of_measured_stream_ceiling": round(value / stream_ceiling, 4) if ceil else None},
+        "decode_forms": decode_forms,
         "decode_sweep": sweep,
         "prefill": prefill,
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,1,false,0>", "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "fused_stream_kernel<bf16, K=4, d=128, P=1> (gdn_decode_fused, "
+                                               "m=64)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.m == 64 else None,
                      "bytes_per_launch": bytes_per_launch,
                      "avg_launch_us": round(kern_us, 2),
-                     "measured_ceiling_GBps": ceil["d2d_copy_4GiB_GBps"] if ceil else None,
-                     "frac_of_measured_ceiling": round(achieved / ceil["d2d_copy_4GiB_GBps"], 4) if ceil else None},
+                     "measured_ceiling_GBps": stream_ceiling,
+                     "frac_of_measured_ceiling": round(achieved / stream_ceiling, 4) if ceil else None},
         "ceilings": ceil,
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_pool,
         "host_cpu": host_cpu(),
-        "wall_s": round(wall, 3),
+        "wall_s": round(head["wall"], 3),
     }
     print(json.dumps(out), flush=True)
     return 0

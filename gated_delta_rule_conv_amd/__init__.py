@@ -24,9 +24,9 @@ from ._lib import (  # noqa: F401
     gdn_conv_update,
     gdn_decode_batched,
     gdn_decode_fused,
-    gdn_decode_fused_workspace_size,
     gdn_dims,
     gdn_dims_init,
+    gdn_hbm_probe,
     gdn_last_error,
     gdn_prefill_chunked,
     gdn_prefill_fused,
@@ -41,7 +41,6 @@ from .layer import (  # noqa: F401
     channels,
     conv_update,
     decode,
-    decode_counters,
     decode_fused,
     prefill,
     prefill_fused,

@@ -23,9 +23,9 @@ GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 GDN_MMA_AUTO, GDN_MMA_FP32, GDN_MMA_BF16X3 = 0, 1, 2
 GDN_PREFILL_AUTO, GDN_PREFILL_WHOLE, GDN_PREFILL_SEGMENTS = 0, 1, 2
 
-EXPORTED = ("gdn_dims_init", "gdn_conv_update", "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_fused_workspace_size",
-            "gdn_prefill_fused", "gdn_decode_batched", "gdn_decode_fused_workspace_size", "gdn_decode_fused",
-            "gdn_slot_copy", "gdn_slot_pointers", "gdn_last_error", "gdn_abi_version")
+EXPORTED = ("gdn_dims_init", "gdn_conv_update", "gdn_prefill_workspace_size", "gdn_prefill_chunked",
+            "gdn_prefill_fused_workspace_size", "gdn_prefill_fused", "gdn_decode_batched", "gdn_decode_fused",
+            "gdn_slot_copy", "gdn_slot_pointers", "gdn_last_error", "gdn_abi_version", "gdn_hbm_probe")
 
 
 class gdn_dims(ctypes.Structure):
@@ -95,14 +95,15 @@ def _load() -> ctypes.CDLL:
     lib.gdn_prefill_fused_workspace_size.argtypes = [D, I32, I32, ctypes.POINTER(SZ)]
     lib.gdn_prefill_fused.argtypes = [D, P, I64, P, P, P, P, P, P, I32, I32, P, P, P, SZ, P]
     lib.gdn_decode_batched.argtypes = [D, P, I64, P, I64, P, I64, P, P, P, P, I32, P]
-    lib.gdn_decode_fused_workspace_size.argtypes = [D, I32, ctypes.POINTER(SZ)]
-    lib.gdn_decode_fused.argtypes = [D, P, I64, P, P, P, P, P, P, P, I32, P, SZ, P]
+    lib.gdn_decode_fused.argtypes = [D, P, I64, P, P, P, P, P, P, P, P, I32, P]
     lib.gdn_slot_copy.argtypes = [D, P, P, P, P, I32, P]
     lib.gdn_slot_pointers.argtypes = [U64, I64, I32, P, I32, P, P]
     for fn in ("gdn_dims_init", "gdn_conv_update", "gdn_prefill_workspace_size", "gdn_prefill_chunked",
                "gdn_prefill_fused_workspace_size", "gdn_prefill_fused", "gdn_decode_batched",
-               "gdn_decode_fused_workspace_size", "gdn_decode_fused", "gdn_slot_copy", "gdn_slot_pointers"):
+               "gdn_decode_fused", "gdn_slot_copy", "gdn_slot_pointers"):
         getattr(lib, fn).restype = ctypes.c_int
+    lib.gdn_hbm_probe.argtypes = [P, SZ, ctypes.c_uint32, P]
+    lib.gdn_hbm_probe.restype = ctypes.c_int
     lib.gdn_last_error.argtypes = []
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_abi_version.argtypes = []
@@ -206,18 +207,11 @@ def gdn_decode_batched(dims: gdn_dims, q, q_stride: int, k, k_stride: int, v, v_
     _check("gdn_decode_batched", st)
 
 
-def gdn_decode_fused_workspace_size(dims: gdn_dims, m: int) -> int:
-    out = ctypes.c_size_t(0)
-    _check("gdn_decode_fused_workspace_size",
-           _LIB.gdn_decode_fused_workspace_size(ctypes.byref(dims), m, ctypes.byref(out)))
-    return int(out.value)
-
-
 def gdn_decode_fused(dims: gdn_dims, x, x_stride: int, conv_w, conv_b, g, beta, o, state_ptrs, conv_state_ptrs,
-                     m: int, workspace, workspace_bytes: int, stream=None) -> None:
+                     conv_state_out_ptrs, m: int, stream=None) -> None:
     st = _LIB.gdn_decode_fused(ctypes.byref(dims), _ptr(x), x_stride, _ptr(conv_w), _ptr(conv_b), _ptr(g),
-                               _ptr(beta), _ptr(o), _ptr(state_ptrs), _ptr(conv_state_ptrs), m, _ptr(workspace),
-                               workspace_bytes, _stream(stream, x, o, state_ptrs))
+                               _ptr(beta), _ptr(o), _ptr(state_ptrs), _ptr(conv_state_ptrs),
+                               _ptr(conv_state_out_ptrs), m, _stream(stream, x, o, state_ptrs))
     _check("gdn_decode_fused", st)
 
 
@@ -227,6 +221,13 @@ def gdn_slot_copy(dims: gdn_dims, src_state_ptrs, dst_state_ptrs, src_conv_ptrs,
                             _ptr(dst_conv_ptrs), n,
                             _stream(stream, src_state_ptrs, dst_state_ptrs, src_conv_ptrs, dst_conv_ptrs))
     _check("gdn_slot_copy", st)
+
+
+def gdn_hbm_probe(buf, nbytes: int, salt: int = 0, stream=None) -> None:
+    """Measurement helper (include/gdn_probe.h): an in-place streaming pass over buf."""
+    st = _LIB.gdn_hbm_probe(_ptr(buf), nbytes, salt, _stream(stream, buf))
+    if st != GDN_OK:
+        raise GDNError("gdn_hbm_probe", st, "buffer NULL, misaligned or not a multiple of 16 KiB")
 
 
 def gdn_slot_pointers(pool_base: int, slot_bytes: int, pool_slots: int, slot_idx, m: int, out_ptrs,

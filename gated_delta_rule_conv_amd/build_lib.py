@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "conv.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["gdn_api.cpp", "conv.hip", "decode.hip", "prefill.hip", "probe.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

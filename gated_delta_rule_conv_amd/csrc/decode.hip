@@ -49,6 +49,17 @@ typedef __attribute__((address_space(1))) uint16_t gu16;
 
 constexpr int kDecodeWaves = 4;  // waves per workgroup
 
+// Workgroups are dealt round-robin to MI355X's 8 XCDs, each with its own L2. With a
+// slot's workgroups along grid.x (a multiple of 8 of them), workgroup x runs on XCD x % 8;
+// renumbering them so that XCD r takes the consecutive block [r n/8, (r+1) n/8) puts the
+// workgroups of one head -- which read the same k and q and write neighbouring bytes --
+// on one XCD, sharing its L2.
+__device__ __forceinline__ int xcd_block() {
+  const int n = gridDim.x;
+  const int b = blockIdx.x;
+  return (n % 8 == 0) ? (b % 8) * (n / 8) + b / 8 : b;
+}
+
 // element `off` of o, in o's dtype: OB 0 fp32, 1 bf16, 2 as the o_bf16 flag says
 template <int OB>
 __device__ __forceinline__ void* o_row(const RecurArgs& a, int64_t off) {
@@ -65,39 +76,38 @@ struct DecodeCfg {
   static_assert(NPART * ROWS == D, "units must tile the head");
 };
 
-// The arithmetic of one unit once its loads are in registers: normalise k and q (the
-// lane holds 16 columns of each), then for each of the P row passes the two row dots,
-// the delta-rule update of the rows and their outputs. Both decode kernels call this, so
-// the fused kernel's bits equal the separate conv + decode launches.
+// The arithmetic of one unit once its loads are in registers. The lane holds 16 columns
+// of the raw k and q (unnormalised); with rk = 1/sqrt(|k|^2 + eps) and rq = scale/sqrt(
+// |q|^2 + eps), k^ = rk k and q^ = rq q enter only through dot products and one scaled
+// fma, so the vectors are never rescaled:
+//     a_r = rk (S_r . k),  p_r = rq (S_r . q),  u_r = beta (v_r - alpha a_r),
+//     S_r <- alpha S_r + (u_r rk) k,           o_r = alpha p_r + u_r (k^ . q^),
+// with k^ . q^ = rk rq (k . q). 1/sqrt is the hardware reciprocal square root (about one
+// ulp). Every decode kernel runs this code, so their bits agree.
 // OB: how o is stored -- 0 fp32, 1 bf16 (rounded to nearest even), 2 as the o_bf16 flag says.
 template <int D, int P, int OB>
-__device__ __forceinline__ void decode_rows(const f32x4 (&s)[P][4], f32x4 (&kv)[4], f32x4 (&qv)[4], const float (&vr)[P],
-                                            float gval, float beta, float eps, float scale, bool qk_norm, gf32x4* S,
-                                            void* orow, bool o_bf16, int row0, int c) {
+__device__ __forceinline__ void decode_rows(const f32x4 (&s)[P][4], const f32x4 (&kv)[4], const f32x4 (&qv)[4],
+                                            const float (&vr)[P], float gval, float beta, float eps, float scale,
+                                            bool qk_norm, gf32x4* S, void* orow, bool o_bf16, int row0, int c) {
   using Cfg = DecodeCfg<D, P>;
   constexpr int LPR = Cfg::LPR, RPP = Cfg::RPP;
-  // k^ and q^ at this lane's 16 columns, and k^ . q^
-  float kk = 0.f, qq = 0.f;
+  // |k|^2, |q|^2 and k . q over the row's lanes
+  float kk = 0.f, qq = 0.f, kqr = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     kk = fmaf(kv[e].x, kv[e].x, kk); kk = fmaf(kv[e].y, kv[e].y, kk);
     kk = fmaf(kv[e].z, kv[e].z, kk); kk = fmaf(kv[e].w, kv[e].w, kk);
     qq = fmaf(qv[e].x, qv[e].x, qq); qq = fmaf(qv[e].y, qv[e].y, qq);
     qq = fmaf(qv[e].z, qv[e].z, qq); qq = fmaf(qv[e].w, qv[e].w, qq);
+    kqr = fmaf(kv[e].x, qv[e].x, kqr); kqr = fmaf(kv[e].y, qv[e].y, kqr);
+    kqr = fmaf(kv[e].z, qv[e].z, kqr); kqr = fmaf(kv[e].w, qv[e].w, kqr);
   }
   kk = group_sum<LPR>(kk);
   qq = group_sum<LPR>(qq);
-  const float rk = qk_norm ? 1.0f / sqrtf(kk + eps) : 1.0f;
-  const float rq = qk_norm ? scale / sqrtf(qq + eps) : scale;
-  float kq = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    kv[e].x *= rk; kv[e].y *= rk; kv[e].z *= rk; kv[e].w *= rk;
-    qv[e].x *= rq; qv[e].y *= rq; qv[e].z *= rq; qv[e].w *= rq;
-    kq = fmaf(kv[e].x, qv[e].x, kq); kq = fmaf(kv[e].y, qv[e].y, kq);
-    kq = fmaf(kv[e].z, qv[e].z, kq); kq = fmaf(kv[e].w, qv[e].w, kq);
-  }
-  kq = group_sum<LPR>(kq);
+  kqr = group_sum<LPR>(kqr);
+  const float rk = qk_norm ? __builtin_amdgcn_rsqf(kk + eps) : 1.0f;
+  const float rq = qk_norm ? scale * __builtin_amdgcn_rsqf(qq + eps) : scale;
+  const float kq = kqr * (rk * rq);
   const float alpha = expf(gval);
 
 #pragma unroll
@@ -111,17 +121,18 @@ __device__ __forceinline__ void decode_rows(const f32x4 (&s)[P][4], f32x4 (&kv)[
       sq = fmaf(s[p][e].x, qv[e].x, sq); sq = fmaf(s[p][e].y, qv[e].y, sq);
       sq = fmaf(s[p][e].z, qv[e].z, sq); sq = fmaf(s[p][e].w, qv[e].w, sq);
     }
-    sk = group_sum<LPR>(sk);
-    sq = group_sum<LPR>(sq);
+    sk = group_sum<LPR>(sk) * rk;
+    sq = group_sum<LPR>(sq) * rq;
     const float ur = beta * (vr[p] - alpha * sk);
+    const float urk = ur * rk;
     gf32x4* rowp = S + static_cast<int64_t>(r) * (D / 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       f32x4 n;
-      n.x = fmaf(ur, kv[e].x, alpha * s[p][e].x);
-      n.y = fmaf(ur, kv[e].y, alpha * s[p][e].y);
-      n.z = fmaf(ur, kv[e].z, alpha * s[p][e].z);
-      n.w = fmaf(ur, kv[e].w, alpha * s[p][e].w);
+      n.x = fmaf(urk, kv[e].x, alpha * s[p][e].x);
+      n.y = fmaf(urk, kv[e].y, alpha * s[p][e].y);
+      n.z = fmaf(urk, kv[e].z, alpha * s[p][e].z);
+      n.w = fmaf(urk, kv[e].w, alpha * s[p][e].w);
       __builtin_nontemporal_store(n, rowp + c + LPR * e);
     }
     if (c == 0) {
@@ -135,20 +146,22 @@ __device__ __forceinline__ void decode_rows(const f32x4 (&s)[P][4], f32x4 (&kv)[
 }
 
 
+// Grid: (units of a slot / 4, m); the slot is blockIdx.y, so the only runtime division
+// a wave makes before its first load is the k-head of its v-head.
 template <int D, int P, bool SCHED_FENCE, int OB>
-__global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(RecurArgs a, int32_t total_units) {
+__global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(RecurArgs a) {
   using Cfg = DecodeCfg<D, P>;
   constexpr int LPR = Cfg::LPR, RPP = Cfg::RPP, NPART = Cfg::NPART;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int u = blockIdx.x * kDecodeWaves + w;
-  if (u >= total_units) return;
-  const int part = u % NPART;
-  const int j = (u / NPART) % a.hv;
-  const int i = (u / NPART) / a.hv;
+  const int us = xcd_block() * kDecodeWaves + w;  // unit within the slot
+  if (us >= a.hv * NPART) return;
+  const int part = us % NPART;
+  const int j = us / NPART;
+  const int i = blockIdx.y;
   const uint64_t sp = ((cu64*)a.state_ptrs)[i];
   if (sp == 0) return;  // inactive slot
-  const int h = j / (a.hv / a.hk);
+  const int h = j / a.group;
   const int c = lane % LPR;   // column group inside the row
   const int rl = lane / LPR;  // row inside a pass
   const int row0 = part * Cfg::ROWS + rl;
@@ -184,12 +197,12 @@ __global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(RecurArgs a
 
 template <int D, int P, bool F>
 hipError_t launch_units(const RecurArgs& a, int32_t m, hipStream_t s) {
-  const int64_t units = static_cast<int64_t>(m) * a.hv * DecodeCfg<D, P>::NPART;
-  const unsigned blocks = static_cast<unsigned>((units + kDecodeWaves - 1) / kDecodeWaves);
+  const int units = a.hv * DecodeCfg<D, P>::NPART;  // per slot
+  const dim3 grid(static_cast<unsigned>((units + kDecodeWaves - 1) / kDecodeWaves), static_cast<unsigned>(m));
   if (a.o_bf16)
-    decode_kernel<D, P, F, 1><<<blocks, kDecodeWaves * kWave, 0, s>>>(a, static_cast<int32_t>(units));
+    decode_kernel<D, P, F, 1><<<grid, kDecodeWaves * kWave, 0, s>>>(a);
   else
-    decode_kernel<D, P, F, 0><<<blocks, kDecodeWaves * kWave, 0, s>>>(a, static_cast<int32_t>(units));
+    decode_kernel<D, P, F, 0><<<grid, kDecodeWaves * kWave, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -210,90 +223,76 @@ hipError_t launch_decode(const RecurArgs& a, int32_t m, hipStream_t s) {
 
 namespace {
 // ---------------------------------------------------------------- fused conv + decode
-// One launch for the whole decode step of a layer: the depthwise conv of the token's
-// q, k and v channels (against the slot's conv state), the conv state commit, and the
-// decode above. A workgroup is WPB units of one (slot, v-head), i.e. VR consecutive
-// state rows. Threads first convolve 4 channels each -- the 2d q/k channels of the
-// head's k-head (wave 0) and then the VR v channels of the workgroup's rows -- into LDS
-// with the conv kernels' arithmetic (conv4_raw). In one-pass units and short launches
-// the conv inputs are loaded before the state rows, so the conv waits only for its own
-// (mostly cached) inputs while the state is still streaming in; otherwise after them
-// (see CONV_FIRST). The waves then take k, q and v from LDS and run decode_rows
-// unchanged.
+// One launch for the whole decode step of a layer: the depthwise conv of the token's q,
+// k and v channels (against the slot's conv state), the conv-state commit, and the
+// decode above, with the conv output kept in LDS. Two forms: in place (below) and
+// streaming (further down), for when the new conv states go to other buffers.
 //
-// Conv state commit. The v channels of a workgroup's rows are read by that workgroup
-// alone, so their lanes write the shifted state right after reading it. The q/k
-// channels of k-head h are read by every workgroup of the (hv/hk) v-heads sharing it;
-// each of those workgroups adds one to counters[slot][h] once all its reads have
-// returned, and the one that brings it to the total writes the q/k conv state (from
-// the rows it keeps in LDS) and resets the counter to zero for the next call.
-template <int D, int P>
+// In place. One workgroup per (slot i, k-head h) holds everything that reads k-head h's q and k:
+// its 2d q/k conv channels, and the G = hv/hk v-heads j = hG .. hG + G - 1 that share it,
+// each with its d v channels and d state rows. Every conv-state value of the slot is then
+// read by exactly one thread of one workgroup, and that thread writes the shifted rows
+// back itself once its reads have returned (the values it stores are the values it
+// loaded): no other workgroup ever reads them, so the commit needs no ordering across
+// workgroups -- no counters and no workspace.
+//
+// The group's G d state rows are cut into blocks of ROWS rows (P passes of RPP rows, as a
+// decode_kernel unit), dealt to the waves in order, so the waves sweep the slot's G
+// consecutive head states front to back. Threads convolve 4 channels each (the q/k
+// channels, then the v channels) with the conv kernels' per-channel arithmetic
+// (conv4_raw) into LDS; one barrier that orders LDS only (state loads stay in flight
+// across it); then every wave takes k, q and its rows' v from LDS and runs decode_rows,
+// the code of decode_kernel, so o, the state and the conv state come out bit-identical to
+// gdn_conv_update + gdn_decode_batched. (The price of the large workgroups: at m = 64 one
+// of them fits a CU at a time, and each of a CU's rounds starts with a full memory round
+// trip with nothing else in flight -- 53.9 us per launch against 47.5 us streaming.)
+template <int D>
 struct FusedCfg {
-  static constexpr int NPART = DecodeCfg<D, P>::NPART;
-  static constexpr int WPB = NPART < kDecodeWaves ? NPART : kDecodeWaves;  // waves per workgroup
-  static constexpr int BPH = NPART / WPB;                                 // workgroups per (slot, v-head)
-  static constexpr int NT = WPB * kWave;
-  static constexpr int VR = WPB * DecodeCfg<D, P>::ROWS;                  // state rows per workgroup
-  static constexpr int CV = 4;                                            // channels per conv thread
-  static constexpr int GQK = 2 * D / CV;                                  // q/k channel groups
-  static constexpr int GV = VR / CV;                                      // v channel groups
-  static constexpr int NCG = GQK + GV;
-  static constexpr int NCW = (NCG + kWave - 1) / kWave;                   // waves that convolve
-  static_assert(GQK <= kWave, "the q/k groups are wave 0's");
-  static_assert(NCG <= NT, "one channel group per thread");
-  // One-pass units with bf16 inputs are held to 72 VGPRs, at least 7 waves per SIMD
-  // (they take 64: 8 waves); fp32 inputs need more registers for the raw conv inputs.
-  template <typename T>
-  static constexpr int min_blocks() { return (P == 1 && sizeof(T) == 2 && WPB == 4) ? 7 : 1; }
+  static constexpr int P = D == 128 ? 2 : 1;   // passes per block
+  using DC = DecodeCfg<D, P>;
+  static constexpr int ROWS = DC::ROWS;        // state rows per block: 16 (d = 64, 128) or 32 (d = 32)
+  static constexpr int MAXW = 16;              // waves per workgroup at most
+  static constexpr int CV = 4;                 // channels per conv thread
+  // waves of a workgroup for G v-heads per k-head, and blocks per wave
+  __host__ static int waves(int G) { return (G * D / ROWS) < MAXW ? G * D / ROWS : MAXW; }
+  __host__ static int iters(int G) { return (G * D / ROWS + waves(G) - 1) / waves(G); }
 };
 
-template <typename T, int K, int D, int P, bool SCHED_FENCE, bool CONV_FIRST>
-__global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min_blocks<T>())) void fused_decode_kernel(FusedArgs f) {
-  using Cfg = DecodeCfg<D, P>;
-  using FC = FusedCfg<D, P>;
+// The convolving waves load their conv inputs before their first state rows, so the conv
+// waits only for its own (mostly cached) inputs.
+template <typename T, int K, int D, bool SILU>
+__global__ __launch_bounds__(FusedCfg<D>::MAXW * kWave) void fused_decode_kernel(FusedArgs f, int32_t nit) {
+  using FC = FusedCfg<D>;
+  using DC = typename FC::DC;
   using V4 = Vec4<T>;
-  constexpr int LPR = Cfg::LPR, RPP = Cfg::RPP, ROWS = Cfg::ROWS;
-  constexpr int WPB = FC::WPB, BPH = FC::BPH, VR = FC::VR, GQK = FC::GQK, GV = FC::GV, NCG = FC::NCG;
-  constexpr int V = FC::CV;
+  constexpr int P = FC::P, LPR = DC::LPR, RPP = DC::RPP, ROWS = FC::ROWS, V = FC::CV;
   typedef __attribute__((address_space(1))) T GT;
-  __shared__ __attribute__((aligned(16))) float yqk[2 * D];  // q then k of the k-head
-  __shared__ __attribute__((aligned(16))) float yv[VR];
-  __shared__ typename V4::Raw qk_rows[K - 1][GQK];  // new q/k conv-state rows
+  extern __shared__ __attribute__((aligned(16))) float fused_lds[];  // conv output: q, k (2d), v of the group (G d)
   const RecurArgs& a = f.r;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int bh = blockIdx.x % BPH;
-  const int j = (blockIdx.x / BPH) % a.hv;
-  const int i = (blockIdx.x / BPH) / a.hv;
+  const int G = a.group;
+  const int i = blockIdx.y;
+  const int h = blockIdx.x;
   const uint64_t sp = ((cu64*)a.state_ptrs)[i];
   const uint64_t cp = ((cu64*)f.conv_ptrs)[i];
   if (sp == 0 || cp == 0) return;  // inactive slot (the whole workgroup)
-  const int h = j / (a.hv / a.hk);
-  const int part = bh * WPB + w;
-  const int c = lane % LPR;
-  const int rl = lane / LPR;
-  const int row0 = part * ROWS + rl;
-  gf32x4* S = (gf32x4*)(reinterpret_cast<float*>(sp) + static_cast<int64_t>(j) * D * D);
-  GT* cs = (GT*)reinterpret_cast<T*>(cp);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int nt = blockDim.x;
+  const int nw = nt / kWave;
+  const int c = lane % LPR;   // column group inside a row
+  const int rl = lane / LPR;  // row inside a pass
   const int C = f.channels;
+  const int NCG = (2 + G) * D / V;  // channel groups: q, k, then v of the group's v-heads
+  GT* cs = (GT*)reinterpret_cast<T*>(cp);
 
-  // Thread t < NCG takes channel group t (q/k groups, then v groups); other threads that
-  // load repeat a v group and drop the result. Everything is in flight before anything
-  // waits. CONV_FIRST: the conv inputs are loaded before the state rows, so the conv
-  // waits only for its own (mostly cached) inputs -- best where the launch is short and
-  // latency-bound; with two passes per wave every wave then loads conv inputs (loads
-  // under a branch made the compiler copy their results at its end, which waits for them
-  // before the state loads can issue). Otherwise the state rows go first and only the
-  // convolving waves load conv inputs, which issues fewer loads where the launch fills
-  // the chip.
-  const bool conv_wave = w < FC::NCW;
-  const int grp = tid < NCG ? tid : GQK + (tid - NCG) % GV;
-  const bool is_qk = grp < GQK;
-  const int ch0 = is_qk ? (grp * V < D ? h * D + grp * V : a.hk * D + h * D + (grp * V - D))
-                        : 2 * a.hk * D + j * D + bh * VR + (grp - GQK) * V;
+  // channel group g: its first channel of x, the taps and the conv state (its LDS offset is g V)
+  auto channel_of = [&](int g) {
+    const int e = g * V;
+    return e < D ? h * D + e : e < 2 * D ? a.hk * D + h * D + (e - D) : 2 * a.hk * D + h * G * D + (e - 2 * D);
+  };
   typename V4::Raw xr, sr[K - 1], wr[K], br;
-  auto load_conv = [&]() {
+  auto load_conv = [&](int ch0) {
 #pragma unroll
     for (int t = 0; t < K - 1; ++t) sr[t] = V4::load_raw_g(cs + static_cast<int64_t>(t) * C + ch0);
     xr = V4::load_raw(static_cast<const T*>(f.x) + static_cast<int64_t>(i) * f.x_stride + ch0);
@@ -302,105 +301,270 @@ __global__ __launch_bounds__((FusedCfg<D, P>::NT), (FusedCfg<D, P>::template min
     // with no bias, taps stand in for the load and are never used
     br = V4::load_raw(static_cast<const T*>(f.b ? f.b : f.w) + ch0);
   };
+  // convolve channel group g (loaded), put it in LDS and commit its new conv-state rows
+  // (old rows 1 .. K-2, then x): this thread is the only reader of those values
+  auto conv_commit = [&](int g, int ch0) {
+    float out[V];
+    conv4_raw<T, K>(wr, br, f.b != nullptr, sr, xr, SILU, out);
+    *reinterpret_cast<f32x4*>(&fused_lds[g * V]) = f32x4{out[0], out[1], out[2], out[3]};
+#pragma unroll
+    for (int t = 0; t < K - 2; ++t) V4::store_raw_g(cs + static_cast<int64_t>(t) * C + ch0, sr[t + 1]);
+    V4::store_raw_g(cs + static_cast<int64_t>(K - 2) * C + ch0, xr);
+  };
+
+  // block b of the group's rows: v-head h G + b ROWS / d, rows (b ROWS) % d + rl + p RPP
   f32x4 s[P][4];
-  auto load_state = [&]() {
+  auto state_of = [&](int b) {
+    const int jj = (b * ROWS) / D;
+    return (gf32x4*)(reinterpret_cast<float*>(sp) + static_cast<int64_t>(h * G + jj) * D * D);
+  };
+  auto load_block = [&](int b) {
+    gf32x4* S = state_of(b);
+    const int row0 = (b * ROWS) % D + rl;
 #pragma unroll
     for (int p = 0; p < P; ++p)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         s[p][e] = __builtin_nontemporal_load(S + static_cast<int64_t>(row0 + p * RPP) * (D / 4) + c + LPR * e);
   };
-  if constexpr (!CONV_FIRST) {
-    load_state();
-    if (conv_wave) load_conv();
-  } else {
-    if (conv_wave || P > 1) load_conv();
-    load_state();
-  }
-  const int64_t gi = static_cast<int64_t>(i) * a.hv + j;
-  const float gval = ((cfloat*)a.g)[gi];
-  const float beta = ((cfloat*)a.beta)[gi];
-  if constexpr (SCHED_FENCE) __builtin_amdgcn_sched_barrier(0);
 
-  // Only wave 0 reads q/k conv state. Once its reads have returned (their values are
-  // consumed here) it counts this workgroup in, with a relaxed atomic: no later write
-  // can reach a read that is done, and the commit needs nothing from the other
-  // workgroups but the count itself. (Acquire or release at device scope would write
-  // back and invalidate this XCD's L2.) The count comes back while the waves compute.
-  int32_t* ctr = f.counters + static_cast<int64_t>(i) * a.hk + h;
-  int before = 0;
+  const bool conv_wave = w * kWave < NCG;
+  const int g0 = tid < NCG ? tid : NCG - 1;  // (lanes past the last group repeat it and drop the result)
+  const int ch00 = channel_of(g0);
+  const bool first_block = w * ROWS < G * D;
+  if (conv_wave) load_conv(ch00);
+  if (first_block) load_block(w);
   if (conv_wave) {
-    float out[V];
-    conv4_raw<T, K>(wr, br, f.b != nullptr, sr, xr, f.silu != 0, out);
-    if (tid < NCG) {
-      float* dst = is_qk ? &yqk[grp * V] : &yv[(grp - GQK) * V];
-      *reinterpret_cast<f32x4*>(dst) = f32x4{out[0], out[1], out[2], out[3]};
-      // new conv-state rows = old rows 1 .. K-2, then x
-      if (!is_qk) {
-        // v channels: this thread is their only reader, so they are written now
-#pragma unroll
-        for (int t = 0; t < K - 2; ++t) V4::store_raw_g(cs + static_cast<int64_t>(t) * C + ch0, sr[t + 1]);
-        V4::store_raw_g(cs + static_cast<int64_t>(K - 2) * C + ch0, xr);
-      } else {
-        // q/k channels: kept in LDS for the commit, in case this workgroup is the last
-#pragma unroll
-        for (int t = 0; t < K - 2; ++t) qk_rows[t][grp] = sr[t + 1];
-        qk_rows[K - 2][grp] = xr;
-      }
+    if (tid < NCG) conv_commit(tid, ch00);
+    // more channel groups than threads (many v-heads per k-head): the rest in turn
+    for (int g = tid + nt; g < NCG; g += nt) {
+      const int ch0 = channel_of(g);
+      load_conv(ch0);
+      conv_commit(g, ch0);
     }
-    if (tid == 0) before = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  // A barrier that orders LDS only: the waves' state loads (and wave 0's count) stay in
-  // flight across it, where __syncthreads() would wait for all of them.
+  // A barrier that orders LDS only: the state loads stay in flight across it, where
+  // __syncthreads() would wait for all of them.
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
-  f32x4 kv[4], qv[4];
+  for (int it = 0; it < nit; ++it) {
+    const int b = it * nw + w;
+    if (b * ROWS >= G * D) break;
+    if (it > 0) load_block(b);
+    const int jj = (b * ROWS) / D;
+    const int j = h * G + jj;
+    const int64_t gi = static_cast<int64_t>(i) * a.hv + j;
+    const float gval = ((cfloat*)a.g)[gi];
+    const float beta = ((cfloat*)a.beta)[gi];
+    f32x4 kv[4], qv[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    qv[e] = *reinterpret_cast<const f32x4*>(&yqk[4 * (c + LPR * e)]);
-    kv[e] = *reinterpret_cast<const f32x4*>(&yqk[D + 4 * (c + LPR * e)]);
-  }
-  float vr[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) vr[p] = yv[w * ROWS + rl + p * RPP];
-  decode_rows<D, P, 2>(s, kv, qv, vr, gval, beta, a.eps, a.scale, a.qk_norm != 0, S, o_row<2>(a, gi * D), a.o_bf16 != 0, row0, c);
-
-  // the last workgroup of (slot, k-head) writes the q/k conv state (wave 0, from the
-  // rows it put in LDS itself) and leaves the counter at zero
-  if (w == 0 && __builtin_amdgcn_readfirstlane(before) == (a.hv / a.hk) * BPH - 1) {
-    if (lane < GQK) {
-#pragma unroll
-      for (int t = 0; t < K - 1; ++t) V4::store_raw_g(cs + static_cast<int64_t>(t) * C + ch0, qk_rows[t][lane]);
+    for (int e = 0; e < 4; ++e) {
+      qv[e] = *reinterpret_cast<const f32x4*>(&fused_lds[4 * (c + LPR * e)]);
+      kv[e] = *reinterpret_cast<const f32x4*>(&fused_lds[D + 4 * (c + LPR * e)]);
     }
-    if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int row0 = (b * ROWS) % D + rl;
+    float vr[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) vr[p] = fused_lds[2 * D + jj * D + row0 + p * RPP];
+    decode_rows<D, P, 2>(s, kv, qv, vr, gval, beta, a.eps, a.scale, a.qk_norm != 0, state_of(b), o_row<2>(a, gi * D),
+                         a.o_bf16 != 0, row0, c);
   }
 }
 
-template <typename T, int K, int D, int P, bool F, bool CF>
-hipError_t launch_fused_units(const FusedArgs& f, int32_t m, hipStream_t s) {
-  using FC = FusedCfg<D, P>;
-  const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(m) * f.r.hv * FC::BPH);
-  fused_decode_kernel<T, K, D, P, F, CF><<<blocks, FC::NT, 0, s>>>(f);
+// ------------------------------------------------------------- fused, streaming form
+// When the new conv states go to other buffers than the old ones are read from, no
+// workgroup's writes can reach another's reads, so a workgroup need not cover a whole
+// k-head. This form keeps decode_kernel's units (one wave = P passes of RPP rows of one
+// (slot, v-head), dealt in (slot, head, row) order), NW = min(4, units per head) waves to
+// a workgroup, all on one (slot, v-head). The workgroup's threads convolve the k-head's 2d
+// q and k channels between them, one channel each, and every wave the v channels of its
+// own rows; the values meet in LDS behind one barrier that orders LDS only (the state
+// loads stay in flight across it). Each new conv-state row is written once: a v channel by
+// the thread that convolved it, the q/k channels by the workgroup holding the first rows of
+// the (slot, k-head)'s first v-head.
+//
+// One channel of the conv with the operations of ConvTaps::apply and conv4_raw, in their
+// order (acc = b; acc = fma(w_j, z_j, acc), j = 0 .. K-1; then the activation), so all
+// give the same bits. z[0 .. K-2] are the preceding rows (oldest first), cur the token.
+template <typename T, int K, bool SILU>
+__device__ __forceinline__ float conv1(const float (&w)[K], float b, const float (&z)[K - 1], float cur) {
+  float acc = b;
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) acc = fmaf(w[j], z[j], acc);
+  acc = fmaf(w[K - 1], cur, acc);
+  if constexpr (SILU) acc = gdn::silu(acc);
+  return acc;
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v) {
+  if constexpr (sizeof(T) == 2) return bf16_to_f32(v);
+  else return v;
+}
+
+template <typename T, int K, int D, int P, bool SILU>
+__global__ __launch_bounds__(kDecodeWaves* kWave) void fused_stream_kernel(FusedArgs f) {
+  using Cfg = DecodeCfg<D, P>;
+  constexpr int LPR = Cfg::LPR, RPP = Cfg::RPP, NPART = Cfg::NPART, ROWS = Cfg::ROWS;
+  constexpr int NW = NPART < kDecodeWaves ? NPART : kDecodeWaves;  // waves per workgroup
+  static_assert(NPART % NW == 0 && 2 * D <= NW * kWave && ROWS <= kWave, "workgroup shape");
+  typedef __attribute__((address_space(1))) T GT;
+  typedef __attribute__((address_space(1))) const T CGT;
+  __shared__ __attribute__((aligned(16))) float qk_l[2 * D];  // q, k of the k-head
+  __shared__ float v_l[NW][ROWS];                            // v at each wave's rows
+  const RecurArgs& a = f.r;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int us = xcd_block() * NW + w;  // unit within the slot (NW divides NPART: whole workgroups)
+  const int part = us % NPART;
+  const int j = us / NPART;
+  const int i = blockIdx.y;
+  const uint64_t sp = ((cu64*)a.state_ptrs)[i];
+  const uint64_t cin = ((cu64*)f.conv_ptrs)[i];
+  const uint64_t cout = ((cu64*)f.conv_out_ptrs)[i];
+  if (sp == 0 || cin == 0 || cout == 0) return;  // inactive slot (the whole workgroup)
+  const int G = a.group;
+  const int h = j / G;
+  const int c = lane % LPR;
+  const int rl = lane / LPR;
+  const int row0 = part * ROWS + rl;
+  const int C = f.channels;
+  CGT* csin = (CGT*)reinterpret_cast<const T*>(cin);
+  GT* csout = (GT*)reinterpret_cast<T*>(cout);
+  const T* x = static_cast<const T*>(f.x) + static_cast<int64_t>(i) * f.x_stride;
+  const T* wt = static_cast<const T*>(f.w);
+  const T* bs = static_cast<const T*>(f.b ? f.b : f.w);  // (taps stand in when there is no bias)
+  const bool has_b = f.b != nullptr;
+
+  // conv inputs first (mostly cached: the conv then waits only for them while the state
+  // streams in). Thread t < 2d: q/k channel t of the k-head; lane l < ROWS: the v channel
+  // of the wave's row l. Threads without a channel load channel 0's and drop the result.
+  const bool has_qk = tid < 2 * D;
+  const int e = has_qk ? tid : 0;
+  const int chq = e < D ? h * D + e : a.hk * D + h * D + (e - D);
+  const bool has_v = lane < ROWS;
+  const int chv = 2 * a.hk * D + j * D + part * ROWS + (has_v ? lane : 0);
+  T qz[K - 1], qx, qb, vz[K - 1], vx, vb;
+  float qw[K], vw[K];
+#pragma unroll
+  for (int t = 0; t < K - 1; ++t) {
+    qz[t] = csin[static_cast<int64_t>(t) * C + chq];
+    vz[t] = csin[static_cast<int64_t>(t) * C + chv];
+  }
+  qx = x[chq];
+  vx = x[chv];
+#pragma unroll
+  for (int t = 0; t < K; ++t) {
+    qw[t] = to_f32<T>(wt[static_cast<int64_t>(chq) * K + t]);
+    vw[t] = to_f32<T>(wt[static_cast<int64_t>(chv) * K + t]);
+  }
+  qb = bs[chq];
+  vb = bs[chv];
+  gf32x4* S = (gf32x4*)(reinterpret_cast<float*>(sp) + static_cast<int64_t>(j) * D * D);
+  f32x4 s[P][4];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      s[p][q] = __builtin_nontemporal_load(S + static_cast<int64_t>(row0 + p * RPP) * (D / 4) + c + LPR * q);
+  const int64_t gi = static_cast<int64_t>(i) * a.hv + j;
+  const float gval = ((cfloat*)a.g)[gi];
+  const float beta = ((cfloat*)a.beta)[gi];
+
+  {
+    float zq[K - 1], zv[K - 1];
+#pragma unroll
+    for (int t = 0; t < K - 1; ++t) {
+      zq[t] = to_f32<T>(qz[t]);
+      zv[t] = to_f32<T>(vz[t]);
+    }
+    const float oq = conv1<T, K, SILU>(qw, has_b ? to_f32<T>(qb) : 0.f, zq, to_f32<T>(qx));
+    const float ov = conv1<T, K, SILU>(vw, has_b ? to_f32<T>(vb) : 0.f, zv, to_f32<T>(vx));
+    if (has_qk) qk_l[tid] = oq;
+    if (has_v) v_l[w][lane] = ov;
+  }
+  if constexpr (NW > 1) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  } else {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+  f32x4 kv[4], qv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    qv[q] = *reinterpret_cast<const f32x4*>(&qk_l[4 * (c + LPR * q)]);
+    kv[q] = *reinterpret_cast<const f32x4*>(&qk_l[D + 4 * (c + LPR * q)]);
+  }
+  float vr[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) vr[p] = v_l[w][rl + p * RPP];
+  decode_rows<D, P, 2>(s, kv, qv, vr, gval, beta, a.eps, a.scale, a.qk_norm != 0, S, o_row<2>(a, gi * D),
+                       a.o_bf16 != 0, row0, c);
+
+  // the new conv-state rows (old rows 1 .. K-2, then x)
+  if (has_v) {
+#pragma unroll
+    for (int t = 0; t < K - 2; ++t) csout[static_cast<int64_t>(t) * C + chv] = vz[t + 1];
+    csout[static_cast<int64_t>(K - 2) * C + chv] = vx;
+  }
+  if ((j % G) == 0 && part < NW && has_qk) {
+#pragma unroll
+    for (int t = 0; t < K - 2; ++t) csout[static_cast<int64_t>(t) * C + chq] = qz[t + 1];
+    csout[static_cast<int64_t>(K - 2) * C + chq] = qx;
+  }
+}
+
+template <typename T, int K, int D, int P>
+hipError_t launch_stream_p(const FusedArgs& f, int32_t m, hipStream_t s) {
+  using Cfg = DecodeCfg<D, P>;
+  constexpr int NW = Cfg::NPART < kDecodeWaves ? Cfg::NPART : kDecodeWaves;
+  const dim3 blocks(static_cast<unsigned>(f.r.hv * Cfg::NPART / NW), static_cast<unsigned>(m));
+  if (f.silu)
+    fused_stream_kernel<T, K, D, P, true><<<blocks, NW * kWave, 0, s>>>(f);
+  else
+    fused_stream_kernel<T, K, D, P, false><<<blocks, NW * kWave, 0, s>>>(f);
+  return hipGetLastError();
+}
+
+// unit size as launch_decode (d = 32: one pass; d = 64: one pass of 16 rows, so that a
+// head's rows fill a four-wave workgroup)
+template <typename T, int K, int D>
+hipError_t launch_stream_d(const FusedArgs& f, int32_t m, hipStream_t s) {
+  if constexpr (D == 128) {
+    if (static_cast<int64_t>(m) * f.r.hv >= 1024) return launch_stream_p<T, K, D, 1>(f, m, s);
+    return launch_stream_p<T, K, D, 2>(f, m, s);
+  } else {
+    return launch_stream_p<T, K, D, 1>(f, m, s);
+  }
+}
+
+template <typename T, int K, int D>
+hipError_t launch_fused_d(const FusedArgs& f, int32_t m, hipStream_t s) {
+  if (f.conv_out_ptrs != f.conv_ptrs) return launch_stream_d<T, K, D>(f, m, s);
+  using FC = FusedCfg<D>;
+  const int G = f.r.group;
+  const dim3 blocks(static_cast<unsigned>(f.r.hk), static_cast<unsigned>(m));
+  const unsigned threads = static_cast<unsigned>(FC::waves(G) * kWave);
+  const size_t lds = static_cast<size_t>(2 + G) * D * sizeof(float);
+  if (f.silu)
+    fused_decode_kernel<T, K, D, true><<<blocks, threads, lds, s>>>(f, FC::iters(G));
+  else
+    fused_decode_kernel<T, K, D, false><<<blocks, threads, lds, s>>>(f, FC::iters(G));
   return hipGetLastError();
 }
 
 template <typename T, int K>
 hipError_t launch_fused_k(const FusedArgs& f, int32_t m, hipStream_t s) {
-  // unit size as launch_decode; below m * Hv = 256 (a launch of a few hundred
-  // workgroups) the two-pass units load the conv inputs first
-  const int64_t mh = static_cast<int64_t>(m) * f.r.hv;
   switch (f.r.d) {
-    case 32: return launch_fused_units<T, K, 32, 1, false, true>(f, m, s);
-    case 64:
-      if (mh >= 1024) return launch_fused_units<T, K, 64, 1, false, true>(f, m, s);
-      return mh >= 256 ? launch_fused_units<T, K, 64, 2, true, false>(f, m, s)
-                       : launch_fused_units<T, K, 64, 2, true, true>(f, m, s);
-    default:
-      if (mh >= 1024) return launch_fused_units<T, K, 128, 1, false, true>(f, m, s);
-      return mh >= 256 ? launch_fused_units<T, K, 128, 2, true, false>(f, m, s)
-                       : launch_fused_units<T, K, 128, 2, true, true>(f, m, s);
+    case 32: return launch_fused_d<T, K, 32>(f, m, s);
+    case 64: return launch_fused_d<T, K, 64>(f, m, s);
+    default: return launch_fused_d<T, K, 128>(f, m, s);
   }
 }
 
@@ -414,7 +578,6 @@ hipError_t launch_fused_t(const FusedArgs& f, int32_t m, hipStream_t s) {
 }
 }  // namespace
 
-// Same unit-size rule as launch_decode.
 hipError_t launch_decode_fused(const FusedArgs& f, int32_t m, hipStream_t s) {
   if (m == 0) return hipSuccess;
   return f.bf16 ? launch_fused_t<uint16_t>(f, m, s) : launch_fused_t<float>(f, m, s);

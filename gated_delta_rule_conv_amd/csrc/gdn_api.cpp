@@ -203,7 +203,8 @@ gdn_status gdn_prefill_chunked(const gdn_dims* dims, const float* q, int64_t q_s
   gdn::PrefillArgs a{};
   a.r = gdn::RecurArgs{q, q_stride, k, k_stride, v, v_stride, g, beta, o, state_ptrs, dims->num_k_heads,
                        dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0};
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0,
+                       dims->num_v_heads / dims->num_k_heads};
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
   a.total_tokens = total_tokens;
@@ -278,7 +279,8 @@ gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stri
   gdn::PrefillArgs a{};
   a.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, yv, vw, g, beta, o, state_ptrs, dims->num_k_heads,
                        dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0};
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0,
+                       dims->num_v_heads / dims->num_k_heads};
   a.conv = gdn::ConvIn{x, x_stride, conv_w, conv_b, conv_state_ptrs, static_cast<int32_t>(C), K, silu, bf16};
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
@@ -304,23 +306,15 @@ gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_st
   if (gdn_status st = check_qkv(dims, fn, q, q_stride, k, k_stride, v, v_stride, g, beta, o, m)) return st;
   gdn::RecurArgs a{q, q_stride, k, k_stride, v, v_stride, g, beta, o, state_ptrs, dims->num_k_heads,
                    dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0};
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0,
+                       dims->num_v_heads / dims->num_k_heads};
   return hip_status(gdn::launch_decode(a, m, static_cast<hipStream_t>(stream)), fn);
-}
-
-gdn_status gdn_decode_fused_workspace_size(const gdn_dims* dims, int32_t m, size_t* bytes) {
-  const char* fn = "gdn_decode_fused_workspace_size";
-  if (gdn_status st = check_dims(dims, fn)) return st;
-  if (!bytes) return fail(GDN_ERR_NULL, "%s: bytes is NULL", fn);
-  if (m < 0) return fail(GDN_ERR_SHAPE, "%s: negative m", fn);
-  *bytes = static_cast<size_t>(m) * dims->num_k_heads * sizeof(int32_t);
-  return GDN_OK;
 }
 
 gdn_status gdn_decode_fused(const gdn_dims* dims, const void* x, int64_t x_stride, const void* conv_w,
                             const void* conv_b, const float* g, const float* beta, void* o,
-                            const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, int32_t m,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs,
+                            const uint64_t* conv_state_out_ptrs, int32_t m, void* stream) {
   const char* fn = "gdn_decode_fused";
   if (gdn_status st = check_dims(dims, fn)) return st;
   if (m < 0) return fail(GDN_ERR_SHAPE, "%s: negative m", fn);
@@ -334,22 +328,23 @@ gdn_status gdn_decode_fused(const gdn_dims* dims, const void* x, int64_t x_strid
                 static_cast<long long>(C));
   if (!aligned16(x) || !aligned16(conv_w) || (conv_b && !aligned16(conv_b)) || (x_stride * esz) % 16)
     return fail(GDN_ERR_ALIGN, "%s: x, conv_w, conv_b must be 16-byte aligned and x_stride a multiple of 16 bytes", fn);
-  const size_t need = static_cast<size_t>(m) * dims->num_k_heads * sizeof(int32_t);
-  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 3u))
-    return fail(GDN_ERR_WORKSPACE, "%s: a 4-byte aligned counter workspace of %zu bytes is needed, %zu given", fn, need,
-                workspace_bytes);
-  const int64_t blocks = static_cast<int64_t>(m) * dims->num_v_heads * (dims->head_dim / 32);
-  if (blocks > 0x7fffffff) return fail(GDN_ERR_SHAPE, "%s: m = %d too large for one launch", fn, m);
+  // one workgroup per (slot, k-head) keeps the conv output of the k-head and its v-heads in LDS
+  const int64_t group = dims->num_v_heads / dims->num_k_heads;
+  if ((2 + group) * dims->head_dim * 4 > 65536)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: %lld v-heads per k-head at head_dim %d exceed one workgroup's LDS", fn,
+                static_cast<long long>(group), dims->head_dim);
+  if (m > 65535) return fail(GDN_ERR_SHAPE, "%s: m = %d above the grid limit 65535", fn, m);
   gdn::FusedArgs f{};
   f.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, nullptr, 0, g, beta, o, state_ptrs, dims->num_k_heads,
                        dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0};
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0,
+                       dims->num_v_heads / dims->num_k_heads};
   f.x = x;
   f.x_stride = x_stride;
   f.w = conv_w;
   f.b = conv_b;
   f.conv_ptrs = conv_state_ptrs;
-  f.counters = static_cast<int32_t*>(workspace);
+  f.conv_out_ptrs = conv_state_out_ptrs ? conv_state_out_ptrs : conv_state_ptrs;
   f.channels = static_cast<int32_t>(C);
   f.width = dims->conv_width;
   f.silu = dims->activation == GDN_ACT_SILU;

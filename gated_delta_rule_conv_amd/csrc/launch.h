@@ -51,6 +51,7 @@ struct RecurArgs {
   float scale;
   int32_t o_bf16;   // o holds the fp32 results rounded to bf16 (nearest even)
   int32_t qk_norm;  // q and k L2-normalised (else used as given; q still times scale)
+  int32_t group;    // hv / hk: v-heads per k-head
 };
 
 hipError_t launch_decode(const RecurArgs& a, int32_t m, hipStream_t s);
@@ -62,8 +63,8 @@ struct FusedArgs {
   int64_t x_stride;
   const void* w;
   const void* b;  // nullable
-  const uint64_t* conv_ptrs;
-  int32_t* counters;  // [m][hk], zero on entry and on exit
+  const uint64_t* conv_ptrs;      // old conv state per slot (read)
+  const uint64_t* conv_out_ptrs;  // new conv state per slot: conv_ptrs itself (in place) or other buffers
   int32_t channels;
   int32_t width;
   int32_t silu;

@@ -113,17 +113,12 @@ def decode(dims: gdn_dims, y: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
 
 
 def decode_fused(dims: gdn_dims, x: torch.Tensor, conv_w: torch.Tensor, conv_b, g: torch.Tensor, beta: torch.Tensor,
-                 o: torch.Tensor, state_ptrs: torch.Tensor, conv_state_ptrs: torch.Tensor, counters: torch.Tensor,
-                 stream=None) -> None:
-    """conv_update (decode mode) + decode in one launch; counters from decode_counters()."""
+                 o: torch.Tensor, state_ptrs: torch.Tensor, conv_state_ptrs: torch.Tensor,
+                 conv_state_out_ptrs=None, stream=None) -> None:
+    """conv_update (decode mode) + decode in one launch. The new conv states go to
+    conv_state_out_ptrs (other buffers, the faster form) or, when None, in place."""
     _lib.gdn_decode_fused(dims, x, x.stride(0), conv_w, conv_b, g, beta, o, state_ptrs, conv_state_ptrs,
-                          state_ptrs.numel(), counters, counters.numel() * counters.element_size(), stream)
-
-
-def decode_counters(dims: gdn_dims, m: int, device="cuda") -> torch.Tensor:
-    """Zero-filled counter workspace of decode_fused for up to m slots (left zero by every call)."""
-    n = _lib.gdn_decode_fused_workspace_size(dims, m) // 4
-    return torch.zeros(max(n, 1), dtype=torch.int32, device=device)
+                          conv_state_out_ptrs, state_ptrs.numel(), stream)
 
 
 def prefill_workspace(dims: gdn_dims, num_seqs: int, total_tokens: int, device="cuda") -> torch.Tensor:
@@ -136,6 +131,6 @@ def prefill_fused_workspace(dims: gdn_dims, num_seqs: int, total_tokens: int, de
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-__all__ = ["SlotPool", "channels", "conv_update", "decode", "decode_counters", "decode_fused", "prefill",
+__all__ = ["SlotPool", "channels", "conv_update", "decode", "decode_fused", "prefill",
            "prefill_fused", "prefill_fused_workspace", "prefill_workspace", "qkv_views", "torch_in_dtype", "GDN_F32",
            "GDN_BF16"]

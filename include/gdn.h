@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -250,12 +250,6 @@ gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_st
                               void* stream);
 
 /* ---------------------------------------------------------------------------------
- * gdn_decode_fused_workspace_size -- bytes of the counter workspace gdn_decode_fused
- * needs for up to m slots (m * Hk int32 counters), written to *bytes.
- */
-gdn_status gdn_decode_fused_workspace_size(const gdn_dims* dims, int32_t m, size_t* bytes);
-
-/* ---------------------------------------------------------------------------------
  * gdn_decode_fused -- the whole decode step of a layer in one launch: the conv of
  * gdn_conv_update in decode mode (token i <-> slot i), its conv-state commit, then
  * gdn_decode_batched on the conv output, which never leaves the chip. o, the states
@@ -266,19 +260,27 @@ gdn_status gdn_decode_fused_workspace_size(const gdn_dims* dims, int32_t m, size
  *
  *  x, x_stride, conv_w, conv_b   as gdn_conv_update (x: [m][C] in_dtype).
  *  g, beta, o                    as gdn_decode_batched.
- *  state_ptrs, conv_state_ptrs   device u64 [m]: slot i's recurrent state and conv
- *             state. Slot i is inactive (nothing read or written, o rows untouched) when
- *             either entry is 0.
- *  workspace  device int32 counters, at least gdn_decode_fused_workspace_size(dims, m)
- *             bytes, 4-byte aligned. They must be zero before the first call (e.g.
- *             zero-filled once when allocated); every call leaves them zero again. Calls
- *             that share a workspace must not overlap in time (same stream is fine).
+ *  state_ptrs, conv_state_ptrs   device u64 [m]: slot i's recurrent state (updated in
+ *             place) and its conv state ([K-1][C] in_dtype, read).
+ *  conv_state_out_ptrs  device u64 [m]: where slot i's new conv state goes. NULL, or the
+ *             same array as conv_state_ptrs, updates the conv states in place. Any other
+ *             array names separate buffers (e.g. a second conv pool the caller alternates
+ *             with the first from step to step): the old state is then only read and stays
+ *             as it was. Unchecked precondition for that case: no output buffer overlaps a
+ *             conv state the call reads, and the outputs are distinct from one another.
+ *             Separate buffers let the launch run without cross-workgroup ordering: it is
+ *             the faster form; in place, one workgroup per (slot, k-head) reads and
+ *             rewrites every conv-state value of its channels itself.
+ *  Slot i is inactive (nothing read or written, o rows untouched) when its state pointer,
+ *  its conv-state pointer or its output conv-state pointer is 0.
+ *  No workspace. Errors: as the two calls; GDN_ERR_UNSUPPORTED when (2 + Hv/Hk) *
+ *  head_dim * 4 bytes of conv output exceed 64 KiB.
  *  Alignment: x, conv_w, conv_b 16-byte aligned, x_stride a multiple of 16 bytes.
  */
 gdn_status gdn_decode_fused(const gdn_dims* dims, const void* x, int64_t x_stride, const void* conv_w,
                             const void* conv_b, const float* g, const float* beta, void* o,
-                            const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, int32_t m,
-                            void* workspace, size_t workspace_bytes, void* stream);
+                            const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs,
+                            const uint64_t* conv_state_out_ptrs, int32_t m, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * gdn_slot_pointers -- build a device u64 pointer array from slot indices, on the

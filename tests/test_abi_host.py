@@ -20,9 +20,14 @@ FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
 
 
 def _declared_symbols():
-    with open(os.path.join(ROOT, "include", "gdn.h")) as f:
-        text = f.read()
-    return sorted(set(re.findall(r"^(?:gdn_status|const char\*|int32_t)\s+(gdn_\w+)\s*\(", text, re.M)))
+    """Every function declared in include/*.h."""
+    syms = set()
+    for name in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if name.endswith(".h"):
+            with open(os.path.join(ROOT, "include", name)) as f:
+                text = f.read()
+            syms |= set(re.findall(r"^(?:gdn_status|const char\*|int32_t)\s+(gdn_\w+)\s*\(", text, re.M))
+    return sorted(syms)
 
 
 def test_header_symbols_are_exported():
@@ -34,7 +39,7 @@ def test_header_symbols_are_exported():
 
 
 def test_abi_version_and_struct_size():
-    assert gdn.gdn_abi_version() == 5
+    assert gdn.gdn_abi_version() == 6
     assert ctypes.sizeof(_lib.gdn_dims) == 14 * 4
 
 
@@ -122,29 +127,28 @@ def test_decode_argument_checks():
 def test_decode_fused_argument_checks():
     d = dims()
     C = 8192
-    need = gdn.gdn_decode_fused_workspace_size(d, 4)
-    assert need == 4 * 16 * 4
-    assert _status(gdn.gdn_decode_fused_workspace_size, d, -1)[0] == _lib.GDN_ERR_SHAPE
-    ok_pre = (FAKE, C, FAKE, None, FAKE, FAKE, FAKE)  # x, x_stride, conv_w, conv_b, g, beta, o
-    # every pointer array is required
-    assert _status(gdn.gdn_decode_fused, d, *ok_pre, None, FAKE, 4, FAKE, need, 0)[0] == _lib.GDN_ERR_NULL
-    assert _status(gdn.gdn_decode_fused, d, *ok_pre, FAKE, None, 4, FAKE, need, 0)[0] == _lib.GDN_ERR_NULL
-    assert _status(gdn.gdn_decode_fused, d, None, C, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, need,
-                   0)[0] == _lib.GDN_ERR_NULL
-    # workspace missing, too small or misaligned
-    assert _status(gdn.gdn_decode_fused, d, *ok_pre, FAKE, FAKE, 4, None, need, 0)[0] == _lib.GDN_ERR_WORKSPACE
-    assert _status(gdn.gdn_decode_fused, d, *ok_pre, FAKE, FAKE, 4, FAKE, need - 4, 0)[0] == _lib.GDN_ERR_WORKSPACE
-    assert _status(gdn.gdn_decode_fused, d, *ok_pre, FAKE, FAKE, 4, FAKE + 2, need, 0)[0] == _lib.GDN_ERR_WORKSPACE
+    pre = (FAKE, C, FAKE, None, FAKE, FAKE, FAKE)  # x, x_stride, conv_w, conv_b, g, beta, o
+
+    def call(*args, dm=d):
+        return _status(gdn.gdn_decode_fused, dm, *args)[0]
+
+    # the state and conv-state pointer arrays are required (the output array is optional)
+    assert call(*pre, None, FAKE, None, 4, 0) == _lib.GDN_ERR_NULL
+    assert call(*pre, FAKE, None, None, 4, 0) == _lib.GDN_ERR_NULL
+    assert call(*pre, FAKE, None, FAKE, 4, 0) == _lib.GDN_ERR_NULL
+    assert call(None, *pre[1:], FAKE, FAKE, None, 4, 0) == _lib.GDN_ERR_NULL
     # x stride below C, or not a multiple of 16 bytes; misaligned x
-    assert _status(gdn.gdn_decode_fused, d, FAKE, C - 8, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, need,
-                   0)[0] == _lib.GDN_ERR_SHAPE
-    assert _status(gdn.gdn_decode_fused, d, FAKE, C + 4, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, need,
-                   0)[0] == _lib.GDN_ERR_ALIGN
-    assert _status(gdn.gdn_decode_fused, d, FAKE + 8, C, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, need,
-                   0)[0] == _lib.GDN_ERR_ALIGN
-    assert _status(gdn.gdn_decode_fused, d, *ok_pre, FAKE, FAKE, -1, FAKE, need, 0)[0] == _lib.GDN_ERR_SHAPE
+    assert call(FAKE, C - 8, *pre[2:], FAKE, FAKE, None, 4, 0) == _lib.GDN_ERR_SHAPE
+    assert call(FAKE, C + 4, *pre[2:], FAKE, FAKE, None, 4, 0) == _lib.GDN_ERR_ALIGN
+    assert call(FAKE + 8, C, *pre[2:], FAKE, FAKE, None, 4, 0) == _lib.GDN_ERR_ALIGN
+    assert call(*pre, FAKE, FAKE, None, -1, 0) == _lib.GDN_ERR_SHAPE
+    # in place, one workgroup per (slot, k-head) holds the conv output of the k-head's q, k
+    # and its v-heads in LDS: (2 + Hv/Hk) * d * 4 bytes may not exceed 64 KiB
+    wide = dims(num_k_heads=1, num_v_heads=200, head_dim=128)
+    st, msg = _status(gdn.gdn_decode_fused, wide, FAKE, 202 * 128, *pre[2:], FAKE, FAKE, None, 4, 0)
+    assert st == _lib.GDN_ERR_UNSUPPORTED and "LDS" in msg
     # m = 0 launches nothing
-    gdn.gdn_decode_fused(d, *ok_pre, FAKE, FAKE, 0, None, 0, 0)
+    gdn.gdn_decode_fused(d, *pre, FAKE, FAKE, None, 0, 0)
 
 
 def test_conv_argument_checks():
@@ -302,6 +306,7 @@ _C99_PROBE = r"""
 #include <stdio.h>
 #include <string.h>
 #include "gdn.h"
+#include "gdn_probe.h"
 
 int main(void) {
   gdn_dims z = {0};  /* zero-filled: every enumerated field at its default */
@@ -326,6 +331,7 @@ int main(void) {
     return 15;
   if (gdn_dims_init(NULL, 1, 1, 32) != GDN_ERR_NULL) return 16;
   if (gdn_abi_version() != GDN_ABI_VERSION) return 17;
+  if (gdn_hbm_probe(NULL, 16384, 0, NULL) != GDN_ERR_NULL) return 18;
   printf("c99 ok\n");
   return 0;
 }
@@ -351,3 +357,10 @@ def test_header_compiles_as_c99_and_zero_filled_dims_normalise(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and "c99 ok" in r.stdout, (r.returncode, r.stdout, r.stderr)
+
+
+def test_hbm_probe_checks():
+    assert _status(gdn.gdn_hbm_probe, None, 16384)[0] == _lib.GDN_ERR_NULL
+    assert _status(gdn.gdn_hbm_probe, FAKE + 8, 16384)[0] == _lib.GDN_ERR_ALIGN
+    assert _status(gdn.gdn_hbm_probe, FAKE, 16384 + 16)[0] == _lib.GDN_ERR_ALIGN
+    gdn.gdn_hbm_probe(FAKE, 0)  # nothing to stream: nothing launched

@@ -81,7 +81,6 @@ def test_decode_step_full_size_30_layers_every_slot():
     assert worst_o <= TOL_BF16 and worst_S <= TOL_BF16
 
     # the one-launch step on the pre-step copies gives the same bits
-    counters = gdn.decode_counters(dims, M, device="cuda")
     of = torch.empty((M, Hv, d), dtype=torch.float32, device="cuda")
     for l in fused_layers:
         st, cs = copies[l]
@@ -89,7 +88,7 @@ def test_decode_step_full_size_30_layers_every_slot():
         cp1 = torch.empty((M,), dtype=torch.int64, device="cuda")
         gdn.gdn_slot_pointers(st.data_ptr(), s_bytes, POOL, idx, M, sp1)
         gdn.gdn_slot_pointers(cs.data_ptr(), c_bytes, POOL, idx, M, cp1)
-        gdn.decode_fused(dims, x[l], conv_w[l], None, g[l], beta[l], of, sp1, cp1, counters)
+        gdn.decode_fused(dims, x[l], conv_w[l], None, g[l], beta[l], of, sp1, cp1)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bits_of(of), bits_of(o[l]))
         np.testing.assert_array_equal(bits_of(st), bits_of(states[l]))

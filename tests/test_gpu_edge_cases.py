@@ -199,11 +199,10 @@ def run_decode(inp, dims, fused, m):
     rows = torch.tensor([[s * L + t for s in range(m)] for t in range(L)], dtype=torch.int64, device="cuda")
     o = torch.empty((L, m, sh.num_v_heads, sh.head_dim), dtype=torch.float32, device="cuda")
     y = torch.empty((m, sh.channels), dtype=torch.float32, device="cuda")
-    counters = gdn.decode_counters(dims, m)
     for t in range(L):
         xt, gt, bt = x[rows[t]].contiguous(), g[rows[t]].contiguous(), beta[rows[t]].contiguous()
         if fused:
-            gdn.decode_fused(dims, xt, w, None, gt, bt, o[t], sp, cp, counters)
+            gdn.decode_fused(dims, xt, w, None, gt, bt, o[t], sp, cp)
         else:
             gdn.conv_update(dims, xt, y, w, None, cp)
             gdn.decode(dims, y, gt, bt, o[t], sp)
@@ -258,7 +257,6 @@ def test_scale_with_norm_on_prefill_then_decode():
         o1, _, _, pool = run_prefill(part, dims, fused=fused)
         sp, cp = pool.pointers(torch.arange(2, dtype=torch.int32, device="cuda"))
         w = to_dev(full["conv_w"], "bf16")
-        counters = gdn.decode_counters(dims, 2)
         outs = []
         for t in range(L2):
             rows = [cu[s] + L1 + t for s in range(2)]
@@ -266,7 +264,7 @@ def test_scale_with_norm_on_prefill_then_decode():
             g, beta = to_dev(full["g"][rows], "f32"), to_dev(full["beta"][rows], "f32")
             o = torch.empty((2, 4, 128), dtype=torch.float32, device="cuda")
             if fused:
-                gdn.decode_fused(dims, x, w, None, g, beta, o, sp, cp, counters)
+                gdn.decode_fused(dims, x, w, None, g, beta, o, sp, cp)
             else:
                 y = torch.empty((2, shape.channels), dtype=torch.float32, device="cuda")
                 gdn.conv_update(dims, x, y, w, None, cp)

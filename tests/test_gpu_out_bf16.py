@@ -49,7 +49,7 @@ def test_decode_bf16_output_is_the_rounded_fp32_output(m, fused):
         o = torch.empty((m, sh.num_v_heads, sh.head_dim), dtype=torch.bfloat16 if out == "bf16" else torch.float32,
                         device="cuda")
         if fused:
-            gdn.decode_fused(dims, x, w, None, g, beta, o, sp, cp, gdn.decode_counters(dims, m))
+            gdn.decode_fused(dims, x, w, None, g, beta, o, sp, cp)
         else:
             y = torch.empty((m, sh.channels), dtype=torch.float32, device="cuda")
             gdn.conv_update(dims, x, y, w, None, cp)

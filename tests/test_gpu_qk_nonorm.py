@@ -41,7 +41,7 @@ def test_decode_without_qk_norm_matches_oracle(fused):
     w = to_dev(base["conv_w"], "bf16")
     o = torch.empty((6, 32, 128), dtype=torch.float32, device="cuda")
     if fused:
-        gdn.decode_fused(dims, x, w, None, g, beta, o, sp, cp, gdn.decode_counters(dims, 6))
+        gdn.decode_fused(dims, x, w, None, g, beta, o, sp, cp)
     else:
         y = torch.empty((6, sh.channels), dtype=torch.float32, device="cuda")
         gdn.conv_update(dims, x, y, w, None, cp)

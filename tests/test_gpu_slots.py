@@ -163,7 +163,6 @@ def test_reused_slot_equals_never_used_slot():
     new = make_prefill(PREFILL_L4096, lens=(90,), shape=shape, s0_std=0.0, conv_state_std=0.0)
     conv_w = to_dev(new["conv_w"], "bf16")
     pool = gdn.SlotPool(dims, 4)  # zero states: fresh slots
-    counters = gdn.decode_counters(dims, 2)
 
     def prefill(slots, inp):
         T = inp["x"].shape[0]
@@ -188,7 +187,7 @@ def test_reused_slot_equals_never_used_slot():
         beta = to_dev(inp["beta"], "f32").repeat(n, 1)
         o = torch.empty((n, Hv, d), dtype=torch.float32, device="cuda")
         if fused:
-            gdn.decode_fused(dims, x, conv_w, None, g, beta, o, sp, cp, counters)
+            gdn.decode_fused(dims, x, conv_w, None, g, beta, o, sp, cp)
         else:
             y = torch.empty((n, C), dtype=torch.float32, device="cuda")
             gdn.conv_update(dims, x, y, conv_w, None, cp)
