@@ -30,6 +30,8 @@ from ._lib import (  # noqa: F401
     gdn_last_error,
     gdn_prefill_chunked,
     gdn_prefill_fused,
+    gdn_prefill_fused_static,
+    GDN_STATIC_SCRATCH_BYTES,
     gdn_prefill_fused_workspace_size,
     gdn_prefill_workspace_size,
     gdn_slot_copy,

@@ -24,7 +24,8 @@ GDN_MMA_AUTO, GDN_MMA_FP32, GDN_MMA_BF16X3 = 0, 1, 2
 GDN_PREFILL_AUTO, GDN_PREFILL_WHOLE, GDN_PREFILL_SEGMENTS = 0, 1, 2
 
 EXPORTED = ("gdn_dims_init", "gdn_conv_update", "gdn_prefill_workspace_size", "gdn_prefill_chunked",
-            "gdn_prefill_fused_workspace_size", "gdn_prefill_fused", "gdn_decode_batched", "gdn_decode_fused",
+            "gdn_prefill_fused_workspace_size", "gdn_prefill_fused", "gdn_prefill_fused_static", "gdn_decode_batched",
+            "gdn_decode_fused",
             "gdn_slot_copy", "gdn_slot_pointers", "gdn_last_error", "gdn_abi_version", "gdn_hbm_probe")
 
 
@@ -94,12 +95,13 @@ def _load() -> ctypes.CDLL:
     lib.gdn_prefill_chunked.argtypes = [D, P, I64, P, I64, P, I64, P, P, P, P, I32, I32, P, P, SZ, P]
     lib.gdn_prefill_fused_workspace_size.argtypes = [D, I32, I32, ctypes.POINTER(SZ)]
     lib.gdn_prefill_fused.argtypes = [D, P, I64, P, P, P, P, P, P, I32, I32, P, P, P, SZ, P]
+    lib.gdn_prefill_fused_static.argtypes = [D, P, I64, P, P, P, P, P, P, I32, I32, P, P, P]
     lib.gdn_decode_batched.argtypes = [D, P, I64, P, I64, P, I64, P, P, P, P, I32, P]
     lib.gdn_decode_fused.argtypes = [D, P, I64, P, P, P, P, P, P, P, P, I32, P]
     lib.gdn_slot_copy.argtypes = [D, P, P, P, P, I32, P]
     lib.gdn_slot_pointers.argtypes = [U64, I64, I32, P, I32, P, P]
     for fn in ("gdn_dims_init", "gdn_conv_update", "gdn_prefill_workspace_size", "gdn_prefill_chunked",
-               "gdn_prefill_fused_workspace_size", "gdn_prefill_fused", "gdn_decode_batched",
+               "gdn_prefill_fused_workspace_size", "gdn_prefill_fused", "gdn_prefill_fused_static", "gdn_decode_batched",
                "gdn_decode_fused", "gdn_slot_copy", "gdn_slot_pointers"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.gdn_hbm_probe.argtypes = [P, SZ, ctypes.c_uint32, P]
@@ -198,6 +200,17 @@ def gdn_prefill_fused(dims: gdn_dims, x, x_stride: int, conv_w, conv_b, g, beta,
                                 _ptr(conv_state_ptrs), _ptr(workspace), workspace_bytes,
                                 _stream(stream, x, o, state_ptrs))
     _check("gdn_prefill_fused", st)
+
+
+GDN_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def gdn_prefill_fused_static(dims: gdn_dims, x, x_stride: int, conv_w, conv_b, g, beta, o, cu_seqlens,
+                             num_seqs: int, total_tokens: int, state_ptrs, conv_state_ptrs, stream=None) -> None:
+    st = _LIB.gdn_prefill_fused_static(ctypes.byref(dims), _ptr(x), x_stride, _ptr(conv_w), _ptr(conv_b), _ptr(g),
+                                       _ptr(beta), _ptr(o), _ptr(cu_seqlens), num_seqs, total_tokens,
+                                       _ptr(state_ptrs), _ptr(conv_state_ptrs), _stream(stream, x, o, state_ptrs))
+    _check("gdn_prefill_fused_static", st)
 
 
 def gdn_decode_batched(dims: gdn_dims, q, q_stride: int, k, k_stride: int, v, v_stride: int, g, beta, o,

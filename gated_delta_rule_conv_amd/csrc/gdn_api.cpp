@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/gdn.h"
@@ -102,6 +103,117 @@ size_t fused_prefill_bytes(const gdn_dims* d, int32_t num_seqs, int32_t total_to
 int resolve_mma(const gdn_dims* d) {
   if (d->mma != GDN_MMA_AUTO) return d->mma;
   return d->in_dtype == GDN_F32 ? GDN_MMA_FP32 : GDN_MMA_BF16X3;
+}
+
+// gdn_prefill_fused's checks and launches, for it and for gdn_prefill_fused_static
+// (whose workspace is the library's own device array); fn names the caller in errors.
+// launch = false: the host checks only (the workspace pointer is then never used).
+gdn_status prefill_fused_impl(const char* fn, const gdn_dims* dims, const void* x, int64_t x_stride,
+                              const void* conv_w, const void* conv_b, const float* g, const float* beta, void* o,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                              const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, void* workspace,
+                              size_t workspace_bytes, void* stream, bool launch = true) {
+  if (gdn_status st = check_dims(dims, fn)) return st;
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_SHAPE, "%s: negative count", fn);
+  if (num_seqs == 0) {
+    if (total_tokens != 0) return fail(GDN_ERR_SHAPE, "%s: tokens without sequences", fn);
+    return GDN_OK;
+  }
+  if (!cu_seqlens || !state_ptrs || !conv_state_ptrs)
+    return fail(GDN_ERR_NULL, "%s: cu_seqlens, state_ptrs and conv_state_ptrs are required", fn);
+  const int64_t C = channels(dims);
+  const int64_t esz = dims->in_dtype == GDN_BF16 ? 2 : 4;
+  const int64_t qk = 2 * static_cast<int64_t>(dims->num_k_heads) * dims->head_dim;  // q | k channels
+  const int64_t vw = static_cast<int64_t>(dims->num_v_heads) * dims->head_dim;
+  if (total_tokens > 0) {
+    if (!x || !conv_w || !g || !beta || !o)
+      return fail(GDN_ERR_NULL, "%s: x, conv_w, g, beta and o are required", fn);
+    if (x_stride < 0) return fail(GDN_ERR_SHAPE, "%s: negative stride", fn);
+    if (total_tokens > 1 && x_stride < C)
+      return fail(GDN_ERR_SHAPE, "%s: x row stride %lld below the channel count %lld", fn,
+                  static_cast<long long>(x_stride), static_cast<long long>(C));
+    if (!aligned16(x) || !aligned16(conv_w) || (conv_b && !aligned16(conv_b)) || (x_stride * esz) % 16)
+      return fail(GDN_ERR_ALIGN, "%s: x, conv_w, conv_b must be 16-byte aligned and x_stride a multiple of 16 bytes",
+                  fn);
+  }
+  const size_t pre = gdn::prefill_workspace_bytes(dims->num_k_heads, dims->num_v_heads, dims->head_dim,
+                                                  dims->chunk_size, num_seqs, total_tokens, dims->prefill_form);
+  const size_t need = fused_prefill_bytes(dims, num_seqs, total_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(GDN_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  if (total_tokens == 0 || !launch) return GDN_OK;  // (zero-length sequences only: nothing changes)
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* yv = reinterpret_cast<float*>(static_cast<char*>(workspace) + pre);  // v part of the conv output
+  const int K = dims->conv_width;
+  const bool silu = dims->activation == GDN_ACT_SILU, bf16 = dims->in_dtype == GDN_BF16;
+  const char* xb = static_cast<const char*>(x);
+  const char* wb = static_cast<const char*>(conv_w);
+  const char* bb = static_cast<const char*>(conv_b);
+  // 1. the v channels' conv into the workspace (the conv states are committed in step 2)
+  gdn::ConvArgs cv{xb + qk * esz, x_stride, yv, vw, wb + qk * K * esz, bb ? bb + qk * esz : nullptr, cu_seqlens,
+                   conv_state_ptrs, num_seqs, total_tokens, static_cast<int32_t>(vw), K, silu, bf16, C,
+                   static_cast<int32_t>(qk)};
+  if (gdn_status st = hip_status(gdn::launch_conv_prefill_only(cv, s), fn)) return st;
+  // 2. the chunked prefill, the q/k conv inside its intra-chunk kernel
+  gdn::PrefillArgs a{};
+  a.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, yv, vw, g, beta, o, state_ptrs, dims->num_k_heads,
+                       dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
+                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0,
+                       dims->num_v_heads / dims->num_k_heads};
+  a.conv = gdn::ConvIn{x, x_stride, conv_w, conv_b, conv_state_ptrs, static_cast<int32_t>(C), K, silu, bf16};
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.chunk = dims->chunk_size;
+  a.form = dims->prefill_form;
+  a.mma = resolve_mma(dims);
+  a.workspace = workspace;
+  // (the chunk-0 workgroups of its intra-chunk kernel also commit every channel's conv
+  // state, after the last reader of the old rows)
+  return hip_status(gdn::launch_prefill(a, s), fn);
+}
+
+// The workspace of gdn_prefill_fused_static: a file-scope device array, one per GPU the
+// library runs on, held until the process ends (64 MiB: the workspace of about 1280 tokens
+// of a 16 q/k-head, 32 v-head, d = 128 layer, 48 KiB per token). Its device address on
+// each GPU is looked up once, with that GPU current, and kept; host code never uses the
+// array's own name as an address. Every call on a GPU uses the same array, so calls on one
+// GPU must not overlap in time (one stream, or streams ordered by events); the prefill
+// reads nothing from its workspace that it has not written in the same call, so nothing
+// needs clearing between calls.
+constexpr size_t kStaticScratchBytes = GDN_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the scratch array's device address on the GPU that `stream` runs on
+gdn_status static_scratch(hipStream_t stream, const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(GDN_ERR_HIP, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_status(e, fn);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, fn);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u))
+      return fail(GDN_ERR_HIP, "%s: static scratch address %p unusable", fn, p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
 }
 
 }  // namespace
@@ -230,68 +342,37 @@ gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stri
                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
                              const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  const char* fn = "gdn_prefill_fused";
+  return prefill_fused_impl("gdn_prefill_fused", dims, x, x_stride, conv_w, conv_b, g, beta, o, cu_seqlens, num_seqs,
+                            total_tokens, state_ptrs, conv_state_ptrs, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_fused_static(const gdn_dims* dims, const void* x, int64_t x_stride, const void* conv_w,
+                                    const void* conv_b, const float* g, const float* beta, void* o,
+                                    const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                                    const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, void* stream) {
+  const char* fn = "gdn_prefill_fused_static";
   if (gdn_status st = check_dims(dims, fn)) return st;
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_SHAPE, "%s: negative count", fn);
   if (num_seqs == 0) {
     if (total_tokens != 0) return fail(GDN_ERR_SHAPE, "%s: tokens without sequences", fn);
     return GDN_OK;
   }
-  if (!cu_seqlens || !state_ptrs || !conv_state_ptrs)
-    return fail(GDN_ERR_NULL, "%s: cu_seqlens, state_ptrs and conv_state_ptrs are required", fn);
-  const int64_t C = channels(dims);
-  const int64_t esz = dims->in_dtype == GDN_BF16 ? 2 : 4;
-  const int64_t qk = 2 * static_cast<int64_t>(dims->num_k_heads) * dims->head_dim;  // q | k channels
-  const int64_t vw = static_cast<int64_t>(dims->num_v_heads) * dims->head_dim;
-  if (total_tokens > 0) {
-    if (!x || !conv_w || !g || !beta || !o)
-      return fail(GDN_ERR_NULL, "%s: x, conv_w, g, beta and o are required", fn);
-    if (x_stride < 0) return fail(GDN_ERR_SHAPE, "%s: negative stride", fn);
-    if (total_tokens > 1 && x_stride < C)
-      return fail(GDN_ERR_SHAPE, "%s: x row stride %lld below the channel count %lld", fn,
-                  static_cast<long long>(x_stride), static_cast<long long>(C));
-    if (!aligned16(x) || !aligned16(conv_w) || (conv_b && !aligned16(conv_b)) || (x_stride * esz) % 16)
-      return fail(GDN_ERR_ALIGN, "%s: x, conv_w, conv_b must be 16-byte aligned and x_stride a multiple of 16 bytes",
-                  fn);
-  }
-  const size_t pre = gdn::prefill_workspace_bytes(dims->num_k_heads, dims->num_v_heads, dims->head_dim,
-                                                  dims->chunk_size, num_seqs, total_tokens, dims->prefill_form);
   const size_t need = fused_prefill_bytes(dims, num_seqs, total_tokens);
-  if (!workspace || workspace_bytes < need)
-    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, need, workspace_bytes,
-                workspace ? "" : " (NULL)");
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-    return fail(GDN_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
-  if (total_tokens == 0) return GDN_OK;  // (zero-length sequences only: nothing changes)
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float* yv = reinterpret_cast<float*>(static_cast<char*>(workspace) + pre);  // v part of the conv output
-  const int K = dims->conv_width;
-  const bool silu = dims->activation == GDN_ACT_SILU, bf16 = dims->in_dtype == GDN_BF16;
-  const char* xb = static_cast<const char*>(x);
-  const char* wb = static_cast<const char*>(conv_w);
-  const char* bb = static_cast<const char*>(conv_b);
-  // 1. the v channels' conv into the workspace (the conv states are committed in step 2)
-  gdn::ConvArgs cv{xb + qk * esz, x_stride, yv, vw, wb + qk * K * esz, bb ? bb + qk * esz : nullptr, cu_seqlens,
-                   conv_state_ptrs, num_seqs, total_tokens, static_cast<int32_t>(vw), K, silu, bf16, C,
-                   static_cast<int32_t>(qk)};
-  if (gdn_status st = hip_status(gdn::launch_conv_prefill_only(cv, s), fn)) return st;
-  // 2. the chunked prefill, the q/k conv inside its intra-chunk kernel
-  gdn::PrefillArgs a{};
-  a.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, yv, vw, g, beta, o, state_ptrs, dims->num_k_heads,
-                       dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
-                       dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0,
-                       dims->num_v_heads / dims->num_k_heads};
-  a.conv = gdn::ConvIn{x, x_stride, conv_w, conv_b, conv_state_ptrs, static_cast<int32_t>(C), K, silu, bf16};
-  a.cu_seqlens = cu_seqlens;
-  a.num_seqs = num_seqs;
-  a.total_tokens = total_tokens;
-  a.chunk = dims->chunk_size;
-  a.form = dims->prefill_form;
-  a.mma = resolve_mma(dims);
-  a.workspace = workspace;
-  // (the chunk-0 workgroups of its intra-chunk kernel also commit every channel's conv
-  // state, after the last reader of the old rows)
-  return hip_status(gdn::launch_prefill(a, s), fn);
+  if (need > kStaticScratchBytes)
+    return fail(GDN_ERR_WORKSPACE,
+                "%s: %d sequences of %d tokens need %zu bytes of workspace, above the library's static %zu "
+                "(split the batch, or pass a workspace to gdn_prefill_fused)",
+                fn, num_seqs, total_tokens, need, kStaticScratchBytes);
+  // every host check first (a stand-in for the array's address: 256-byte aligned, never used)
+  void* ws = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
+  if (gdn_status st = prefill_fused_impl(fn, dims, x, x_stride, conv_w, conv_b, g, beta, o, cu_seqlens, num_seqs,
+                                         total_tokens, state_ptrs, conv_state_ptrs, ws, kStaticScratchBytes, stream,
+                                         false))
+    return st;
+  if (total_tokens == 0) return GDN_OK;
+  if (gdn_status st = static_scratch(static_cast<hipStream_t>(stream), fn, &ws)) return st;
+  return prefill_fused_impl(fn, dims, x, x_stride, conv_w, conv_b, g, beta, o, cu_seqlens, num_seqs, total_tokens,
+                            state_ptrs, conv_state_ptrs, ws, kStaticScratchBytes, stream);
 }
 
 gdn_status gdn_decode_batched(const gdn_dims* dims, const float* q, int64_t q_stride, const float* k,

@@ -105,6 +105,14 @@ def prefill_fused(dims: gdn_dims, x: torch.Tensor, conv_w: torch.Tensor, conv_b,
                            workspace.numel() * workspace.element_size(), stream)
 
 
+def prefill_fused_static(dims: gdn_dims, x: torch.Tensor, conv_w: torch.Tensor, conv_b, g: torch.Tensor,
+                         beta: torch.Tensor, o: torch.Tensor, cu_seqlens: torch.Tensor, state_ptrs: torch.Tensor,
+                         conv_state_ptrs: torch.Tensor, stream=None) -> None:
+    """prefill_fused with the library's own 64 MiB device workspace: nothing allocated."""
+    _lib.gdn_prefill_fused_static(dims, x, x.stride(0), conv_w, conv_b, g, beta, o, cu_seqlens, state_ptrs.numel(),
+                                  x.shape[0], state_ptrs, conv_state_ptrs, stream)
+
+
 def decode(dims: gdn_dims, y: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, o: torch.Tensor,
            state_ptrs: torch.Tensor, stream=None) -> None:
     q, k, v = qkv_views(dims, y)
@@ -131,6 +139,6 @@ def prefill_fused_workspace(dims: gdn_dims, num_seqs: int, total_tokens: int, de
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-__all__ = ["SlotPool", "channels", "conv_update", "decode", "decode_fused", "prefill",
-           "prefill_fused", "prefill_fused_workspace", "prefill_workspace", "qkv_views", "torch_in_dtype", "GDN_F32",
-           "GDN_BF16"]
+__all__ = ["SlotPool", "channels", "conv_update", "decode", "decode_fused", "prefill", "prefill_fused",
+           "prefill_fused_static", "prefill_fused_workspace", "prefill_workspace", "qkv_views", "torch_in_dtype",
+           "GDN_F32", "GDN_BF16"]

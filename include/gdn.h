@@ -226,6 +226,29 @@ gdn_status gdn_prefill_fused(const gdn_dims* dims, const void* x, int64_t x_stri
                              size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * gdn_prefill_fused_static -- gdn_prefill_fused with no workspace argument, for callers
+ * that cannot allocate device memory (code being captured into a HIP graph, serving loops
+ * that may not call hipMalloc, harnesses that forbid it). The workspace is the library's
+ * own file-scope device array of 64 MiB (GDN_STATIC_SCRATCH_BYTES), one per GPU it runs on,
+ * held until the process ends; this entry point itself allocates nothing. The same
+ * kernels run on the same bits as gdn_prefill_fused.
+ *
+ *  Arguments as gdn_prefill_fused, without workspace and workspace_bytes.
+ *  Limit: gdn_prefill_fused_workspace_size(dims, num_seqs, total_tokens) must not exceed
+ *  GDN_STATIC_SCRATCH_BYTES (about 1280 tokens of a 16 q/k-head, 32 v-head, d = 128
+ *  layer); above it the call returns GDN_ERR_WORKSPACE and launches nothing.
+ *  Every call on one GPU uses that GPU's single array: calls on one GPU must not overlap
+ *  in time (one stream, or streams ordered by events); overlapping calls race. Nothing
+ *  in the array needs clearing between calls. The GPU is the one `stream` belongs to
+ *  (the current device for the null stream).
+ */
+#define GDN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_prefill_fused_static(const gdn_dims* dims, const void* x, int64_t x_stride, const void* conv_w,
+                                    const void* conv_b, const float* g, const float* beta, void* o,
+                                    const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                                    const uint64_t* state_ptrs, const uint64_t* conv_state_ptrs, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * gdn_decode_batched -- one token for each of m slots: L2 norm + one step of the gated
  * delta rule on each slot's state, in place ("System Design", "GDN Kernel Dispatch
  * Detail", decode branch: decay the temporal state and write the delta, then

@@ -364,3 +364,19 @@ def test_hbm_probe_checks():
     assert _status(gdn.gdn_hbm_probe, FAKE + 8, 16384)[0] == _lib.GDN_ERR_ALIGN
     assert _status(gdn.gdn_hbm_probe, FAKE, 16384 + 16)[0] == _lib.GDN_ERR_ALIGN
     gdn.gdn_hbm_probe(FAKE, 0)  # nothing to stream: nothing launched
+
+
+def test_prefill_fused_static_limit_checked_before_any_launch():
+    """The no-allocation prefill takes its workspace from the library's own 64 MiB device
+    array: a call needing more is refused on the host (nothing launched), as are the
+    arguments gdn_prefill_fused refuses."""
+    d = dims()
+    args = (FAKE, 8192, FAKE, None, FAKE, FAKE, FAKE, FAKE)  # x, x_stride, conv_w, conv_b, g, beta, o, cu
+    assert gdn.gdn_prefill_fused_workspace_size(d, 8, 15717) > gdn.GDN_STATIC_SCRATCH_BYTES
+    st, msg = _status(gdn.gdn_prefill_fused_static, d, *args, 8, 15717, FAKE, FAKE)
+    assert st == _lib.GDN_ERR_WORKSPACE and str(gdn.GDN_STATIC_SCRATCH_BYTES) in msg
+    assert gdn.gdn_prefill_fused_workspace_size(d, 1, 1024) <= gdn.GDN_STATIC_SCRATCH_BYTES
+    assert _status(gdn.gdn_prefill_fused_static, dims(conv_width=9), *args, 1, 64, FAKE, FAKE)[0] == \
+        _lib.GDN_ERR_UNSUPPORTED
+    assert _status(gdn.gdn_prefill_fused_static, d, *args[:7], None, 1, 64, FAKE, FAKE)[0] == _lib.GDN_ERR_NULL
+    gdn.gdn_prefill_fused_static(d, *args, 0, 0, None, None)  # no sequences: nothing to do
