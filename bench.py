@@ -490,16 +490,22 @@ def time_decode_kernel(rig: DecodeRig, rounds: int) -> float:
 
 
 def copy_probe(mib: int = 256, reps: int = 4) -> None:
-    """A plain device copy of known size, for scaling hardware byte counters."""
+    """Kernels of known traffic, for scaling hardware byte counters: torch's device copy
+    (reads mib MiB, writes mib MiB) and the library's in-place streaming pass
+    (gdn_hbm_probe: reads and writes the same mib MiB), reps launches each."""
     import torch
+
+    import gated_delta_rule_conv_amd as gdn
 
     n = mib * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(reps):
         dst.copy_(src)
+    for i in range(reps):
+        gdn.gdn_hbm_probe(src, src.numel() * 4, i + 1)
     torch.cuda.synchronize()
-    log(f"copy probe: {reps} copies of {mib} MiB")
+    log(f"copy probe: {reps} device copies and {reps} in-place streaming passes of {mib} MiB")
 
 
 def main() -> int:
