@@ -820,14 +820,22 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
 }
 
 // ------------------------------------------------------------------------ inter-chunk
+// LDS banking on gfx950 (measured with per-pattern bank-conflict counters): 64 banks of
+// 4 bytes; a 16-byte write is served 8 lanes at a time (lanes 8i .. 8i+7, one aligned
+// 128-byte window), an 8-byte write 16 lanes at a time (one 128-byte window), an 8-byte
+// read -- the transposing ds_read_b64_tr_b16 included -- 32 lanes at a time (one
+// 256-byte window); lanes of one such pass that hit the same bank at different addresses
+// are served one after another. The tiles below are laid out so that the reads of every
+// step, and the 16-byte writes, meet no conflict.
+//
 // K^ of the current chunk in LDS as a C x D matrix (one plane per operand part: bf16 hi
 // and lo, or fp32), written by rows from the K side's A fragments and read by columns as
 // the B operand of the state update, whose contraction runs over tokens. A row is D
-// values in 16-byte groups; group g of row t is stored at position g ^ swz(t). For the
-// row-wise fragment writes (8 lanes: 8 consecutive rows, one group) and the column-wise
-// reads (4 row groups 8 apart, 2 groups of one row each) that spreads the 16-byte groups
-// one instruction touches over 8 distinct positions of an aligned 128 bytes, so neither
-// access conflicts on LDS banks (at D = 128; smaller D only loses that spread).
+// values in 16-byte groups; group g of row t is stored at position g ^ swz(t). With bf16
+// planes (256-byte rows) swz(t) = 5 t mod 16: the 8 consecutive rows of a row-wise write
+// (one group each) land in 8 distinct groups, and the 32 lanes of a column read (rows t0 ..
+// t0 + 3 and t0 + 8 .. t0 + 11, ..., two 8-byte halves of one group each) in 32 distinct
+// 8-byte slots.
 template <int POL, int D, int C>
 struct KTile {
   using F = typename Mma<POL>::Frag;
@@ -837,7 +845,10 @@ struct KTile {
   static constexpr int GPR = ROW / 16;  // 16-byte groups per row
   static constexpr int PLANE = C * ROW;
   static constexpr int BYTES = POL == kPolBF16X3 ? 2 * PLANE : PLANE;
-  __device__ __forceinline__ static int swz(int t) { return ((t & 7) ^ (((t >> 3) & 3) << 1)) & (GPR - 1); }
+  __device__ __forceinline__ static int swz(int t) {
+    if constexpr (POL == kPolBF16X3) return (5 * t) & (GPR - 1);
+    return ((t & 7) ^ (((t >> 3) & 3) << 1)) & (GPR - 1);
+  }
   __device__ __forceinline__ static int off(int t, int d) {
     return t * ROW + ((((d * ES) >> 4) ^ swz(t)) << 4) + ((d * ES) & 15);
   }
@@ -899,6 +910,56 @@ struct KTile {
   }
 };
 
+// A 16-row operand tile in LDS (the state slice, 16 x D, and R^T, U^T, Us^T, 16 x C),
+// stored pre-split as Split<> does. bf16 planes: rows unpadded, 16-byte group g of row r
+// at position g ^ (r mod NG) (NG groups per row), so that a fragment read (16 rows, one
+// group column per 16 lanes) covers all banks once; a 4-value write is 8 bytes, half a
+// group. fp32: rows padded by 4 values, as Split<> stores them.
+template <int POL, int COLS>
+struct RowTile {
+  using M = Mma<POL>;
+  using F = typename M::Frag;
+  static constexpr bool kPlanes = POL == kPolBF16X3;
+  static constexpr int LD = kPlanes ? COLS : COLS + 4;  // elements per row
+  static constexpr int NG = COLS * 2 / 16;              // 16-byte groups per bf16 row
+  static constexpr int PLANE = 16 * COLS * 2;           // bytes per bf16 plane
+  static constexpr int BYTES = kPlanes ? 2 * PLANE : 16 * LD * 4;
+  __device__ __forceinline__ static int off(int row, int col) {  // byte offset in a bf16 plane
+    const int b = col * 2;
+    return row * (COLS * 2) + ((((b >> 4) ^ row) & (NG - 1)) << 4) + (b & 15);
+  }
+  // the fragment of row `row`, columns col .. col + KPL - 1 (col a multiple of KPL)
+  __device__ __forceinline__ static F load(const char* base, int row, int col) {
+    if constexpr (kPlanes) {
+      const char* p = base + off(row, col);
+      F f;
+      f.hi = *reinterpret_cast<const bf16x8*>(p);
+      f.lo = *reinterpret_cast<const bf16x8*>(p + PLANE);
+      return f;
+    } else {
+      return Split<POL>::load(base, 16, LD, row, col);
+    }
+  }
+  // 4 consecutive values of row `row` from column col (a multiple of 4)
+  __device__ __forceinline__ static void store4(char* base, int row, int col, const float* x) {
+    if constexpr (kPlanes) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 h, l;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 t = static_cast<__bf16>(x[e]);
+        h[e] = t;
+        l[e] = static_cast<__bf16>(x[e] - static_cast<float>(t));
+      }
+      char* p = base + off(row, col);
+      *reinterpret_cast<bf16x4*>(p) = h;
+      *reinterpret_cast<bf16x4*>(p + PLANE) = l;
+    } else {
+      Split<POL>::store(base, 16, LD, row, col, x, 4);
+    }
+  }
+};
+
 // Everything one wave reads from global memory for one chunk; loaded one chunk ahead so
 // the loads overlap the previous chunk's arithmetic. Waves 0-3 ("K side") hold K^ rows
 // and T rows, waves 4-7 ("Q side") hold Q^ rows and P rows, of token tile wave % 4.
@@ -941,11 +1002,11 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
   constexpr int NT = C / 16;      // token tiles per chunk
   constexpr int ST = D / 16;      // 16-column tiles of the state slice (one per wave)
   constexpr int NV = In::NV, NK = In::NK;
-  constexpr int PADE = POL == kPolBF16X3 ? 8 : 4;  // row padding in elements
-  constexpr int SLD = D + PADE;                     // LDS row strides
-  constexpr int RLD = C + PADE;
-  constexpr int S_BYTES = kDVB * SLD * 4;
-  constexpr int R_BYTES = kDVB * RLD * 4;
+  using TS = RowTile<POL, D>;  // the state slice
+  using TR = RowTile<POL, C>;  // R^T, U^T, Us^T
+  static_assert(kDVB == 16, "16-row tiles");
+  constexpr int S_BYTES = TS::BYTES;
+  constexpr int R_BYTES = TR::BYTES;
   __shared__ __attribute__((aligned(16))) char lds[S_BYTES + 3 * R_BYTES + KT::BYTES];
   char* Sl = lds;                     // state slice  [16][D]   B operand of K^S^T, Q^S^T
   char* Rt = lds + S_BYTES;           // R^T          [16][C]   B operand of T R
@@ -1022,7 +1083,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
       for (int rr = 0; rr < 4; ++rr) sacc[rr] = (mrow && blk * kDVB + l16 == scol + rr) ? 1.f : 0.f;
     }
     float sv[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
-    SP::store(Sl, kDVB, SLD, l16, scol, sv, 4);
+    TS::store4(Sl, l16, scol, sv);
   }
 
   // The operand loads of one chunk, in three groups so that the prefetching variant can
@@ -1056,16 +1117,22 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
     in.egn = gb[C - 1];
     if (active) {
       const char* mrows = tp + (qside ? static_cast<size_t>(NT) * NK * FIO::BYTES : 0);
+      // (fragments wholly above the diagonal are not in the workspace, and their products
+      // are skipped; tt is uniform over the wave)
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        in.mf[kk] = FIO::load(mrows + static_cast<size_t>(tt * NK + kk) * FIO::BYTES, lane);
-      // the factors of this lane's 4 output rows are 4 consecutive floats of each array
+        if (kk * KSTEP < tt * 16 + 16)
+          in.mf[kk] = FIO::load(mrows + static_cast<size_t>(tt * NK + kk) * FIO::BYTES, lane);
+      // the factors of this lane's 4 output rows are 4 consecutive floats of each array;
+      // the Q side uses e^gam only
       const float4 g4 = *reinterpret_cast<const float4*>(gb + tt * 16 + 4 * lg);
-      const float4 b4 = *reinterpret_cast<const float4*>(gb + C + tt * 16 + 4 * lg);
       in.eg[0] = g4.x; in.eg[1] = g4.y; in.eg[2] = g4.z; in.eg[3] = g4.w;
-      in.bt[0] = b4.x; in.bt[1] = b4.y; in.bt[2] = b4.z; in.bt[3] = b4.w;
-      const float4 d4 = *reinterpret_cast<const float4*>(gb + 2 * C + tt * 16 + 4 * lg);
-      in.ed[0] = d4.x; in.ed[1] = d4.y; in.ed[2] = d4.z; in.ed[3] = d4.w;
+      if (!qside) {
+        const float4 b4 = *reinterpret_cast<const float4*>(gb + C + tt * 16 + 4 * lg);
+        in.bt[0] = b4.x; in.bt[1] = b4.y; in.bt[2] = b4.z; in.bt[3] = b4.w;
+        const float4 d4 = *reinterpret_cast<const float4*>(gb + 2 * C + tt * 16 + 4 * lg);
+        in.ed[0] = d4.x; in.ed[1] = d4.y; in.ed[2] = d4.z; in.ed[3] = d4.w;
+      }
       if (with_v) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -1090,7 +1157,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
     f32x4 a3[3];
     zero3(a3);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) M::mma3(a3, in.af[v], SP::load(Sl, kDVB, SLD, l16, kl + v * KSTEP));
+    for (int v = 0; v < NV; ++v) M::mma3(a3, in.af[v], TS::load(Sl, l16, kl + v * KSTEP));
     const f32x4 acc = total(a3);
     if (!qside) {
       // K^ rows of this token tile into LDS for the update (read after two barriers)
@@ -1102,7 +1169,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
         const float vt = (tt * 16 + 4 * lg + rr < in.n) ? in.vv[rr] : 0.f;
         rv[rr] = in.bt[rr] * (vt - in.eg[rr] * acc[rr]);
       }
-      SP::store(Rt, kDVB, RLD, l16, tt * 16 + 4 * lg, rv, 4);
+      TR::store4(Rt, l16, tt * 16 + 4 * lg, rv);
     } else {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) oacc[rr] = in.eg[rr] * acc[rr];
@@ -1115,7 +1182,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       if (kk * KSTEP < tt * 16 + 16) {
-        const F rf = (kFullK || kk * KSTEP + kl < C) ? SP::load(Rt, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+        const F rf = (kFullK || kk * KSTEP + kl < C) ? TR::load(Rt, l16, kk * KSTEP + kl) : SP::zero();
         M::mma3(u3, in.mf[kk], rf);
       }
     }
@@ -1126,8 +1193,8 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
       ut[rr] = uacc[rr];
       us[rr] = in.ed[rr] * uacc[rr];
     }
-    SP::store(Ut, kDVB, RLD, l16, tt * 16 + 4 * lg, ut, 4);
-    SP::store(Us, kDVB, RLD, l16, tt * 16 + 4 * lg, us, 4);
+    TR::store4(Ut, l16, tt * 16 + 4 * lg, ut);
+    TR::store4(Us, l16, tt * 16 + 4 * lg, us);
   };
   // rows t < n of this wave's token tile of O for chunk c
   auto store_o = [&](int c, int n, const f32x4& o) {
@@ -1151,7 +1218,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       if (kk * KSTEP < tt * 16 + 16) {
-        const F uf = (kFullK || kk * KSTEP + kl < C) ? SP::load(Ut, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+        const F uf = (kFullK || kk * KSTEP + kl < C) ? TR::load(Ut, l16, kk * KSTEP + kl) : SP::zero();
         M::mma3(o3, in.mf[kk], uf);
       }
     }
@@ -1167,7 +1234,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
     for (int kk = 0; kk < NK; ++kk) {
       const bool live = kFullK || kk * KSTEP + kl < C;
       const F kc = live ? KT::column16(Kl, wave * 16, kk * KSTEP + kl, l16) : SP::zero();
-      const F ub = live ? SP::load(Us, kDVB, RLD, l16, kk * KSTEP + kl) : SP::zero();
+      const F ub = live ? TR::load(Us, l16, kk * KSTEP + kl) : SP::zero();
       M::mma3(s3, kc, ub);
     }
     const f32x4 upd = total(s3);
@@ -1175,7 +1242,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) sv[rr] = fmaf(sacc[rr], egn, upd[rr]);
     sacc = f32x4{sv[0], sv[1], sv[2], sv[3]};
-    SP::store(Sl, kDVB, SLD, l16, scol, sv, 4);
+    TS::store4(Sl, l16, scol, sv);
   };
 
   if constexpr (PF) {
