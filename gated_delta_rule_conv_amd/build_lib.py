@@ -31,10 +31,8 @@ FLAGS = [
 ]
 
 
-# Per-file additions. decode.hip: the fused decode kernel's one counter atomic is issued
-# early and its result used only at the end; the default wave-level atomic combining
-# would consume the result at once and stall wave 0 on the round trip.
-FILE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+# Per-file additions (none at present).
+FILE_FLAGS: dict = {}
 
 
 def hipcc() -> str:
