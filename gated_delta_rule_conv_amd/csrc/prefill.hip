@@ -34,8 +34,9 @@
 //                        T R, P U and U^T K run on MFMA (K^ is staged through LDS for the
 //                        last one, whose contraction runs over tokens). The 16-row slices
 //                        of one head are mapped to one XCD so they share K, Q, T and P
-//                        through its L2. Below 512 workgroups one runs per CU and prefetches
-//                        the next chunk's operands; from 512 on two share a CU instead.
+//                        through its L2. Each workgroup prefetches the next chunk's
+//                        operands; where 16-row workgroups would be 512 or more, a
+//                        workgroup takes two 16-row blocks of a head (one CU each).
 // In the chunk-parallel form the last launch is replaced by three: the inter-chunk kernel
 // computing every segment's affine state map, segment_scan_kernel forming the segments'
 // start states, and the inter-chunk kernel producing every segment's outputs.
@@ -60,8 +61,8 @@ constexpr int kThreads = 512;      // intra-chunk workgroup: 8 waves
 constexpr int kWaves = 8;
 constexpr int kInterThreads = 512; // inter-chunk workgroup: 8 waves
 constexpr int kDVB = 16;           // state rows per inter-chunk workgroup
-// Inter-chunk variant choice: with at least two workgroups per CU (MI355X: 256 CUs) the
-// lean, two-per-CU variant runs; below that the one-per-CU variant that prefetches.
+// Inter-chunk variant choice: where 16-row workgroups would fill every CU (MI355X: 256)
+// twice over, a workgroup takes two 16-row blocks; below that one (both prefetch).
 constexpr int kInterPrefetchMaxCUs = 256;
 constexpr int kMetaThreads = 1024;
 constexpr int kLptMaxSeqs = 256;   // longest-first ordering only up to this many sequences
@@ -963,7 +964,7 @@ struct RowTile {
 // Everything one wave reads from global memory for one chunk; loaded one chunk ahead so
 // the loads overlap the previous chunk's arithmetic. Waves 0-3 ("K side") hold K^ rows
 // and T rows, waves 4-7 ("Q side") hold Q^ rows and P rows, of token tile wave % 4.
-template <int POL, int D, int C>
+template <int POL, int D, int C, int NR>
 struct ChunkIn {
   using F = typename Mma<POL>::Frag;
   static constexpr int KSTEP = Mma<POL>::KSTEP;
@@ -971,7 +972,8 @@ struct ChunkIn {
   static constexpr int NK = (C + KSTEP - 1) / KSTEP;  // k-steps over the chunk's tokens
   F af[NV];     // K^ (or Q^) row of token 16*tt + l16
   F mf[NK];     // T (or P) row of token 16*tt + l16
-  float vv[4];  // v at the 4 output rows this lane holds (K side; rows >= n masked at use)
+  float vv[NR][4];  // v at the 4 output rows this lane holds in each of the workgroup's NR
+                    // row blocks (K side; rows >= n masked at use)
   float eg[4];  // e^gam, beta and e^{gam_n - gam} at those rows
   float bt[4];
   float ed[4];
@@ -989,12 +991,21 @@ constexpr int kModeWhole = 0;
 constexpr int kModeTransfer = 1;
 constexpr int kModeSegment = 2;
 
-template <int POL, int D, int C, bool PF, int MODE>
-__global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(PrefillArgs a, Workspace w) {
+// NR: 16-row state blocks per workgroup. NR = 2 (whole sequences) serves two blocks of a
+// head with one set of operand loads. A step is bound by the CU's memory pipe (each
+// streams ~96 KiB of K^, Q^, T and P through it, at L2 latency), so where a launch has
+// workgroups to spare, one two-block workgroup per CU that prefetches the next chunk moves
+// half the operand bytes per state row of two one-block workgroups sharing the CU, and
+// keeps its loads in flight across the step (on the ragged 8-sequence pack: 537 -> 357 us;
+// two blocks without the prefetch lost to two one-block workgroups). Each block's
+// arithmetic is the one-block kernel's, so the results are the same bits.
+template <int POL, int D, int C, bool PF, int MODE, int NR = 1>
+__global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_chunk_kernel(PrefillArgs a, Workspace w) {
+  static_assert(NR == 1 || (NR == 2 && MODE == kModeWhole), "two blocks per workgroup: whole sequences only");
   using M = Mma<POL>;
   using SP = Split<POL>;
   using F = typename M::Frag;
-  using In = ChunkIn<POL, D, C>;
+  using In = ChunkIn<POL, D, C, NR>;
   using FIO = FragIO<POL>;
   using KT = KTile<POL, D, C>;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
@@ -1007,15 +1018,15 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
   static_assert(kDVB == 16, "16-row tiles");
   constexpr int S_BYTES = TS::BYTES;
   constexpr int R_BYTES = TR::BYTES;
-  __shared__ __attribute__((aligned(16))) char lds[S_BYTES + 3 * R_BYTES + KT::BYTES];
-  char* Sl = lds;                     // state slice  [16][D]   B operand of K^S^T, Q^S^T
-  char* Rt = lds + S_BYTES;           // R^T          [16][C]   B operand of T R
-  char* Ut = Rt + R_BYTES;            // U^T          [16][C]   B operand of P U
-  char* Us = Ut + R_BYTES;            // (e^{gam_n-gam} U)^T    A operand of the update
-  char* Kl = Us + R_BYTES;            // K^           [C][D]    B operand of the update
+  __shared__ __attribute__((aligned(16))) char lds[NR * (S_BYTES + 3 * R_BYTES) + KT::BYTES];
+  char* Sl = lds;                     // state slices [NR][16][D]  B operand of K^S^T, Q^S^T
+  char* Rt = lds + NR * S_BYTES;      // R^T          [NR][16][C]  B operand of T R
+  char* Ut = Rt + NR * R_BYTES;       // U^T          [NR][16][C]  B operand of P U
+  char* Us = Ut + NR * R_BYTES;       // (e^{gam_n-gam} U)^T       A operand of the update
+  char* Kl = Us + NR * R_BYTES;       // K^           [C][D]       B operand of the update
 
   const RecurArgs& r = a.r;
-  constexpr int RB = MODE == kModeTransfer ? 2 * NBLK : NBLK;  // row blocks per head
+  constexpr int RB = MODE == kModeTransfer ? 2 * NBLK : NBLK / NR;  // workgroups per head
   const int per_unit = RB * r.hv;
   const int L = blockIdx.x;
   const int zi = L / per_unit;
@@ -1039,7 +1050,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
     if (MODE == kModeTransfer && last_seg) return;  // (the last segment's map is never used)
   }
   const bool mrow = MODE == kModeTransfer && rb < NBLK;  // a row block of M (else of B, or the state)
-  const int blk = MODE == kModeTransfer && !mrow ? rb - NBLK : rb;
+  const int blk = MODE == kModeTransfer && !mrow ? rb - NBLK : rb * NR;  // first 16-row block
   const int start = a.cu_seqlens[s];
   const int len = a.cu_seqlens[s + 1] - start;
   if (len <= 0) return;
@@ -1071,19 +1082,22 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
   // row l16, columns 16 w + 4 lg .. + 3 (the update is computed transposed, so that these
   // are 4 consecutive values: one 16-byte global and one 8- or 16-byte LDS access).
   const int scol = wave * 16 + 4 * lg;
-  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 sacc[NR];
   if (has_tile) {
-    if constexpr (MODE == kModeWhole) {
-      sacc = *reinterpret_cast<const f32x4*>(Sg + l16 * D + scol);
-    } else if constexpr (MODE == kModeSegment) {
-      sacc = *reinterpret_cast<const f32x4*>(
-          w.zs + (static_cast<size_t>(seg) * r.hv + j) * mat + static_cast<size_t>(blk * kDVB + l16) * D + scol);
-    } else {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) sacc[rr] = (mrow && blk * kDVB + l16 == scol + rr) ? 1.f : 0.f;
+    for (int q = 0; q < NR; ++q) {
+      if constexpr (MODE == kModeWhole) {
+        sacc[q] = *reinterpret_cast<const f32x4*>(Sg + (q * kDVB + l16) * D + scol);
+      } else if constexpr (MODE == kModeSegment) {
+        sacc[q] = *reinterpret_cast<const f32x4*>(
+            w.zs + (static_cast<size_t>(seg) * r.hv + j) * mat + static_cast<size_t>(blk * kDVB + l16) * D + scol);
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sacc[q][rr] = (mrow && blk * kDVB + l16 == scol + rr) ? 1.f : 0.f;
+      }
+      float sv[4] = {sacc[q][0], sacc[q][1], sacc[q][2], sacc[q][3]};
+      TS::store4(Sl + q * S_BYTES, l16, scol, sv);
     }
-    float sv[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
-    TS::store4(Sl, l16, scol, sv);
   }
 
   // The operand loads of one chunk, in three groups so that the prefetching variant can
@@ -1141,7 +1155,9 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
           // are masked where the value is used (using a load in the step that issues it
           // would wait for every load before it, the prefetch included)
           const int tc = min(t, in.n - 1);
-          in.vv[rr] = vscale * r.v[static_cast<int64_t>(t0 + tc) * r.v_stride + j * D + blk * kDVB + l16];
+#pragma unroll
+          for (int q = 0; q < NR; ++q)
+            in.vv[q][rr] = vscale * r.v[static_cast<int64_t>(t0 + tc) * r.v_stride + j * D + (blk + q) * kDVB + l16];
         }
       }
     }
@@ -1153,96 +1169,119 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
 
   // phase 1: X = K^ S^T (K side; then R = diag(beta) (V - diag(e^gam) X) into LDS and the
   // K^ rows into the K^ tile) or Y = Q^ S^T (Q side; returns e^gam Y)
-  auto phase1 = [&](const In& in, f32x4& oacc) {
-    f32x4 a3[3];
-    zero3(a3);
-#pragma unroll
-    for (int v = 0; v < NV; ++v) M::mma3(a3, in.af[v], TS::load(Sl, l16, kl + v * KSTEP));
-    const f32x4 acc = total(a3);
+  auto phase1 = [&](const In& in, f32x4 (&oacc)[NR]) {
     if (!qside) {
       // K^ rows of this token tile into LDS for the update (read after two barriers)
 #pragma unroll
       for (int v = 0; v < NV; ++v) KT::put(Kl, tt * 16 + l16, v * KSTEP + kl, in.af[v]);
-      float rv[4];
+    }
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float vt = (tt * 16 + 4 * lg + rr < in.n) ? in.vv[rr] : 0.f;
-        rv[rr] = in.bt[rr] * (vt - in.eg[rr] * acc[rr]);
+    for (int q = 0; q < NR; ++q) {
+      f32x4 a3[3];
+      zero3(a3);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) M::mma3(a3, in.af[v], TS::load(Sl + q * S_BYTES, l16, kl + v * KSTEP));
+      const f32x4 acc = total(a3);
+      if (!qside) {
+        float rv[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float vt = (tt * 16 + 4 * lg + rr < in.n) ? in.vv[q][rr] : 0.f;
+          rv[rr] = in.bt[rr] * (vt - in.eg[rr] * acc[rr]);
+        }
+        TR::store4(Rt + q * R_BYTES, l16, tt * 16 + 4 * lg, rv);
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) oacc[q][rr] = in.eg[rr] * acc[rr];
       }
-      TR::store4(Rt, l16, tt * 16 + 4 * lg, rv);
-    } else {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) oacc[rr] = in.eg[rr] * acc[rr];
     }
   };
   // phase 2 (K side): U = T R, T lower triangular; U^T and (e^{gam_n - gam} U)^T into LDS
   auto phase2 = [&](const In& in) {
-    f32x4 u3[3];
-    zero3(u3);
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      if (kk * KSTEP < tt * 16 + 16) {
-        const F rf = (kFullK || kk * KSTEP + kl < C) ? TR::load(Rt, l16, kk * KSTEP + kl) : SP::zero();
-        M::mma3(u3, in.mf[kk], rf);
+    for (int q = 0; q < NR; ++q) {
+      f32x4 u3[3];
+      zero3(u3);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        if (kk * KSTEP < tt * 16 + 16) {
+          const F rf =
+              (kFullK || kk * KSTEP + kl < C) ? TR::load(Rt + q * R_BYTES, l16, kk * KSTEP + kl) : SP::zero();
+          M::mma3(u3, in.mf[kk], rf);
+        }
       }
-    }
-    const f32x4 uacc = total(u3);
-    float ut[4], us[4];
+      const f32x4 uacc = total(u3);
+      float ut[4], us[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      ut[rr] = uacc[rr];
-      us[rr] = in.ed[rr] * uacc[rr];
+      for (int rr = 0; rr < 4; ++rr) {
+        ut[rr] = uacc[rr];
+        us[rr] = in.ed[rr] * uacc[rr];
+      }
+      TR::store4(Ut + q * R_BYTES, l16, tt * 16 + 4 * lg, ut);
+      TR::store4(Us + q * R_BYTES, l16, tt * 16 + 4 * lg, us);
     }
-    TR::store4(Ut, l16, tt * 16 + 4 * lg, ut);
-    TR::store4(Us, l16, tt * 16 + 4 * lg, us);
   };
   // rows t < n of this wave's token tile of O for chunk c
-  auto store_o = [&](int c, int n, const f32x4& o) {
+  auto store_o = [&](int c, int n, const f32x4 (&o)[NR]) {
     const int t0 = start + c * C;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int t = tt * 16 + 4 * lg + rr;
-      if (kOut && t < n) {
-        const int64_t e = (static_cast<int64_t>(t0 + t) * r.hv + j) * D + blk * kDVB + l16;
-        if (r.o_bf16)
-          static_cast<uint16_t*>(r.o)[e] = f32_to_bf16_rne(o[rr]);
-        else
-          static_cast<float*>(r.o)[e] = o[rr];
+    for (int q = 0; q < NR; ++q) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int t = tt * 16 + 4 * lg + rr;
+        if (kOut && t < n) {
+          const int64_t e = (static_cast<int64_t>(t0 + t) * r.hv + j) * D + (blk + q) * kDVB + l16;
+          if (r.o_bf16)
+            static_cast<uint16_t*>(r.o)[e] = f32_to_bf16_rne(o[q][rr]);
+          else
+            static_cast<float*>(r.o)[e] = o[q][rr];
+        }
       }
     }
   };
   // phase 3, Q side: O = e^gam Y + P U
-  auto phase3_out = [&](const In& in, f32x4& oacc) {
-    f32x4 o3[3];
-    zero3(o3);
+  auto phase3_out = [&](const In& in, f32x4 (&oacc)[NR]) {
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      if (kk * KSTEP < tt * 16 + 16) {
-        const F uf = (kFullK || kk * KSTEP + kl < C) ? TR::load(Ut, l16, kk * KSTEP + kl) : SP::zero();
-        M::mma3(o3, in.mf[kk], uf);
+    for (int q = 0; q < NR; ++q) {
+      f32x4 o3[3];
+      zero3(o3);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        if (kk * KSTEP < tt * 16 + 16) {
+          const F uf =
+              (kFullK || kk * KSTEP + kl < C) ? TR::load(Ut + q * R_BYTES, l16, kk * KSTEP + kl) : SP::zero();
+          M::mma3(o3, in.mf[kk], uf);
+        }
       }
+      oacc[q] += total(o3);
     }
-    oacc += total(o3);
   };
   // phase 3, state tile `wave`: S <- e^{gam_n} S + Us^T K^, computed as its transpose
   // K^T Us (A operand: columns of K^, B operand: rows of Us)
   auto phase3_state = [&](const In& in) {
     const float egn = in.egn;
-    f32x4 s3[3];
-    zero3(s3);
+    f32x4 s3[NR][3];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) zero3(s3[q]);
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const bool live = kFullK || kk * KSTEP + kl < C;
       const F kc = live ? KT::column16(Kl, wave * 16, kk * KSTEP + kl, l16) : SP::zero();
-      const F ub = live ? TR::load(Us, l16, kk * KSTEP + kl) : SP::zero();
-      M::mma3(s3, kc, ub);
-    }
-    const f32x4 upd = total(s3);
-    float sv[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) sv[rr] = fmaf(sacc[rr], egn, upd[rr]);
-    sacc = f32x4{sv[0], sv[1], sv[2], sv[3]};
-    TS::store4(Sl, l16, scol, sv);
+      for (int q = 0; q < NR; ++q) {
+        const F ub = live ? TR::load(Us + q * R_BYTES, l16, kk * KSTEP + kl) : SP::zero();
+        M::mma3(s3[q], kc, ub);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      const f32x4 upd = total(s3[q]);
+      float sv[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sv[rr] = fmaf(sacc[q][rr], egn, upd[rr]);
+      sacc[q] = f32x4{sv[0], sv[1], sv[2], sv[3]};
+      TS::store4(Sl + q * S_BYTES, l16, scol, sv);
+    }
   };
 
   if constexpr (PF) {
@@ -1265,7 +1304,7 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
     auto step_k = [&](int c, const In& in, In& nxt, int cn) {
       wait_vmem();
       load_a(cn, nxt);
-      f32x4 unused;
+      f32x4 unused[NR];
       if (active) phase1(in, unused);
       __syncthreads();
       if (active) phase2(in);
@@ -1274,12 +1313,14 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
       if (has_tile) phase3_state(in);
       __syncthreads();
     };
-    f32x4 oprev = {0.f, 0.f, 0.f, 0.f};  // outputs of the previous chunk, stored one step late
-    int nprev = 0;                          // (0: nothing to store)
+    f32x4 oprev[NR];  // outputs of the previous chunk, stored one step late
+    int nprev = 0;    // (0: nothing to store)
     auto step_q = [&](int c, const In& in, In& nxt, int cn) {
       wait_vmem();
       store_o(c - 1, nprev, oprev);
-      f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 oacc[NR];
+#pragma unroll
+      for (int q = 0; q < NR; ++q) oacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (active) phase1(in, oacc);
       __syncthreads();
       load(cn, nxt, false);
@@ -1287,7 +1328,8 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
       if (active) phase3_out(in, oacc);
       if (has_tile) phase3_state(in);
       __syncthreads();
-      oprev = oacc;
+#pragma unroll
+      for (int q = 0; q < NR; ++q) oprev[q] = oacc[q];
       nprev = in.n;
     };
     if (!qside) {
@@ -1311,7 +1353,9 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
     __syncthreads();  // Sl filled
     for (int c = c_begin; c < c_end; ++c) {
       load(c, in0, true);  // (the Q side loads v too: fewer registers than a branch)
-      f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 oacc[NR];
+#pragma unroll
+      for (int q = 0; q < NR; ++q) oacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (active) phase1(in0, oacc);
       __syncthreads();
       if (active && !qside) phase2(in0);
@@ -1331,13 +1375,14 @@ __global__ __launch_bounds__(kInterThreads, PF ? 1 : 2) void inter_chunk_kernel(
         // M^T[n][i] for row i = blk*16 + l16 and columns n = scol + rr of M
         float* mt = w.mt + (static_cast<size_t>(seg) * r.hv + j) * mat;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) mt[static_cast<size_t>(scol + rr) * D + blk * kDVB + l16] = sacc[rr];
+        for (int rr = 0; rr < 4; ++rr) mt[static_cast<size_t>(scol + rr) * D + blk * kDVB + l16] = sacc[0][rr];
       } else {
         float* bt = w.bt + (static_cast<size_t>(seg) * r.hv + j) * mat + static_cast<size_t>(blk * kDVB) * D;
-        *reinterpret_cast<f32x4*>(bt + l16 * D + scol) = sacc;
+        *reinterpret_cast<f32x4*>(bt + l16 * D + scol) = sacc[0];
       }
     } else if (last_seg) {
-      *reinterpret_cast<f32x4*>(Sg + l16 * D + scol) = sacc;
+#pragma unroll
+      for (int q = 0; q < NR; ++q) *reinterpret_cast<f32x4*>(Sg + (q * kDVB + l16) * D + scol) = sacc[q];
     }
   }
 }
@@ -1478,8 +1523,8 @@ hipError_t launch_chunked(const PrefillArgs& a, const Workspace& w, hipStream_t 
     return hipGetLastError();
   }
   const unsigned blocks = static_cast<unsigned>(NBLK * a.r.hv * a.num_seqs);
-  if (blocks >= 2 * kInterPrefetchMaxCUs)
-    inter_chunk_kernel<POL, D, C, false, kModeWhole><<<blocks, kInterThreads, 0, s>>>(a, w);
+  if (blocks >= 2 * kInterPrefetchMaxCUs)  // two 16-row blocks per workgroup (NBLK is even)
+    inter_chunk_kernel<POL, D, C, true, kModeWhole, 2><<<blocks / 2, kInterThreads, 0, s>>>(a, w);
   else
     inter_chunk_kernel<POL, D, C, true, kModeWhole><<<blocks, kInterThreads, 0, s>>>(a, w);
   return hipGetLastError();

@@ -158,12 +158,12 @@ def test_packed_equals_solo_bit_exact():
 
 
 def test_one_and_two_workgroups_per_cu_variants_bit_exact():
-    """The inter-chunk launch has two variants with the same arithmetic: below 512
-    workgroups one per CU with the next chunk's operands prefetched, from 512 on two per
-    CU without prefetch. At 16/32 heads and d = 128 a sequence alone has 256 workgroups and
-    packed with a second sequence 512, so the two runs take different variants; the
+    """The inter-chunk launch has two variants with the same arithmetic: below 512 16-row
+    blocks one block per workgroup, from 512 on two blocks of a head per workgroup (one set
+    of operand loads for both). At 16/32 heads and d = 128 a sequence alone has 256 blocks
+    and packed with a second sequence 512, so the two runs take different variants; the
     sequence's o and state must agree bit for bit."""
-    announce("prefill inter variants (prefetch vs two per CU) bit-exact")
+    announce("prefill inter variants (one vs two 16-row blocks per workgroup) bit-exact")
     lens = (300, 130)
     inp = make_prefill(PREFILL_L4096, lens=lens, s0_std=0.02, conv_state_std=1.0)
     o, S = PrefillRun(inp).run()
@@ -174,7 +174,7 @@ def test_one_and_two_workgroups_per_cu_variants_bit_exact():
     np.testing.assert_array_equal(o1.view(np.int32), o[:300].view(np.int32))
     np.testing.assert_array_equal(S1[0].view(np.int32), S[0].view(np.int32))
     ref = _oracle(inp)
-    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16, label="two per CU")
+    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16, label="two blocks per workgroup")
 
 
 def test_split_and_decode_continuation():
