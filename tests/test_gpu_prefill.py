@@ -157,15 +157,18 @@ def test_packed_equals_solo_bit_exact():
         np.testing.assert_array_equal(S1[0].view(np.int32), S[s].view(np.int32))
 
 
-def test_one_and_two_workgroups_per_cu_variants_bit_exact():
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+def test_one_and_two_workgroups_per_cu_variants_bit_exact(in_dtype):
     """The inter-chunk launch has two variants with the same arithmetic: below 512 16-row
     blocks one block per workgroup, from 512 on two blocks of a head per workgroup (one set
     of operand loads for both). At 16/32 heads and d = 128 a sequence alone has 256 blocks
     and packed with a second sequence 512, so the two runs take different variants; the
-    sequence's o and state must agree bit for bit."""
-    announce("prefill inter variants (one vs two 16-row blocks per workgroup) bit-exact")
+    sequence's o and state must agree bit for bit, with either product precision (bf16x3
+    for bf16 input, fp32 MFMA for fp32 input)."""
+    announce(f"prefill inter variants (one vs two 16-row blocks per workgroup) bit-exact, {in_dtype}")
     lens = (300, 130)
-    inp = make_prefill(PREFILL_L4096, lens=lens, s0_std=0.02, conv_state_std=1.0)
+    shape = LayerShape(16, 32, 128, conv_width=4, chunk=64, in_dtype=in_dtype)
+    inp = make_prefill(PREFILL_L4096, lens=lens, shape=shape, s0_std=0.02, conv_state_std=1.0)
     o, S = PrefillRun(inp).run()
     solo = dict(inp, x=inp["x"][:300], cu_seqlens=np.array([0, 300], dtype=np.int32),
                 conv_state=inp["conv_state"][:1], S0=inp["S0"][:1], g=inp["g"][:300], beta=inp["beta"][:300],
@@ -174,7 +177,7 @@ def test_one_and_two_workgroups_per_cu_variants_bit_exact():
     np.testing.assert_array_equal(o1.view(np.int32), o[:300].view(np.int32))
     np.testing.assert_array_equal(S1[0].view(np.int32), S[0].view(np.int32))
     ref = _oracle(inp)
-    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16, label="two blocks per workgroup")
+    _check(o, S, ref, inp["cu_seqlens"], TOL_BF16 if in_dtype == "bf16" else TOL_F32, label="two blocks per workgroup")
 
 
 def test_split_and_decode_continuation():
