@@ -17,6 +17,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // 11:8).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Waits until at most N vector memory operations of this wave are outstanding (the N
+// issued last may still be in flight; on gfx9 a wave's loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_leaving() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // ---------------------------------------------------------------- bf16 <-> fp32
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);

@@ -152,18 +152,19 @@ gdn_status prefill_fused_impl(const char* fn, const gdn_dims* dims, const void* 
   const char* xb = static_cast<const char*>(x);
   const char* wb = static_cast<const char*>(conv_w);
   const char* bb = static_cast<const char*>(conv_b);
-  // 1. the v channels' conv into the workspace (the conv states are committed in step 2)
+  // the v channels' conv into the workspace (run by launch_prefill where the inter-chunk
+  // kernel does not convolve v itself); the conv states are committed inside the prefill
   gdn::ConvArgs cv{xb + qk * esz, x_stride, yv, vw, wb + qk * K * esz, bb ? bb + qk * esz : nullptr, cu_seqlens,
                    conv_state_ptrs, num_seqs, total_tokens, static_cast<int32_t>(vw), K, silu, bf16, C,
                    static_cast<int32_t>(qk)};
-  if (gdn_status st = hip_status(gdn::launch_conv_prefill_only(cv, s), fn)) return st;
-  // 2. the chunked prefill, the q/k conv inside its intra-chunk kernel
+  // the chunked prefill, the q/k conv inside its intra-chunk kernel
   gdn::PrefillArgs a{};
   a.r = gdn::RecurArgs{nullptr, 0, nullptr, 0, yv, vw, g, beta, o, state_ptrs, dims->num_k_heads,
                        dims->num_v_heads, dims->head_dim, dims->l2_eps, dims->scale,
                        dims->out_dtype == GDN_BF16, dims->qk_l2norm_off == 0,
                        dims->num_v_heads / dims->num_k_heads};
   a.conv = gdn::ConvIn{x, x_stride, conv_w, conv_b, conv_state_ptrs, static_cast<int32_t>(C), K, silu, bf16};
+  a.vconv = cv;
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
   a.total_tokens = total_tokens;
@@ -171,8 +172,9 @@ gdn_status prefill_fused_impl(const char* fn, const gdn_dims* dims, const void* 
   a.form = dims->prefill_form;
   a.mma = resolve_mma(dims);
   a.workspace = workspace;
-  // (the chunk-0 workgroups of its intra-chunk kernel also commit every channel's conv
-  // state, after the last reader of the old rows)
+  // (the conv states are committed by the last readers of their old rows: the q/k
+  // channels by the intra-chunk kernel's chunk-0 workgroups, the v channels by the
+  // inter-chunk kernel where it convolves v, else by the intra-chunk kernel too)
   return hip_status(gdn::launch_prefill(a, s), fn);
 }
 

@@ -90,6 +90,11 @@ struct ConvIn {
 struct PrefillArgs {
   RecurArgs r;
   ConvIn conv;
+  // Fused entry point only (conv.x != nullptr): the conv of the v channels into r.v, which
+  // launch_prefill runs as a kernel of its own unless the inter-chunk kernel convolves v
+  // itself (whole sequences, 64-token chunks).
+  ConvArgs vconv;
+  int32_t v_in_inter;  // set by launch_prefill
   const int32_t* cu_seqlens;
   int32_t num_seqs;
   int32_t total_tokens;

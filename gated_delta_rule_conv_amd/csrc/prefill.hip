@@ -18,6 +18,8 @@
 // can overflow, so no clamp is needed.
 //
 // Launches, in stream order:
+//   (fused entry point, chunk-parallel form or chunks other than 64 tokens: the conv of
+//   the v channels into the workspace, a kernel of conv.hip)
 //   chunk_table_kernel : cu_seqlens -> chunk table (sequence, start, length), per-sequence
 //                        chunk offsets, a longest-first sequence order and (chunk-parallel
 //                        form) the segment table, on the device.
@@ -27,7 +29,8 @@
 //                        forward substitution, and P. K^, Q^, T and P go to the workspace.
 //                        Through the fused entry point it also convolves its chunk's q and
 //                        k channels from x, and a sequence's first chunk commits the conv
-//                        state of its k-head's q, k and v channels.
+//                        state of its k-head's q and k channels (and of its v-heads' v
+//                        channels where those were convolved by the kernel above).
 //   inter_chunk_kernel : one workgroup per (sequence, v-head, 16 state rows), walking the
 //                        chunks of its sequence in order with its 16 x d slice of the
 //                        state resident in registers/LDS; the contractions K S^T, Q S^T,
@@ -37,11 +40,15 @@
 //                        through its L2. Each workgroup prefetches the next chunk's
 //                        operands; where 16-row workgroups would be 512 or more, a
 //                        workgroup takes two 16-row blocks of a head (one CU each).
+//                        Through the fused entry point (whole sequences, 64-token chunks)
+//                        it convolves its own v channels from x two chunks ahead, so v
+//                        never goes through memory, and commits their conv state.
 // In the chunk-parallel form the last launch is replaced by three: the inter-chunk kernel
 // computing every segment's affine state map, segment_scan_kernel forming the segments'
 // start states, and the inter-chunk kernel producing every segment's outputs.
 
 #include <algorithm>
+#include <type_traits>
 #include <cmath>
 
 #include "conv_taps.h"
@@ -447,7 +454,8 @@ __device__ __forceinline__ void conv_qk_rows(const PrefillArgs& a, int h, int t0
 // rows of [old conv state | the sequence's x rows] (rows before the sequence come from
 // the old state, as in the conv kernels). The chunk-0 workgroup of the pair runs it after
 // its own loader, the only reader of the old q/k rows; the v rows were read by the v
-// conv, which ran before. A thread owns 8 channels.
+// conv, which ran before. (group = 0 where the inter-chunk kernel convolves v: it
+// commits the v channels itself.) A thread owns 8 channels.
 template <typename T, int K, int D>
 __device__ __forceinline__ void commit_conv_rows_k(const PrefillArgs& a, int h, int group, int s, int tid) {
   constexpr int NQ = sizeof(T) / 2;  // 16-byte pieces of 8 channels
@@ -817,7 +825,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     }
     __syncthreads();
   }
-  if (fused && ent.w == 0) commit_conv_rows<D>(a, h, group, ent.x, tid);
+  if (fused && ent.w == 0) commit_conv_rows<D>(a, h, a.v_in_inter ? 0 : group, ent.x, tid);
 }
 
 // ------------------------------------------------------------------------ inter-chunk
@@ -964,7 +972,11 @@ struct RowTile {
 // Everything one wave reads from global memory for one chunk; loaded one chunk ahead so
 // the loads overlap the previous chunk's arithmetic. Waves 0-3 ("K side") hold K^ rows
 // and T rows, waves 4-7 ("Q side") hold Q^ rows and P rows, of token tile wave % 4.
-template <int POL, int D, int C, int NR>
+// x window of the fused v conv (see inter_chunk_kernel): positions a K-side lane reads per
+// row block, its 4 output rows and the up to 3 before them
+constexpr int kXWin = 7;
+
+template <int POL, int D, int C, int NR, typename XT = float>
 struct ChunkIn {
   using F = typename Mma<POL>::Frag;
   static constexpr int KSTEP = Mma<POL>::KSTEP;
@@ -979,6 +991,7 @@ struct ChunkIn {
   float ed[4];
   float egn;    // e^{gam_n}, gam_n = gam of the chunk's last token
   int n;        // tokens in the chunk
+  XT xw[NR][kXWin];  // fused v conv: the raw x (or conv-state) values of the lane's window
 };
 
 // What one launch of the inter-chunk kernel covers:
@@ -999,13 +1012,15 @@ constexpr int kModeSegment = 2;
 // keeps its loads in flight across the step (on the ragged 8-sequence pack: 537 -> 357 us;
 // two blocks without the prefetch lost to two one-block workgroups). Each block's
 // arithmetic is the one-block kernel's, so the results are the same bits.
-template <int POL, int D, int C, bool PF, int MODE, int NR = 1>
+template <int POL, int D, int C, bool PF, int MODE, int NR = 1, int XV = 0>
 __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_chunk_kernel(PrefillArgs a, Workspace w) {
   static_assert(NR == 1 || (NR == 2 && MODE == kModeWhole), "two blocks per workgroup: whole sequences only");
+  static_assert(XV == 0 || (MODE == kModeWhole && PF && C == 64), "v convolved in the kernel: whole sequences, 64-token chunks");
+  using XT = typename std::conditional<XV == 2, float, uint16_t>::type;  // x dtype of the fused v conv
   using M = Mma<POL>;
   using SP = Split<POL>;
   using F = typename M::Frag;
-  using In = ChunkIn<POL, D, C, NR>;
+  using In = ChunkIn<POL, D, C, NR, XT>;
   using FIO = FragIO<POL>;
   using KT = KTile<POL, D, C>;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
@@ -1054,8 +1069,55 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
   const int start = a.cu_seqlens[s];
   const int len = a.cu_seqlens[s + 1] - start;
   if (len <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int kl = KPL * lg;
+  const bool qside = wave >= 4;
+  const int tt = wave & 3;            // token tile
+
+  // The fused entry point's v conv (XV = 1: bf16 x, 2: fp32 x), in place of reading v:
+  // K-side lane (l16, lg) of token tile tt convolves channel l16 of each of the
+  // workgroup's row blocks for its 4 output rows 16 tt + 4 lg + rr, from a window of the
+  // x rows (or, before the sequence, conv-state rows) at positions 16 tt + 4 lg - (K-1) + i,
+  // i < K + 3, loaded two chunks ahead; the per-channel arithmetic is the conv kernels'
+  // (bias, then one fused multiply-add per tap, oldest row first, then the activation), so
+  // v has the bits the v conv kernel would have written. The workgroup owns the conv
+  // state of these channels and commits it at the end.
+  typedef __attribute__((address_space(1))) const XT GXT;
+  typedef __attribute__((address_space(1))) XT GXTw;
+  const int kw = a.conv.width;
+  const int64_t xs = a.conv.x_stride, cst = a.conv.channels;
+  const int vch0 = 2 * r.hk * D + j * D + blk * kDVB + l16;  // channel of block q: vch0 + 16 q
+  GXT* xv = nullptr;
+  GXTw* cs = nullptr;
+  if constexpr (XV != 0) {
+    xv = (GXT*)static_cast<const XT*>(a.conv.x);
+    cs = (GXTw*)reinterpret_cast<XT*>(a.conv.state_ptrs[s]);
+  }
+  auto xval = [](XT v) {
+    if constexpr (XV == 1) return __uint_as_float(static_cast<uint32_t>(v) << 16);
+    else return static_cast<float>(v);
+  };
+  // new conv-state row i = z row len + i, z = [old conv state (K-1 rows) | the sequence's x]
+  auto commit_v = [&]() {
+    if constexpr (XV != 0) {
+      if (!qside && tt == 0 && lg < kw - 1) {
+        const int rz = len + lg;
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+          const int ch = vch0 + q * kDVB;
+          const XT val = rz < kw - 1 ? cs[static_cast<int64_t>(rz) * cst + ch]
+                                     : xv[static_cast<int64_t>(start + rz - (kw - 1)) * xs + ch];
+          cs[static_cast<int64_t>(lg) * cst + ch] = val;
+        }
+      }
+    }
+  };
   const uint64_t sptr = r.state_ptrs[s];
-  if (sptr == 0) return;
+  if (sptr == 0) {
+    commit_v();
+    return;
+  }
   const int h = j / (r.hv / r.hk);
   const float vscale = mrow ? 0.f : 1.f;  // M's rows see v = 0
   // (In transfer mode the Q-side waves still load and compute, and only skip the o
@@ -1064,11 +1126,6 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
   constexpr bool kOut = MODE != kModeTransfer;  // outputs
   const size_t mat = static_cast<size_t>(D) * D;
   float* Sg = reinterpret_cast<float*>(sptr) + (static_cast<int64_t>(j) * D + blk * kDVB) * D;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, lg = lane >> 4;
-  const int kl = KPL * lg;
-  const bool qside = wave >= 4;
-  const int tt = wave & 3;            // token tile
   // (both are always true at C = 64, D = 128; writing them so lets the compiler see
   // straight-line loads, which keeps its wait counts exact and the prefetch alive)
   const bool active = NT >= 4 || tt < NT;
@@ -1165,6 +1222,54 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
   auto load = [&](int c, In& in, bool with_v) {
     load_a(c, in);
     load_m(c, in, with_v);
+  };
+  float cw[NR][4], cb[NR];  // fused v conv: taps and bias of the lane's channels
+  if constexpr (XV != 0) {
+    GXT* wt = (GXT*)static_cast<const XT*>(a.conv.w);
+    GXT* bs = (GXT*)static_cast<const XT*>(a.conv.b);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      const int ch = vch0 + q * kDVB;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) cw[q][jj] = jj < kw ? xval(wt[static_cast<int64_t>(ch) * kw + jj]) : 0.f;
+      cb[q] = a.conv.b != nullptr ? xval(bs[ch]) : 0.f;
+    }
+  }
+  // the x window of chunk c (positions past the sequence's end repeat its last row; the
+  // rows they would feed are masked where v is used)
+  auto load_x = [&](int c, In& in) {
+    if constexpr (XV != 0) {
+      const int pbase = c * C + tt * 16 + 4 * lg - (kw - 1);
+#pragma unroll
+      for (int i = 0; i < kXWin; ++i) {
+        const int p = min(pbase + i, len - 1);
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+          const int ch = vch0 + q * kDVB;
+          GXT* src = p >= 0 ? xv + static_cast<int64_t>(start + p) * xs + ch
+                            : cs + static_cast<int64_t>(p + kw - 1) * cst + ch;
+          in.xw[q][i] = *src;
+        }
+      }
+    }
+  };
+  // v at this lane's 4 rows of chunk c, from the window
+  auto conv_v = [&](In& in) {
+    if constexpr (XV != 0) {
+      const bool act = a.conv.silu != 0;
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          float acc = cb[q];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (jj < kw) acc = fmaf(cw[q][jj], xval(in.xw[q][rr + jj]), acc);
+          if (act) acc = gdn::silu(acc);
+          in.vv[q][rr] = vscale * acc;
+        }
+      }
+    }
   };
 
   // phase 1: X = K^ S^T (K side; then R = diag(beta) (V - diag(e^gam) X) into LDS and the
@@ -1299,17 +1404,31 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
     // compiler can only wait for everything). The prefetch index is clamped rather than
     // guarded (the last chunk is simply read twice).
     In in0, in1;
-    load(c_begin, in0, !qside);
+    load(c_begin, in0, !qside && XV == 0);
+    if (!qside) {
+      load_x(c_begin, in0);
+      load_x(min(c_begin + 1, c_end - 1), in1);
+      conv_v(in0);
+    }
     __syncthreads();  // Sl filled
-    auto step_k = [&](int c, const In& in, In& nxt, int cn) {
-      wait_vmem();
+    // (with the fused v conv: v of chunk c is formed from its window first, and the wait
+    // leaves the window of chunk c + 1, the loads issued last, in flight; the window of
+    // chunk c + 2 goes into this buffer's slot once its operands are loaded)
+    auto step_k = [&](int c, In& in, In& nxt, int cn) {
+      if constexpr (XV != 0) {
+        wait_vmem_leaving<kXWin * NR>();
+      } else {
+        wait_vmem();
+      }
       load_a(cn, nxt);
       f32x4 unused[NR];
       if (active) phase1(in, unused);
       __syncthreads();
       if (active) phase2(in);
+      conv_v(nxt);  // (v of the next chunk, while the Q side still issues its loads)
       __syncthreads();
-      load_m(cn, nxt, true);
+      load_m(cn, nxt, XV == 0);
+      load_x(min(c + 2, c_end - 1), in);
       if (has_tile) phase3_state(in);
       __syncthreads();
     };
@@ -1385,6 +1504,7 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
       for (int q = 0; q < NR; ++q) *reinterpret_cast<f32x4*>(Sg + (q * kDVB + l16) * D + scol) = sacc[q];
     }
   }
+  commit_v();
 }
 
 // Start states of the segments of the chunk-parallel form: Z_0 = the state in place
@@ -1501,6 +1621,12 @@ __global__ __launch_bounds__(kInterThreads) void segment_scan_kernel(PrefillArgs
   }
 }
 
+// Whole sequences: NR 16-row blocks per workgroup, prefetching; XV: the fused v conv (0: none)
+template <int POL, int D, int C, int NR, int XV>
+void launch_whole(const PrefillArgs& a, const Workspace& w, unsigned workgroups, hipStream_t s) {
+  inter_chunk_kernel<POL, D, C, true, kModeWhole, NR, XV><<<workgroups, kInterThreads, 0, s>>>(a, w);
+}
+
 template <int POL, int D, int C>
 hipError_t launch_chunked(const PrefillArgs& a, const Workspace& w, hipStream_t s) {
   const size_t mc = max_chunks_of(C, a.num_seqs, a.total_tokens);
@@ -1523,10 +1649,21 @@ hipError_t launch_chunked(const PrefillArgs& a, const Workspace& w, hipStream_t 
     return hipGetLastError();
   }
   const unsigned blocks = static_cast<unsigned>(NBLK * a.r.hv * a.num_seqs);
-  if (blocks >= 2 * kInterPrefetchMaxCUs)  // two 16-row blocks per workgroup (NBLK is even)
-    inter_chunk_kernel<POL, D, C, true, kModeWhole, 2><<<blocks / 2, kInterThreads, 0, s>>>(a, w);
-  else
-    inter_chunk_kernel<POL, D, C, true, kModeWhole><<<blocks, kInterThreads, 0, s>>>(a, w);
+  const bool two = blocks >= 2 * kInterPrefetchMaxCUs;  // two 16-row blocks per workgroup (NBLK is even)
+  if constexpr (C == 64) {
+    if (a.v_in_inter) {
+      if (a.conv.bf16) {
+        if (two) launch_whole<POL, D, C, 2, 1>(a, w, blocks / 2, s);
+        else launch_whole<POL, D, C, 1, 1>(a, w, blocks, s);
+      } else {
+        if (two) launch_whole<POL, D, C, 2, 2>(a, w, blocks / 2, s);
+        else launch_whole<POL, D, C, 1, 2>(a, w, blocks, s);
+      }
+      return hipGetLastError();
+    }
+  }
+  if (two) launch_whole<POL, D, C, 2, 0>(a, w, blocks / 2, s);
+  else launch_whole<POL, D, C, 1, 0>(a, w, blocks, s);
   return hipGetLastError();
 }
 
@@ -1555,11 +1692,25 @@ size_t prefill_workspace_bytes(int32_t hk, int32_t hv, int32_t d, int32_t chunk,
   return workspace_bytes(hk, hv, d, chunk, num_seqs, total_tokens, form);
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  if (a.num_seqs == 0 || a.total_tokens == 0) return hipSuccess;
-  const Workspace w = carve(a.workspace, a.r.hk, a.r.hv, a.r.d, a.chunk, a.num_seqs, a.total_tokens, a.form);
+hipError_t launch_prefill(const PrefillArgs& args, hipStream_t s) {
+  if (args.num_seqs == 0 || args.total_tokens == 0) return hipSuccess;
+  const Workspace w = carve(args.workspace, args.r.hk, args.r.hv, args.r.d, args.chunk, args.num_seqs,
+                            args.total_tokens, args.form);
+  PrefillArgs a = args;
+  hipError_t e;
+  if (a.conv.x != nullptr) {
+    // fused entry point: whole sequences in 64-token chunks convolve v inside the
+    // inter-chunk kernel; otherwise the v channels' conv runs first, into r.v
+    a.v_in_inter = (!w.segmented && a.chunk == 64) ? 1 : 0;
+    if (!a.v_in_inter) {
+      e = launch_conv_prefill_only(a.vconv, s);
+      if (e != hipSuccess) return e;
+    }
+  } else {
+    a.v_in_inter = 0;
+  }
   chunk_table_kernel<<<1, kMetaThreads, 0, s>>>(a.cu_seqlens, a.num_seqs, a.chunk, w);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   return a.mma == kPolFP32 ? by_dim<kPolFP32>(a, w, s) : by_dim<kPolBF16X3>(a, w, s);
 }

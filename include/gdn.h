@@ -200,11 +200,12 @@ gdn_status gdn_prefill_fused_workspace_size(const gdn_dims* dims, int32_t num_se
  * gdn_prefill_fused -- the prefill of a layer in one call: gdn_conv_update in prefill
  * mode followed by gdn_prefill_chunked on the q/k/v views of its output ("System
  * Design", "GDN Kernel Dispatch Detail": conv with the per-sequence conv state, then the
- * chunked gated delta rule and the state update), without writing the q and k part of
- * the conv output to memory: the intra-chunk kernel convolves its chunk's q and k
- * channels from x itself (the same per-channel arithmetic as the conv kernel), and only
- * the v part goes through the workspace. o, the recurrent states and the conv states
- * come out bit-identical to those two calls in sequence.
+ * chunked gated delta rule and the state update), without writing the conv output to
+ * memory: the intra-chunk kernel convolves its chunk's q and k channels from x itself, and
+ * the inter-chunk kernel the v channels it needs (the same per-channel arithmetic as the
+ * conv kernel); with the chunk-parallel form or chunks other than 64 tokens the v part of
+ * the conv output goes through the workspace instead. o, the recurrent states and the conv
+ * states come out bit-identical to those two calls in sequence.
  *
  *  x          [total_tokens][C] in dims->in_dtype, row stride x_stride (C = (2 Hk + Hv) d,
  *             channels ordered q | k | v as for gdn_conv_update).
