@@ -100,7 +100,12 @@ def ev():
 SETTLE_S = 0.1
 
 
-def settle(call, seconds: float = SETTLE_S) -> None:
+def set_settle(seconds: float) -> None:
+    global SETTLE_S
+    SETTLE_S = seconds
+
+
+def settle(call, seconds: float | None = None) -> None:
     """Untimed calls, back to back, for at least `seconds` before a timed section: after the
     host has been setting up (inputs, graph capture) the GPU sits at its idle clocks and
     takes tens of milliseconds of work to leave them (measured: the fused L = 4096 prefill
@@ -109,6 +114,10 @@ def settle(call, seconds: float = SETTLE_S) -> None:
     server runs at. The timed calls that follow are unchanged."""
     import torch
 
+    if seconds is None:
+        seconds = SETTLE_S
+    if seconds <= 0:
+        return
     t0 = time.perf_counter()
     n = 0
     while True:
@@ -536,6 +545,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed calls before each timed section (0: none, e.g. for a profiler, "
+                         "whose traces then hold a fixed number of launches per section)")
     ap.add_argument("--m", type=int, default=64)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ragged", action="store_true", help="skip the 8-sequence ragged prefill")
@@ -564,6 +576,7 @@ def main() -> int:
     if args.copy_probe:
         copy_probe()
     K, W = args.steps, args.warmup
+    set_settle(args.settle)
 
     # ---------------------------------------------------------------- decode, m = 64
     def run_decode(form: str):
