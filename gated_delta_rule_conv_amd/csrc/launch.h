@@ -95,6 +95,7 @@ struct PrefillArgs {
   // itself (whole sequences, 64-token chunks).
   ConvArgs vconv;
   int32_t v_in_inter;  // set by launch_prefill
+  int32_t table_free;  // set by launch_prefill: no chunk-table launch (the intra-chunk kernel finds its chunks)
   const int32_t* cu_seqlens;
   int32_t num_seqs;
   int32_t total_tokens;

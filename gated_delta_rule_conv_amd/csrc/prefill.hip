@@ -22,7 +22,10 @@
 //   the v channels into the workspace, a kernel of conv.hip)
 //   chunk_table_kernel : cu_seqlens -> chunk table (sequence, start, length), per-sequence
 //                        chunk offsets, a longest-first sequence order and (chunk-parallel
-//                        form) the segment table, on the device.
+//                        form) the segment table, on the device. Not launched for whole
+//                        sequences when there are at most 64: each intra-chunk workgroup
+//                        then finds its chunk from cu_seqlens, and one of them writes the
+//                        offsets and the order.
 //   intra_chunk_kernel : one workgroup per (chunk, k-head), all chunks in parallel:
 //                        K, Q in LDS (L2-normalised unless that is switched off); K K^T and Q K^T on MFMA; for each v-head
 //                        sharing the k-head: the decay mask, A, T by blocked (16x16)
@@ -545,12 +548,57 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   float* bet = smem + Lo::OFF_BET;
 
   const int chunk = blockIdx.x;
-  if (chunk >= *w.n_chunks) return;
   const int h = blockIdx.y;
-  const int4 ent = w.table[chunk];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the chunk's (sequence, first token, tokens, index in its sequence): from the chunk
+  // table, or -- whole sequences, at most 64 of them, no table launch -- from cu_seqlens,
+  // by one scan in every wave (lane s = sequence s); then the chunk-(0, 0) workgroup writes
+  // the sequences' chunk offsets and the longest-first order for the inter-chunk kernel
+  int4 ent;
+  if (a.table_free) {
+    const int N = a.num_seqs;
+    int start = 0, len = 0;
+    if (lane < N) {
+      start = a.cu_seqlens[lane];
+      len = a.cu_seqlens[lane + 1] - start;
+    }
+    const int nc = (len + C - 1) / C;
+    int inc = nc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += u;
+    }
+    const int first = inc - nc;
+    const int total = __builtin_amdgcn_readlane(inc, 63);
+    if (chunk == 0 && h == 0 && wave == 0) {
+      if (lane < N) {
+        w.chunk_off[lane] = first;
+        int rank = 0;  // longest sequence first, ties by index
+        for (int q = 0; q < N; ++q) {
+          const int lq = __builtin_amdgcn_readlane(len, q);
+          rank += (lq > len) || (lq == len && q < lane);
+        }
+        w.order[rank] = lane;
+      }
+      if (lane == 0) {
+        w.chunk_off[N] = total;
+        *w.n_chunks = total;
+      }
+    }
+    if (chunk >= total) return;
+    const uint64_t owner = __ballot(lane < N && chunk >= first && chunk < first + nc);
+    const int sq = __builtin_ctzll(owner);
+    const int fq = __builtin_amdgcn_readlane(first, sq), sst = __builtin_amdgcn_readlane(start, sq);
+    const int sl = __builtin_amdgcn_readlane(len, sq);
+    const int cq = chunk - fq;
+    ent = make_int4(sq, sst + cq * C, min(C, sl - cq * C), cq);
+  } else {
+    if (chunk >= *w.n_chunks) return;
+    ent = w.table[chunk];
+  }
   const int t0 = ent.y, n = ent.z;
   const RecurArgs& r = a.r;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int group = r.hv / r.hk;
   float g_first = 0.f, b_first = 0.f;  // wave 0: g and beta of the first v-head, read early
@@ -1709,9 +1757,13 @@ hipError_t launch_prefill(const PrefillArgs& args, hipStream_t s) {
   } else {
     a.v_in_inter = 0;
   }
-  chunk_table_kernel<<<1, kMetaThreads, 0, s>>>(a.cu_seqlens, a.num_seqs, a.chunk, w);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // whole sequences, at most 64: the intra-chunk kernel finds its chunks from cu_seqlens
+  a.table_free = (!w.segmented && a.num_seqs <= 64) ? 1 : 0;
+  if (!a.table_free) {
+    chunk_table_kernel<<<1, kMetaThreads, 0, s>>>(a.cu_seqlens, a.num_seqs, a.chunk, w);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return a.mma == kPolFP32 ? by_dim<kPolFP32>(a, w, s) : by_dim<kPolBF16X3>(a, w, s);
 }
 
