@@ -65,7 +65,10 @@ def _run_both(inp, act, form):
 # (hk, hv, d, in_dtype, K, activation, bias, chunk, lens, prefill_form): every head dim,
 # chunk size, conv width and dtype, SiLU and bias, sequences shorter than the conv window
 # (their conv rows come from the conv state), an empty sequence, partial last chunks,
-# both prefill forms (600 tokens at 2/4 heads take the chunk-parallel form)
+# both prefill forms (600 tokens at 2/4 heads take the chunk-parallel form). Whole
+# sequences in 64-token chunks have the inter-chunk kernel convolve v (bf16 and fp32 x,
+# every conv width, bias and SiLU, one and two 16-row blocks per workgroup); the other
+# cases run the v conv as a launch of its own.
 CASES = [
     (16, 32, 128, "bf16", 4, 0, False, 64, (1, 17, 64, 0, 300, 130), 0),
     (2, 4, 64, "bf16", 3, 1, True, 32, (2, 1, 70, 33), 0),
@@ -74,6 +77,10 @@ CASES = [
     (2, 4, 128, "bf16", 4, 0, True, 64, (600,), 2),
     (2, 4, 128, "bf16", 4, 1, False, 64, (600, 2), 0),
     (1, 2, 64, "bf16", 4, 1, False, 16, (129, 7), 1),
+    (2, 4, 128, "bf16", 4, 1, True, 64, (300, 70, 0, 2), 1),
+    (2, 4, 128, "f32", 3, 1, True, 64, (130, 1, 64), 1),
+    (2, 4, 64, "bf16", 2, 0, False, 64, (65, 2, 129), 1),
+    (8, 32, 32, "f32", 4, 1, True, 64, (70, 1, 200, 0, 64, 3, 130, 17), 1),
 ]
 
 
