@@ -1146,7 +1146,11 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
     if constexpr (XV == 1) return __uint_as_float(static_cast<uint32_t>(v) << 16);
     else return static_cast<float>(v);
   };
-  // new conv-state row i = z row len + i, z = [old conv state (K-1 rows) | the sequence's x]
+  // new conv-state row i = z row len + i, z = [old conv state (K-1 rows) | the sequence's x],
+  // by lanes lg = i of K-side wave 0 (the only wave that reads old rows, in its first
+  // window). With len < K-1 a lane reads an old row another lane writes: per block that is
+  // one load instruction of all the lanes, waited for, then one store, so every read lands
+  // first.
   auto commit_v = [&]() {
     if constexpr (XV != 0) {
       if (!qside && tt == 0 && lg < kw - 1) {
