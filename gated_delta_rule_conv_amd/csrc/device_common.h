@@ -163,21 +163,22 @@ struct Vec4<uint16_t> {
 // ---------------------------------------------------------------- DPP reductions
 // dpp_ctrl encodings (GCN/CDNA DPP): quad_perm [1,0,3,2] = 0xB1 (lane ^ 1),
 // quad_perm [2,3,0,1] = 0x4E (lane ^ 2), row_half_mirror = 0x141 (lane i <-> 7 - i
-// inside each group of 8).
+// inside each group of 8), row_mirror = 0x140 (lane i <-> 15 - i inside each row of 16).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of G lanes (G in {1, 2, 4, 8}); every lane of the group
+// Sum over aligned groups of G lanes (G in {1, 2, 4, 8, 16}); every lane of the group
 // ends with the same bits (fp add is commutative), and the order of the additions
 // depends only on G, never on the launch shape.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
   if constexpr (G >= 2) v += dpp_f32<0xB1>(v);
   if constexpr (G >= 4) v += dpp_f32<0x4E>(v);
   if constexpr (G >= 8) v += dpp_f32<0x141>(v);
+  if constexpr (G >= 16) v += dpp_f32<0x140>(v);
   return v;
 }
 

@@ -368,20 +368,37 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
 }
 
 // ------------------------------------------------------------------------ intra-chunk
-// The fused entry point's q/k conv, inside the intra-chunk kernel: the chunk's q and k
-// channels of k-head h, convolved from x (and, before the sequence's first token, from
-// its conv state) into the LDS rows Qh / Kh, not yet normalised; rows >= n are zero. The
-// per-channel arithmetic is ConvTaps::apply, as in the conv kernels, so the values are
-// those the conv kernel would have written. A thread takes 8 adjacent channels (q's d/8
-// groups, then k's) of a strip of rows and loads the K-1 rows before the strip once.
-template <typename T, int K, int D, int C, int KP>
+// Step 1's thread mapping: thread e < ACTIVE owns 8 adjacent channels (group e % G; q's D/8
+// groups, then k's) of the rows RPT (e / G) .. RPT (e / G) + RPT - 1 of the chunk, so one
+// row of q (or k) is held by D/8 adjacent, aligned lanes.
+template <int D, int C>
+struct QKMap {
+  static constexpr int G = 2 * D / kConvVec;                              // 8-channel groups
+  static constexpr int RPT = (G * C >= kThreads) ? G * C / kThreads : 1;  // rows per thread
+  static constexpr int NS = C / RPT;                                       // row strips
+  static constexpr int ACTIVE = G * NS;
+  __device__ __forceinline__ static bool is_q(int tid) { return tid % G < G / 2; }
+  __device__ __forceinline__ static int col(int tid) { return (tid % G % (G / 2)) * kConvVec; }
+  __device__ __forceinline__ static int row0(int tid) { return (tid / G) * RPT; }
+};
+
+// The fused entry point's q/k conv, inside the intra-chunk kernel: the thread's rows and
+// channels (QKMap) of q and k of k-head h, convolved from x (and, before the sequence's
+// first token, from its conv state) into registers, not yet normalised; rows >= n are zero.
+// The per-channel arithmetic is ConvTaps::apply, as in the conv kernels, so the values are
+// those the conv kernel would have written. The K-1 rows before the strip are loaded once.
+template <typename T, int K, int D, int C>
 __device__ __forceinline__ void conv_qk_rows_k(const PrefillArgs& a, int h, int t0, int n, int seq_start, int s,
-                                               float (*Kh)[KP], float (*Qh)[KP], int tid) {
+                                               float (&out)[QKMap<D, C>::RPT][kConvVec], int tid) {
+  using QM = QKMap<D, C>;
+  constexpr int RPT = QM::RPT;
   using V8 = Vec8<T>;
   using GT = const typename V8::GT;
-  constexpr int G = 2 * D / kConvVec;                                 // 8-channel groups
-  constexpr int RPT = (G * C >= kThreads) ? G * C / kThreads : 1;    // rows per thread
-  constexpr int NS = C / RPT;                                          // row strips
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+#pragma unroll
+    for (int c = 0; c < kConvVec; ++c) out[i][c] = 0.f;
+  if (tid >= QM::ACTIVE) return;
   // (global-address-space pointers: every load below is issued before any is used, in
   // one memory round trip)
   GT* x = (GT*)static_cast<const T*>(a.conv.x);
@@ -392,62 +409,69 @@ __device__ __forceinline__ void conv_qk_rows_k(const PrefillArgs& a, int h, int 
   const int64_t cstride = a.conv.channels;
   const int pos0 = t0 - seq_start;  // position of the chunk's first row in its sequence
   const bool silu = a.conv.silu != 0;
-  for (int e = tid; e < G * NS; e += kThreads) {
-    const int grp = e % G, strip = e / G;
-    const bool isq = grp < G / 2;
-    const int col = (isq ? grp : grp - G / 2) * kConvVec;  // column within the head
-    const int ch = (isq ? 0 : a.r.hk * D) + h * D + col;    // channel of x, the taps and the conv state
-    typename V8::Raw wr[K], br;
+  const int ch = (QM::is_q(tid) ? 0 : a.r.hk * D) + h * D + QM::col(tid);  // channel of x, the taps and the conv state
+  typename V8::Raw wr[K], br;
 #pragma unroll
-    for (int t = 0; t < K; ++t) wr[t] = V8::load_raw_g(wt + static_cast<int64_t>(ch) * K + t * kConvVec);
-    br = V8::load_raw_g(bs + ch);
-    const int r0 = strip * RPT;
-    typename V8::Raw z[RPT + K - 1];  // z rows r0 - (K-1) .. r0 + RPT - 1 (chunk coordinates)
+  for (int t = 0; t < K; ++t) wr[t] = V8::load_raw_g(wt + static_cast<int64_t>(ch) * K + t * kConvVec);
+  br = V8::load_raw_g(bs + ch);
+  const int r0 = QM::row0(tid);
+  typename V8::Raw z[RPT + K - 1];  // z rows r0 - (K-1) .. r0 + RPT - 1 (chunk coordinates)
 #pragma unroll
-    for (int i = 0; i < RPT + K - 1; ++i) {
-      const int rr = min(r0 - (K - 1) + i, n - 1);  // rows past the chunk's end repeat its last
-      const int p = pos0 + rr;                       // position in the sequence
-      GT* src = p >= 0 ? x + static_cast<int64_t>(seq_start + p) * a.conv.x_stride + ch
-                       : cs + static_cast<int64_t>(p + K - 1) * cstride + ch;
-      z[i] = V8::load_raw_g(src);
-    }
-    ConvTaps<T, K> taps;
-    taps.from_raw(wr, br, has_b);
+  for (int i = 0; i < RPT + K - 1; ++i) {
+    const int rr = min(r0 - (K - 1) + i, n - 1);  // rows past the chunk's end repeat its last
+    const int p = pos0 + rr;                       // position in the sequence
+    GT* src = p >= 0 ? x + static_cast<int64_t>(seq_start + p) * a.conv.x_stride + ch
+                     : cs + static_cast<int64_t>(p + K - 1) * cstride + ch;
+    z[i] = V8::load_raw_g(src);
+  }
+  ConvTaps<T, K> taps;
+  taps.from_raw(wr, br, has_b);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int row = r0 + i;
-      float out[kConvVec];
-      if (row < n) {
-        float win[K - 1][kConvVec], cur[kConvVec];
+  for (int i = 0; i < RPT; ++i) {
+    if (r0 + i < n) {
+      float win[K - 1][kConvVec], cur[kConvVec];
 #pragma unroll
-        for (int j = 0; j < K - 1; ++j) V8::convert(z[i + j], win[j]);
-        V8::convert(z[i + K - 1], cur);
-        taps.apply(win, cur, silu, out);
-      } else {
-#pragma unroll
-        for (int c = 0; c < kConvVec; ++c) out[c] = 0.f;
-      }
-      float* dst = isq ? &Qh[row][col] : &Kh[row][col];
-      *reinterpret_cast<float4*>(dst) = make_float4(out[0], out[1], out[2], out[3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(out[4], out[5], out[6], out[7]);
+      for (int j = 0; j < K - 1; ++j) V8::convert(z[i + j], win[j]);
+      V8::convert(z[i + K - 1], cur);
+      taps.apply(win, cur, silu, out[i]);
     }
   }
 }
 
-template <int D, int C, int KP>
+template <int D, int C>
 __device__ __forceinline__ void conv_qk_rows(const PrefillArgs& a, int h, int t0, int n, int seq_start, int s,
-                                             float (*Kh)[KP], float (*Qh)[KP], int tid) {
+                                             float (&out)[QKMap<D, C>::RPT][kConvVec], int tid) {
   if (a.conv.bf16) {
     switch (a.conv.width) {
-      case 2: conv_qk_rows_k<uint16_t, 2, D, C, KP>(a, h, t0, n, seq_start, s, Kh, Qh, tid); break;
-      case 3: conv_qk_rows_k<uint16_t, 3, D, C, KP>(a, h, t0, n, seq_start, s, Kh, Qh, tid); break;
-      default: conv_qk_rows_k<uint16_t, 4, D, C, KP>(a, h, t0, n, seq_start, s, Kh, Qh, tid); break;
+      case 2: conv_qk_rows_k<uint16_t, 2, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
+      case 3: conv_qk_rows_k<uint16_t, 3, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
+      default: conv_qk_rows_k<uint16_t, 4, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
     }
   } else {
     switch (a.conv.width) {
-      case 2: conv_qk_rows_k<float, 2, D, C, KP>(a, h, t0, n, seq_start, s, Kh, Qh, tid); break;
-      case 3: conv_qk_rows_k<float, 3, D, C, KP>(a, h, t0, n, seq_start, s, Kh, Qh, tid); break;
-      default: conv_qk_rows_k<float, 4, D, C, KP>(a, h, t0, n, seq_start, s, Kh, Qh, tid); break;
+      case 2: conv_qk_rows_k<float, 2, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
+      case 3: conv_qk_rows_k<float, 3, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
+      default: conv_qk_rows_k<float, 4, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
+    }
+  }
+}
+
+// The same rows and channels of q and k as given (fp32), rows >= n zero.
+template <int D, int C>
+__device__ __forceinline__ void load_qk_rows(const RecurArgs& r, int h, int t0, int n,
+                                             float (&out)[QKMap<D, C>::RPT][kConvVec], int tid) {
+  using QM = QKMap<D, C>;
+  const bool isq = QM::is_q(tid);
+  const float* src = (isq ? r.q : r.k) + h * D + QM::col(tid);
+  const int64_t stride = isq ? r.q_stride : r.k_stride;
+  const int r0 = QM::row0(tid);
+#pragma unroll
+  for (int i = 0; i < QM::RPT; ++i) {
+    if (tid < QM::ACTIVE && r0 + i < n) {
+      load_k<kConvVec>(src + static_cast<int64_t>(t0 + r0 + i) * stride, out[i]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < kConvVec; ++c) out[i][c] = 0.f;
     }
   }
 }
@@ -507,7 +531,8 @@ __device__ __forceinline__ void commit_conv_rows(const PrefillArgs& a, int h, in
 // LDS of the intra-chunk kernel, in floats. K^ and Q^ live only until K K^T and Q K^T are
 // in registers; then G and QK take K^'s place and A and T take Q^'s, so the peak is two
 // areas, each the largest of K^ as fp32 rows, K^ as bf16 hi and lo planes and two C x C
-// matrices (70 KB at C = 64, D = 128), and two workgroups fit on a CU.
+// matrices (70 KB at C = 64, D = 128); with the decay terms of up to 8 v-heads (4 KB) two
+// workgroups still fit on a CU.
 template <int D, int C>
 struct IntraLayout {
   static constexpr int KP = D + 4;  // padded row of K^/Q^
@@ -521,9 +546,10 @@ struct IntraLayout {
   static constexpr int OFF_Q = RS;       // Q^   alias  A, T
   static constexpr int OFF_A = RS;
   static constexpr int OFF_T = RS + C * CP;
-  static constexpr int OFF_GAM = 2 * RS;
-  static constexpr int OFF_BET = OFF_GAM + C;
-  static constexpr int TOTAL = OFF_BET + C;
+  static constexpr int NGB = 8;           // v-heads whose gam and beta are held at once
+  static constexpr int OFF_GAM = 2 * RS;  // [NGB][C]
+  static constexpr int OFF_BET = OFF_GAM + NGB * C;
+  static constexpr int TOTAL = OFF_BET + NGB * C;
 };
 
 template <int POL, int D, int C>
@@ -601,91 +627,96 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   const RecurArgs& r = a.r;
   const int l16 = lane & 15, lg = lane >> 4;
   const int group = r.hv / r.hk;
-  float g_first = 0.f, b_first = 0.f;  // wave 0: g and beta of the first v-head, read early
-  if (wave == 0) {
-    const int tl = min(lane, n - 1);
-    g_first = r.g[static_cast<int64_t>(t0 + tl) * r.hv + h * group];
-    b_first = r.beta[static_cast<int64_t>(t0 + tl) * r.hv + h * group];
-  }
+  // The decay terms of the group's v-heads are formed NGB v-heads at a time, v-head
+  // jb + i of a batch on wave (i + 4) % 8 (waves 4-7 have one product fewer in step 2);
+  // the first batch's g and beta are read here.
+  constexpr int NGB = Lo::NGB;
+  static_assert(NGB == kWaves, "one v-head per wave in a batch");
+  const int my_gb = (wave + 4) % kWaves;  // this wave's v-head within a batch
+  float g_in = 0.f, b_in = 0.f;
+  auto load_gb = [&](int jb) {
+    if (jb + my_gb < group) {
+      const int tl = min(lane, n - 1);  // (a valid token; lanes >= n are masked at use)
+      g_in = r.g[static_cast<int64_t>(t0 + tl) * r.hv + h * group + jb + my_gb];
+      b_in = r.beta[static_cast<int64_t>(t0 + tl) * r.hv + h * group + jb + my_gb];
+    }
+  };
+  load_gb(0);
+  // gam (inclusive cumsum of g over the chunk) and beta into LDS, and the chunk's decay
+  // factors for the inter-chunk kernel into the workspace (lanes >= n hold gam_{n-1})
+  auto decay_terms = [&](int jb) {
+    if (jb + my_gb >= group) return;
+    const int j = h * group + jb + my_gb;
+    float* gam_out = reinterpret_cast<float*>(w.tp + (static_cast<int64_t>(chunk) * r.hv + j) * w.tp_stride +
+                                              2 * static_cast<size_t>(C / 16) * FragCount<POL>::nk(C) * FIO::BYTES);
+    const float gv = wave_inclusive_scan(lane < n ? g_in : 0.f);
+    const float bv = lane < n ? b_in : 0.f;
+    const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), C - 1));
+    if (lane < C) {
+      gam[my_gb * C + lane] = gv;
+      bet[my_gb * C + lane] = bv;
+      gam_out[lane] = expf(gv);
+      gam_out[C + lane] = bv;
+      gam_out[2 * C + lane] = expf(gn - gv);
+    }
+  };
 
-  // 1. normalised K and Q rows of the chunk into LDS; rows >= n are zero. The fused entry
-  // point convolves the rows into LDS first and normalises them there.
-  constexpr int TPR = 8;
-  constexpr int EPT = D / TPR;
+  // 1. normalised K and Q rows of the chunk into LDS; rows >= n are zero. Each thread holds
+  // its rows and channels (QKMap) in registers -- convolved from x through the fused entry
+  // point, else read -- and a row's squared norm is the sum of the thread's 8 squares (in
+  // channel order) summed over the D/8 lanes that hold the row. With bf16x3 products, K^
+  // and Q^ are kept as bf16 hi and lo planes ([C][KH] each, the lo plane after the hi one):
+  // split once here, then read as they are by the products and the export below.
+  using QM = QKMap<D, C>;
   const bool fused = a.conv.x != nullptr;
-  if (fused) {
-    conv_qk_rows<D, C, KP>(a, h, t0, n, t0 - ent.w * C, ent.x, Kh, Qh, tid);
-    __syncthreads();
-  }
-  // With bf16x3 products, K^ and Q^ are kept as bf16 hi and lo planes ([C][KH] each, the
-  // lo plane after the hi one, in the same LDS area as the fp32 rows): split once here,
-  // then read as they are by the products and the export below.
   constexpr bool kPlanes = POL == kPolBF16X3;
   constexpr int KH = Lo::KHF;  // plane row length (elements)
-  static_assert(kThreads / TPR >= C, "one pass over the rows");
   auto* Khp = reinterpret_cast<__bf16*>(smem + Lo::OFF_K);
   auto* Qhp = reinterpret_cast<__bf16*>(smem + Lo::OFF_Q);
   {
-    const int row = tid / TPR, part = tid % TPR;
-    float kv[EPT], qv[EPT];
-    const bool live = row < n;
-    if (live && fused) {
-      load_k<EPT>(&Kh[row][part * EPT], kv);
-      load_k<EPT>(&Qh[row][part * EPT], qv);
-    } else if (live) {
-      load_k<EPT>(r.k + static_cast<int64_t>(t0 + row) * r.k_stride + h * D + part * EPT, kv);
-      load_k<EPT>(r.q + static_cast<int64_t>(t0 + row) * r.q_stride + h * D + part * EPT, qv);
+    float rows[QM::RPT][kConvVec];
+    if (fused) {
+      conv_qk_rows<D, C>(a, h, t0, n, t0 - ent.w * C, ent.x, rows, tid);
     } else {
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) kv[e] = qv[e] = 0.f;
+      load_qk_rows<D, C>(r, h, t0, n, rows, tid);
     }
-    // (the planes overlap the fp32 rows the fused conv left in LDS: all of those are in
-    // registers before any plane is written)
-    if (kPlanes && fused) __syncthreads();
-    float kk = 0.f, qq = 0.f;
+    const bool isq = QM::is_q(tid);
+    const int col = QM::col(tid), r0 = QM::row0(tid);
+    const float num = isq ? r.scale : 1.0f;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      kk = fmaf(kv[e], kv[e], kk);
-      qq = fmaf(qv[e], qv[e], qq);
-    }
-    kk = group_sum<TPR>(kk);
-    qq = group_sum<TPR>(qq);
-    const float rk = live ? (r.qk_norm ? 1.0f / sqrtf(kk + r.eps) : 1.0f) : 0.f;
-    const float rq = live ? (r.qk_norm ? r.scale / sqrtf(qq + r.eps) : r.scale) : 0.f;
-    if (row < C) {
+    for (int i = 0; i < QM::RPT; ++i) {
+      float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        kv[e] *= rk;
-        qv[e] *= rq;
-      }
-      if constexpr (kPlanes) {
-        // (4 values at a time, as EPT is 4 at d = 32; the split is Mma<>::split's)
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      for (int c = 0; c < kConvVec; ++c) ss = fmaf(rows[i][c], rows[i][c], ss);
+      ss = group_sum<D / kConvVec>(ss);
+      const int row = r0 + i;
+      const float rs = row < n ? (r.qk_norm ? num / sqrtf(ss + r.eps) : num) : 0.f;
+      float v[kConvVec];
 #pragma unroll
-        for (int e = 0; e < EPT; e += 4) {
-          bf16x4 kh, kl4, qh, ql4;
+      for (int c = 0; c < kConvVec; ++c) v[c] = rows[i][c] * rs;
+      if (tid < QM::ACTIVE) {
+        if constexpr (kPlanes) {
+          // (the split is Mma<>::split's)
+          bf16x8 hi, lo;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            kh[i] = static_cast<__bf16>(kv[e + i]);
-            kl4[i] = static_cast<__bf16>(kv[e + i] - static_cast<float>(kh[i]));
-            qh[i] = static_cast<__bf16>(qv[e + i]);
-            ql4[i] = static_cast<__bf16>(qv[e + i] - static_cast<float>(qh[i]));
+          for (int c = 0; c < kConvVec; ++c) {
+            hi[c] = static_cast<__bf16>(v[c]);
+            lo[c] = static_cast<__bf16>(v[c] - static_cast<float>(hi[c]));
           }
-          const int o = row * KH + part * EPT + e;
-          *reinterpret_cast<bf16x4*>(Khp + o) = kh;
-          *reinterpret_cast<bf16x4*>(Khp + C * KH + o) = kl4;
-          *reinterpret_cast<bf16x4*>(Qhp + o) = qh;
-          *reinterpret_cast<bf16x4*>(Qhp + C * KH + o) = ql4;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPT; e += 4) {
-          *reinterpret_cast<float4*>(&Kh[row][part * EPT + e]) = make_float4(kv[e], kv[e + 1], kv[e + 2], kv[e + 3]);
-          *reinterpret_cast<float4*>(&Qh[row][part * EPT + e]) = make_float4(qv[e], qv[e + 1], qv[e + 2], qv[e + 3]);
+          __bf16* dst = (isq ? Qhp : Khp) + row * KH + col;
+          *reinterpret_cast<bf16x8*>(dst) = hi;
+          *reinterpret_cast<bf16x8*>(dst + C * KH) = lo;
+        } else {
+          float* dst = isq ? &Qh[row][col] : &Kh[row][col];
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
         }
       }
     }
   }
+  // (here, while this wave's only memory operations in flight are loads: a later wait for
+  // g and beta would also wait for the exports' stores)
+  decay_terms(0);
   __syncthreads();
   // the A-operand fragment of row t, head-dim values d0 .. d0 + KPL - 1 of K^ (or Q^)
   auto frag_of = [&](bool isq, int t, int d0) {
@@ -757,36 +788,19 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   }
   __syncthreads();
 
-  // 3. per v-head of this k-head's group: decay mask, A, T = (I + A)^-1, P. Wave 0 reads
-  // each v-head's g and beta one v-head ahead (the first ones at the start), so their
-  // memory latency stays off the chain of barriers.
-  float g_next = g_first, b_next = b_first;
-  auto load_gb = [&](int j) {
-    const int tl = min(lane, n - 1);  // (a valid token; lanes >= n are masked at use)
-    g_next = r.g[static_cast<int64_t>(t0 + tl) * r.hv + j];
-    b_next = r.beta[static_cast<int64_t>(t0 + tl) * r.hv + j];
-  };
+  // 3. per v-head of this k-head's group: decay mask, A, T = (I + A)^-1, P (the decay
+  // terms of v-heads 8 and on are formed when their batch comes up)
   for (int jj = 0; jj < group; ++jj) {
     const int j = h * group + jj;
     char* tp = w.tp + (static_cast<int64_t>(chunk) * r.hv + j) * w.tp_stride;
     char* pp = tp + static_cast<size_t>(C / 16) * NKF * FIO::BYTES;
-    float* gam_out = reinterpret_cast<float*>(pp + static_cast<size_t>(C / 16) * NKF * FIO::BYTES);
-    if (wave == 0) {
-      float gv = lane < n ? g_next : 0.f;
-      const float bv = lane < n ? b_next : 0.f;
-      if (jj + 1 < group) load_gb(j + 1);
-      gv = wave_inclusive_scan(gv);
-      // the chunk's decay factors for the inter-chunk kernel (lanes >= n hold gam_{n-1})
-      const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), C - 1));
-      if (lane < C) {
-        gam[lane] = gv;
-        bet[lane] = bv;
-        gam_out[lane] = expf(gv);
-        gam_out[C + lane] = bv;
-        gam_out[2 * C + lane] = expf(gn - gv);
-      }
+    if (jj > 0 && jj % NGB == 0) {
+      load_gb(jj);
+      decay_terms(jj);
+      __syncthreads();
     }
-    __syncthreads();
+    const float* gamj = gam + (jj % NGB) * C;
+    const float* betj = bet + (jj % NGB) * C;
 
     // A (strictly lower) into LDS and P (lower incl. diagonal) to the workspace, one
     // fragment lane per thread; the k range runs to the padded NKF * KSTEP so the zero
@@ -804,9 +818,9 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
         float av = 0.f;
         pv[i] = 0.f;
         if (s <= t) {
-          const float dec = expf(gam[t] - gam[s]);
+          const float dec = expf(gamj[t] - gamj[s]);
           pv[i] = dec * QKm[t][s];
-          if (s < t) av = bet[t] * dec * Gm[t][s];
+          if (s < t) av = betj[t] * dec * Gm[t][s];
         }
         if (s < C) Am[t][s] = av;
       }
