@@ -68,7 +68,8 @@ def _run_both(inp, act, form):
 # both prefill forms (600 tokens at 2/4 heads take the chunk-parallel form). Whole
 # sequences in 64-token chunks have the inter-chunk kernel convolve v (bf16 and fp32 x,
 # every conv width, bias and SiLU, one and two 16-row blocks per workgroup); the other
-# cases run the v conv as a launch of its own.
+# cases run the v conv as a launch of its own. Groups of 4, 9 and 12 v-heads per k-head
+# take the intra-chunk kernel's decay terms in one batch of up to 8 v-heads and in two.
 CASES = [
     (16, 32, 128, "bf16", 4, 0, False, 64, (1, 17, 64, 0, 300, 130), 0),
     (2, 4, 64, "bf16", 3, 1, True, 32, (2, 1, 70, 33), 0),
@@ -81,6 +82,9 @@ CASES = [
     (2, 4, 128, "f32", 3, 1, True, 64, (130, 1, 64), 1),
     (2, 4, 64, "bf16", 2, 0, False, 64, (65, 2, 129), 1),
     (8, 32, 32, "f32", 4, 1, True, 64, (70, 1, 200, 0, 64, 3, 130, 17), 1),
+    (2, 8, 128, "bf16", 4, 1, True, 64, (200, 64), 1),
+    (1, 12, 32, "bf16", 4, 1, True, 16, (50, 3, 17), 1),
+    (1, 9, 64, "f32", 3, 0, False, 64, (130, 64, 1), 0),
 ]
 
 
