@@ -531,13 +531,18 @@ __device__ __forceinline__ void commit_conv_rows(const PrefillArgs& a, int h, in
 // LDS of the intra-chunk kernel, in floats. K^ and Q^ live only until K K^T and Q K^T are
 // in registers; then G and QK take K^'s place and A and T take Q^'s, so the peak is two
 // areas, each the largest of K^ as fp32 rows, K^ as bf16 hi and lo planes and two C x C
-// matrices (70 KB at C = 64, D = 128); with the decay terms of up to 8 v-heads (4 KB) two
+// matrices (74 KB at C = 64, D = 128); with the decay terms of up to 8 v-heads (4 KB) two
 // workgroups still fit on a CU.
 template <int D, int C>
 struct IntraLayout {
-  static constexpr int KP = D + 4;  // padded row of K^/Q^
+  // Row strides of K^ and Q^ are 32 bytes more than a multiple of 64 (fp32 rows D + 8
+  // values, bf16 plane rows D + 16): the MFMA fragment reads of steps 1b and 2 (16 rows,
+  // one 16-byte group per lane, groups 16 bytes apart across the four 16-lane quarters)
+  // then meet no bank conflict on gfx950, where rows D + 4 (or D + 8) values long cost
+  // twice the cycles (measured with per-pattern bank-conflict counters).
+  static constexpr int KP = D + 8;  // padded row of K^/Q^
   static constexpr int CP = C + 4;  // padded row of C x C matrices
-  static constexpr int KHF = D + 8;  // a row of K^ (or Q^) as bf16 hi and lo planes, in floats
+  static constexpr int KHF = D + 16;  // a row of K^ (or Q^) as bf16 hi and lo planes, in floats
   static constexpr int RS0 = (C * KP > 2 * C * CP) ? C * KP : 2 * C * CP;
   static constexpr int RS = (RS0 > C * KHF) ? RS0 : C * KHF;  // one area
   static constexpr int OFF_K = 0;        // K^   alias  G, QK
