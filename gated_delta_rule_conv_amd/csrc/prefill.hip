@@ -387,7 +387,7 @@ struct QKMap {
 // first token, from its conv state) into registers, not yet normalised; rows >= n are zero.
 // The per-channel arithmetic is ConvTaps::apply, as in the conv kernels, so the values are
 // those the conv kernel would have written. The K-1 rows before the strip are loaded once.
-template <typename T, int K, int D, int C>
+template <typename T, int K, int D, int C, bool SILU>
 __device__ __forceinline__ void conv_qk_rows_k(const PrefillArgs& a, int h, int t0, int n, int seq_start, int s,
                                                float (&out)[QKMap<D, C>::RPT][kConvVec], int tid) {
   using QM = QKMap<D, C>;
@@ -408,7 +408,6 @@ __device__ __forceinline__ void conv_qk_rows_k(const PrefillArgs& a, int h, int 
   GT* bs = (GT*)static_cast<const T*>(has_b ? a.conv.b : a.conv.w);  // (taps stand in when there is no bias)
   const int64_t cstride = a.conv.channels;
   const int pos0 = t0 - seq_start;  // position of the chunk's first row in its sequence
-  const bool silu = a.conv.silu != 0;
   const int ch = (QM::is_q(tid) ? 0 : a.r.hk * D) + h * D + QM::col(tid);  // channel of x, the taps and the conv state
   typename V8::Raw wr[K], br;
 #pragma unroll
@@ -433,8 +432,19 @@ __device__ __forceinline__ void conv_qk_rows_k(const PrefillArgs& a, int h, int 
 #pragma unroll
       for (int j = 0; j < K - 1; ++j) V8::convert(z[i + j], win[j]);
       V8::convert(z[i + K - 1], cur);
-      taps.apply(win, cur, silu, out[i]);
+      taps.apply(win, cur, SILU, out[i]);
     }
+  }
+}
+
+template <typename T, int K, int D, int C>
+__device__ __forceinline__ void conv_qk_rows_act(const PrefillArgs& a, int h, int t0, int n, int seq_start, int s,
+                                                 float (&out)[QKMap<D, C>::RPT][kConvVec], int tid) {
+  // (the activation as a template argument: no per-value select)
+  if (a.conv.silu) {
+    conv_qk_rows_k<T, K, D, C, true>(a, h, t0, n, seq_start, s, out, tid);
+  } else {
+    conv_qk_rows_k<T, K, D, C, false>(a, h, t0, n, seq_start, s, out, tid);
   }
 }
 
@@ -443,15 +453,15 @@ __device__ __forceinline__ void conv_qk_rows(const PrefillArgs& a, int h, int t0
                                              float (&out)[QKMap<D, C>::RPT][kConvVec], int tid) {
   if (a.conv.bf16) {
     switch (a.conv.width) {
-      case 2: conv_qk_rows_k<uint16_t, 2, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
-      case 3: conv_qk_rows_k<uint16_t, 3, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
-      default: conv_qk_rows_k<uint16_t, 4, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
+      case 2: conv_qk_rows_act<uint16_t, 2, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
+      case 3: conv_qk_rows_act<uint16_t, 3, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
+      default: conv_qk_rows_act<uint16_t, 4, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
     }
   } else {
     switch (a.conv.width) {
-      case 2: conv_qk_rows_k<float, 2, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
-      case 3: conv_qk_rows_k<float, 3, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
-      default: conv_qk_rows_k<float, 4, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
+      case 2: conv_qk_rows_act<float, 2, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
+      case 3: conv_qk_rows_act<float, 3, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
+      default: conv_qk_rows_act<float, 4, D, C>(a, h, t0, n, seq_start, s, out, tid); break;
     }
   }
 }
@@ -688,17 +698,51 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     const bool isq = QM::is_q(tid);
     const int col = QM::col(tid), r0 = QM::row0(tid);
     const float num = isq ? r.scale : 1.0f;
+    // Squared norms of the thread's rows; every lane of a row's group holds the same bits
+    // (group_sum). Where a row's group spans at least RPT lanes, lane l of each aligned run
+    // of RPT lanes forms the factor of row l % RPT only and the RPT factors are gathered
+    // from those lanes (the same bits as if each lane formed all of them), instead of every
+    // lane taking RPT square roots and divisions.
+    constexpr int RPT = QM::RPT;
+    constexpr bool kShare = (RPT == 2 || RPT == 4) && D / kConvVec >= RPT;
+    float ss[RPT], rs[RPT];
 #pragma unroll
-    for (int i = 0; i < QM::RPT; ++i) {
-      float ss = 0.f;
+    for (int i = 0; i < RPT; ++i) {
+      ss[i] = 0.f;
 #pragma unroll
-      for (int c = 0; c < kConvVec; ++c) ss = fmaf(rows[i][c], rows[i][c], ss);
-      ss = group_sum<D / kConvVec>(ss);
+      for (int c = 0; c < kConvVec; ++c) ss[i] = fmaf(rows[i][c], rows[i][c], ss[i]);
+      ss[i] = group_sum<D / kConvVec>(ss[i]);
+    }
+    auto factor = [&](float sq) { return r.qk_norm ? num / sqrtf(sq + r.eps) : num; };
+    if constexpr (kShare) {
+      const int mine = lane % RPT;
+      float sq = ss[0];
+#pragma unroll
+      for (int i = 1; i < RPT; ++i) sq = mine == i ? ss[i] : sq;
+      const float f = factor(sq);
+      auto from = [&](auto ctrl) {  // quad_perm DPP move
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(f), decltype(ctrl)::value, 0xF, 0xF, false));
+      };
+      if constexpr (RPT == 4) {  // lane i of the quad: quad_perm [i, i, i, i]
+        rs[0] = from(std::integral_constant<int, 0x00>());
+        rs[1] = from(std::integral_constant<int, 0x55>());
+        rs[2] = from(std::integral_constant<int, 0xAA>());
+        rs[3] = from(std::integral_constant<int, 0xFF>());
+      } else {  // lane i of each pair: quad_perm [i, i, 2 + i, 2 + i]
+        rs[0] = from(std::integral_constant<int, 0xA0>());
+        rs[1] = from(std::integral_constant<int, 0xF5>());
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) rs[i] = factor(ss[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
       const int row = r0 + i;
-      const float rs = row < n ? (r.qk_norm ? num / sqrtf(ss + r.eps) : num) : 0.f;
+      if (row >= n) rs[i] = 0.f;
       float v[kConvVec];
 #pragma unroll
-      for (int c = 0; c < kConvVec; ++c) v[c] = rows[i][c] * rs;
+      for (int c = 0; c < kConvVec; ++c) v[c] = rows[i][c] * rs[i];
       if (tid < QM::ACTIVE) {
         if constexpr (kPlanes) {
           // (the split is Mma<>::split's)
