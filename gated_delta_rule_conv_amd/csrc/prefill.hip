@@ -415,23 +415,43 @@ __device__ __forceinline__ void conv_qk_rows_k(const PrefillArgs& a, int h, int 
   br = V8::load_raw_g(bs + ch);
   const int r0 = QM::row0(tid);
   typename V8::Raw z[RPT + K - 1];  // z rows r0 - (K-1) .. r0 + RPT - 1 (chunk coordinates)
+  if (pos0 >= K - 1 && a.conv.x_stride <= 0x7FFFFFFF) {
+    // (past a sequence's first K-1 tokens every row comes from x: one base row, t0 - (K-1),
+    // and 32-bit row indices)
+    GT* xb = x + static_cast<int64_t>(t0 - (K - 1)) * a.conv.x_stride + ch;
+    const uint32_t xs = static_cast<uint32_t>(a.conv.x_stride);
 #pragma unroll
-  for (int i = 0; i < RPT + K - 1; ++i) {
-    const int rr = min(r0 - (K - 1) + i, n - 1);  // rows past the chunk's end repeat its last
-    const int p = pos0 + rr;                       // position in the sequence
-    GT* src = p >= 0 ? x + static_cast<int64_t>(seq_start + p) * a.conv.x_stride + ch
-                     : cs + static_cast<int64_t>(p + K - 1) * cstride + ch;
-    z[i] = V8::load_raw_g(src);
+    for (int i = 0; i < RPT + K - 1; ++i) {
+      const uint32_t idx = min(r0 + i, n - 1 + (K - 1));  // rows past the chunk's end repeat its last
+      z[i] = V8::load_raw_g(xb + static_cast<uint64_t>(idx) * xs);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RPT + K - 1; ++i) {
+      const int rr = min(r0 - (K - 1) + i, n - 1);  // rows past the chunk's end repeat its last
+      const int p = pos0 + rr;                       // position in the sequence
+      GT* src = p >= 0 ? x + static_cast<int64_t>(seq_start + p) * a.conv.x_stride + ch
+                       : cs + static_cast<int64_t>(p + K - 1) * cstride + ch;
+      z[i] = V8::load_raw_g(src);
+    }
   }
   ConvTaps<T, K> taps;
   taps.from_raw(wr, br, has_b);
+  // each z row converted once; row i's window is rows i .. i + K - 1
+  float zf[RPT + K - 1][kConvVec];
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) V8::convert(z[j], zf[j]);
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
+    V8::convert(z[i + K - 1], zf[i + K - 1]);
     if (r0 + i < n) {
       float win[K - 1][kConvVec], cur[kConvVec];
 #pragma unroll
-      for (int j = 0; j < K - 1; ++j) V8::convert(z[i + j], win[j]);
-      V8::convert(z[i + K - 1], cur);
+      for (int j = 0; j < K - 1; ++j)
+#pragma unroll
+        for (int c = 0; c < kConvVec; ++c) win[j][c] = zf[i + j][c];
+#pragma unroll
+      for (int c = 0; c < kConvVec; ++c) cur[c] = zf[i + K - 1][c];
       taps.apply(win, cur, SILU, out[i]);
     }
   }
