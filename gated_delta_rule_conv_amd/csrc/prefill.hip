@@ -1375,15 +1375,27 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
   auto load_x = [&](int c, In& in) {
     if constexpr (XV != 0) {
       const int pbase = c * C + tt * 16 + 4 * lg - (kw - 1);
+      if (c > 0 && xs <= 0x7FFFFFFF) {
+        // (past the first chunk every position is in the sequence: one base row and 32-bit
+        // row indices; the same loads in the same order as the general form below)
+        GXT* xb = xv + static_cast<int64_t>(start) * xs + vch0;
 #pragma unroll
-      for (int i = 0; i < kXWin; ++i) {
-        const int p = min(pbase + i, len - 1);
+        for (int i = 0; i < kXWin; ++i) {
+          const uint32_t p = min(pbase + i, len - 1);
 #pragma unroll
-        for (int q = 0; q < NR; ++q) {
-          const int ch = vch0 + q * kDVB;
-          GXT* src = p >= 0 ? xv + static_cast<int64_t>(start + p) * xs + ch
-                            : cs + static_cast<int64_t>(p + kw - 1) * cst + ch;
-          in.xw[q][i] = *src;
+          for (int q = 0; q < NR; ++q) in.xw[q][i] = xb[static_cast<uint64_t>(p) * static_cast<uint32_t>(xs) + q * kDVB];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kXWin; ++i) {
+          const int p = min(pbase + i, len - 1);
+#pragma unroll
+          for (int q = 0; q < NR; ++q) {
+            const int ch = vch0 + q * kDVB;
+            GXT* src = p >= 0 ? xv + static_cast<int64_t>(start + p) * xs + ch
+                              : cs + static_cast<int64_t>(p + kw - 1) * cst + ch;
+            in.xw[q][i] = *src;
+          }
         }
       }
     }
