@@ -1474,19 +1474,23 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
     }
   };
   // rows t < n of this wave's token tile of O for chunk c
+  // (element (token, j, column) of o is at token * hv * D + j * D + column; the lane's
+  // column of block q at token start is obase + 16 q, and a token's offset from it is
+  // formed from a 32-bit token index)
+  const int64_t obase = (static_cast<int64_t>(start) * r.hv + j) * D + blk * kDVB + l16;
+  const uint32_t orow = static_cast<uint32_t>(r.hv * D);
   auto store_o = [&](int c, int n, const f32x4 (&o)[NR]) {
-    const int t0 = start + c * C;
 #pragma unroll
-    for (int q = 0; q < NR; ++q) {
+    for (int rr = 0; rr < 4; ++rr) {
+      const int t = tt * 16 + 4 * lg + rr;
+      if (kOut && t < n) {
+        const int64_t e = obase + static_cast<int64_t>(static_cast<uint64_t>(static_cast<uint32_t>(c * C + t)) * orow);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int t = tt * 16 + 4 * lg + rr;
-        if (kOut && t < n) {
-          const int64_t e = (static_cast<int64_t>(t0 + t) * r.hv + j) * D + (blk + q) * kDVB + l16;
+        for (int q = 0; q < NR; ++q) {
           if (r.o_bf16)
-            static_cast<uint16_t*>(r.o)[e] = f32_to_bf16_rne(o[q][rr]);
+            static_cast<uint16_t*>(r.o)[e + q * kDVB] = f32_to_bf16_rne(o[q][rr]);
           else
-            static_cast<float*>(r.o)[e] = o[q][rr];
+            static_cast<float*>(r.o)[e + q * kDVB] = o[q][rr];
         }
       }
     }
