@@ -1147,7 +1147,10 @@ template <int POL, int D, int C, bool PF, int MODE, int NR = 1, int XV = 0>
 __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_chunk_kernel(PrefillArgs a, Workspace w) {
   static_assert(NR == 1 || (NR == 2 && MODE == kModeWhole), "two blocks per workgroup: whole sequences only");
   static_assert(XV == 0 || (MODE == kModeWhole && PF && C == 64), "v convolved in the kernel: whole sequences, 64-token chunks");
-  using XT = typename std::conditional<XV == 2, float, uint16_t>::type;  // x dtype of the fused v conv
+  // fused v conv: XV = x dtype (1 bf16, 2 fp32) + 4 with SiLU (the activation chosen at
+  // compile time, so that the conv computes no activation it then discards)
+  using XT = typename std::conditional<(XV & 3) == 2, float, uint16_t>::type;
+  constexpr bool kVAct = (XV & 4) != 0;
   using M = Mma<POL>;
   using SP = Split<POL>;
   using F = typename M::Frag;
@@ -1226,7 +1229,7 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
     cs = (GXTw*)reinterpret_cast<XT*>(a.conv.state_ptrs[s]);
   }
   auto xval = [](XT v) {
-    if constexpr (XV == 1) return __uint_as_float(static_cast<uint32_t>(v) << 16);
+    if constexpr ((XV & 3) == 1) return __uint_as_float(static_cast<uint32_t>(v) << 16);
     else return static_cast<float>(v);
   };
   // new conv-state row i = z row len + i, z = [old conv state (K-1 rows) | the sequence's x],
@@ -1403,7 +1406,6 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
   // v at this lane's 4 rows of chunk c, from the window
   auto conv_v = [&](In& in) {
     if constexpr (XV != 0) {
-      const bool act = a.conv.silu != 0;
 #pragma unroll
       for (int q = 0; q < NR; ++q) {
 #pragma unroll
@@ -1412,7 +1414,7 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
             if (jj < kw) acc = fmaf(cw[q][jj], xval(in.xw[q][rr + jj]), acc);
-          if (act) acc = gdn::silu(acc);
+          if constexpr (kVAct) acc = gdn::silu(acc);
           in.vv[q][rr] = vscale * acc;
         }
       }
@@ -1772,7 +1774,8 @@ __global__ __launch_bounds__(kInterThreads) void segment_scan_kernel(PrefillArgs
   }
 }
 
-// Whole sequences: NR 16-row blocks per workgroup, prefetching; XV: the fused v conv (0: none)
+// Whole sequences: NR 16-row blocks per workgroup, prefetching; XV: the fused v conv (0: none;
+// else the x dtype, 1 bf16 or 2 fp32, plus 4 with SiLU)
 template <int POL, int D, int C, int NR, int XV>
 void launch_whole(const PrefillArgs& a, const Workspace& w, unsigned workgroups, hipStream_t s) {
   inter_chunk_kernel<POL, D, C, true, kModeWhole, NR, XV><<<workgroups, kInterThreads, 0, s>>>(a, w);
@@ -1803,12 +1806,17 @@ hipError_t launch_chunked(const PrefillArgs& a, const Workspace& w, hipStream_t 
   const bool two = blocks >= 2 * kInterPrefetchMaxCUs;  // two 16-row blocks per workgroup (NBLK is even)
   if constexpr (C == 64) {
     if (a.v_in_inter) {
+      auto go = [&](auto xv) {
+        constexpr int XV = decltype(xv)::value;
+        if (two) launch_whole<POL, D, C, 2, XV>(a, w, blocks / 2, s);
+        else launch_whole<POL, D, C, 1, XV>(a, w, blocks, s);
+      };
       if (a.conv.bf16) {
-        if (two) launch_whole<POL, D, C, 2, 1>(a, w, blocks / 2, s);
-        else launch_whole<POL, D, C, 1, 1>(a, w, blocks, s);
+        if (a.conv.silu) go(std::integral_constant<int, 5>());
+        else go(std::integral_constant<int, 1>());
       } else {
-        if (two) launch_whole<POL, D, C, 2, 2>(a, w, blocks / 2, s);
-        else launch_whole<POL, D, C, 1, 2>(a, w, blocks, s);
+        if (a.conv.silu) go(std::integral_constant<int, 6>());
+        else go(std::integral_constant<int, 2>());
       }
       return hipGetLastError();
     }
