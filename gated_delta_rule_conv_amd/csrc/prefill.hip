@@ -897,21 +897,23 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     }
     __syncthreads();
 
-    // diagonal 16x16 blocks by forward substitution: lane c of wave b owns column c
-    for (int b = wave; b < NB; b += kWaves) {
-      if (lane < 16) {
-        const int c = lane;
-        float x[16];
+    // diagonal 16x16 blocks by forward substitution, all on one wave: lane 16 b + c owns
+    // column c of block b. (One block per wave would issue the same instructions on four
+    // waves with 16 lanes each; the kernel's time follows the total work of the two
+    // workgroups sharing a CU, so the other waves leave the SIMDs to the other one.)
+    static_assert(NB <= 4, "the diagonal blocks fit one wave");
+    if (wave == 1 && lane < NB * 16) {
+      const int b = lane >> 4, c = lane & 15;
+      float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float acc = (i == c) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) {
+        float acc = (i == c) ? 1.f : 0.f;
 #pragma unroll
-          for (int k = 0; k < i; ++k) acc = fmaf(-Am[b * 16 + i][b * 16 + k], x[k], acc);
-          x[i] = acc;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Tm[b * 16 + i][b * 16 + c] = x[i];
+        for (int k = 0; k < i; ++k) acc = fmaf(-Am[b * 16 + i][b * 16 + k], x[k], acc);
+        x[i] = acc;
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Tm[b * 16 + i][b * 16 + c] = x[i];
     }
     __syncthreads();
 
