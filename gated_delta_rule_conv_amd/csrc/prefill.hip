@@ -598,6 +598,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
   constexpr int NVF = D / KSTEP;              // k-steps over the head dim
   constexpr int NKF = FragCount<POL>::nk(C);  // k-steps over the chunk (padded)
+  constexpr bool kWholeK = NKF * KSTEP == C && KPL % 4 == 0;  // no fragment k range runs past the chunk
   __shared__ __attribute__((aligned(16))) float smem[Lo::TOTAL];
   float(*Kh)[KP] = reinterpret_cast<float(*)[KP]>(smem + Lo::OFF_K);
   float(*Qh)[KP] = reinterpret_cast<float(*)[KP]>(smem + Lo::OFF_Q);
@@ -881,17 +882,34 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
       if ((blk % NKF) * KSTEP >= (blk / NKF + 1) * 16) continue;
       const int t = (blk / NKF) * 16 + ln % 16, s0 = (blk % NKF) * KSTEP + KPL * (ln / 16);
       float pv[KPL];
+      if constexpr (kWholeK) {
+        // (the lane's k range lies inside the chunk: its LDS values are read as whole
+        // 16-byte groups and the mask is applied by selection; the same arithmetic)
+        const float gt = gamj[t], bt = betj[t];
+        float gs[KPL], qk[KPL], gg[KPL];
+        load_k<KPL>(gamj + s0, gs);
+        load_k<KPL>(&QKm[t][s0], qk);
+        load_k<KPL>(&Gm[t][s0], gg);
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) {
-        const int s = s0 + i;
-        float av = 0.f;
-        pv[i] = 0.f;
-        if (s <= t) {
-          const float dec = expf(gamj[t] - gamj[s]);
-          pv[i] = dec * QKm[t][s];
-          if (s < t) av = betj[t] * dec * Gm[t][s];
+        for (int i = 0; i < KPL; ++i) {
+          const int s = s0 + i;
+          const float dec = expf(gt - gs[i]);  // (s > t: unused, possibly inf)
+          pv[i] = s <= t ? dec * qk[i] : 0.f;
+          Am[t][s] = s < t ? bt * dec * gg[i] : 0.f;
         }
-        if (s < C) Am[t][s] = av;
+      } else {
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+          const int s = s0 + i;
+          float av = 0.f;
+          pv[i] = 0.f;
+          if (s <= t) {
+            const float dec = expf(gamj[t] - gamj[s]);
+            pv[i] = dec * QKm[t][s];
+            if (s < t) av = betj[t] * dec * Gm[t][s];
+          }
+          if (s < C) Am[t][s] = av;
+        }
       }
       FIO::store(pp + static_cast<size_t>(blk) * FIO::BYTES, ln, pv);
     }
@@ -952,8 +970,15 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
       if ((blk % NKF) * KSTEP >= (blk / NKF + 1) * 16) continue;  // (above the diagonal, as P)
       const int t = (blk / NKF) * 16 + ln % 16, s0 = (blk % NKF) * KSTEP + KPL * (ln / 16);
       float tv[KPL];
+      if constexpr (kWholeK) {
+        float tr[KPL];
+        load_k<KPL>(&Tm[t][s0], tr);
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) tv[i] = (s0 + i <= t) ? Tm[t][s0 + i] : 0.f;
+        for (int i = 0; i < KPL; ++i) tv[i] = (s0 + i <= t) ? tr[i] : 0.f;
+      } else {
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) tv[i] = (s0 + i <= t) ? Tm[t][s0 + i] : 0.f;
+      }
       FIO::store(tp + static_cast<size_t>(blk) * FIO::BYTES, ln, tv);
     }
     __syncthreads();
@@ -1175,6 +1200,7 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
   char* Ut = Rt + NR * R_BYTES;       // U^T          [NR][16][C]  B operand of P U
   char* Us = Ut + NR * R_BYTES;       // (e^{gam_n-gam} U)^T       A operand of the update
   char* Kl = Us + NR * R_BYTES;       // K^           [C][D]       B operand of the update
+  __shared__ __attribute__((aligned(16))) float Fl[2][3 * C];  // (prefetching form) e^gam, beta, e^{gam_n-gam} of two chunks
 
   const RecurArgs& r = a.r;
   constexpr int RB = MODE == kModeTransfer ? 2 * NBLK : NBLK / NR;  // workgroups per head
@@ -1325,7 +1351,7 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
     chunk_ptrs(c, kq, tp, gb);
     const int t0 = start + c * C;
     in.n = min(C, len - c * C);
-    in.egn = gb[C - 1];
+    if constexpr (!PF) in.egn = gb[C - 1];
     if (active) {
       const char* mrows = tp + (qside ? static_cast<size_t>(NT) * NK * FIO::BYTES : 0);
       // (fragments wholly above the diagonal are not in the workspace, and their products
@@ -1336,13 +1362,16 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
           in.mf[kk] = FIO::load(mrows + static_cast<size_t>(tt * NK + kk) * FIO::BYTES, lane);
       // the factors of this lane's 4 output rows are 4 consecutive floats of each array;
       // the Q side uses e^gam only
-      const float4 g4 = *reinterpret_cast<const float4*>(gb + tt * 16 + 4 * lg);
-      in.eg[0] = g4.x; in.eg[1] = g4.y; in.eg[2] = g4.z; in.eg[3] = g4.w;
-      if (!qside) {
-        const float4 b4 = *reinterpret_cast<const float4*>(gb + C + tt * 16 + 4 * lg);
-        in.bt[0] = b4.x; in.bt[1] = b4.y; in.bt[2] = b4.z; in.bt[3] = b4.w;
-        const float4 d4 = *reinterpret_cast<const float4*>(gb + 2 * C + tt * 16 + 4 * lg);
-        in.ed[0] = d4.x; in.ed[1] = d4.y; in.ed[2] = d4.z; in.ed[3] = d4.w;
+      // (the prefetching form takes the factors from LDS instead: see Fl)
+      if constexpr (!PF) {
+        const float4 g4 = *reinterpret_cast<const float4*>(gb + tt * 16 + 4 * lg);
+        in.eg[0] = g4.x; in.eg[1] = g4.y; in.eg[2] = g4.z; in.eg[3] = g4.w;
+        if (!qside) {
+          const float4 b4 = *reinterpret_cast<const float4*>(gb + C + tt * 16 + 4 * lg);
+          in.bt[0] = b4.x; in.bt[1] = b4.y; in.bt[2] = b4.z; in.bt[3] = b4.w;
+          const float4 d4 = *reinterpret_cast<const float4*>(gb + 2 * C + tt * 16 + 4 * lg);
+          in.ed[0] = d4.x; in.ed[1] = d4.y; in.ed[2] = d4.z; in.ed[3] = d4.w;
+        }
       }
       if (with_v) {
 #pragma unroll
@@ -1558,6 +1587,43 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
     // wait would otherwise have to include it (with loads and stores both outstanding the
     // compiler can only wait for everything). The prefetch index is clamped rather than
     // guarded (the last chunk is simply read twice).
+    // The decay factors of a chunk (3 C floats, contiguous in the workspace) are loaded by
+    // the Q side with one 16-byte load per lane, two chunks ahead, and written into Fl by
+    // its token-tile-0 wave at the top of the step before their chunk's; every wave then
+    // reads its own from Fl at the top of that chunk's step. (Each lane loading its 4
+    // tokens' factors itself took 16 of a step's ~140 vector load instructions, whose issue
+    // is what the step's loads wait on; this takes 4. Buffer (c + 1) % 2 is rewritten at the
+    // top of step c, after the barriers of step c - 1, at whose top chunk c - 1's factors
+    // were last read from it.)
+    constexpr int kFL = 3 * C / 4;  // 16-byte pieces of a chunk's factors
+    auto load_fac = [&](int c) {
+      const char *kq, *tp;
+      const float* gb;
+      chunk_ptrs(c, kq, tp, gb);
+      return *reinterpret_cast<const float4*>(gb + 4 * min(lane, kFL - 1));
+    };
+    auto put_fac = [&](int c, const float4& f) {
+      if (tt == 0 && lane < kFL) *reinterpret_cast<float4*>(&Fl[c & 1][4 * lane]) = f;
+    };
+    auto get_fac = [&](int c, In& in) {
+      const float* f = Fl[c & 1];
+      const float4 g4 = *reinterpret_cast<const float4*>(f + tt * 16 + 4 * lg);
+      in.eg[0] = g4.x; in.eg[1] = g4.y; in.eg[2] = g4.z; in.eg[3] = g4.w;
+      if (!qside) {
+        const float4 b4 = *reinterpret_cast<const float4*>(f + C + tt * 16 + 4 * lg);
+        in.bt[0] = b4.x; in.bt[1] = b4.y; in.bt[2] = b4.z; in.bt[3] = b4.w;
+        const float4 d4 = *reinterpret_cast<const float4*>(f + 2 * C + tt * 16 + 4 * lg);
+        in.ed[0] = d4.x; in.ed[1] = d4.y; in.ed[2] = d4.z; in.ed[3] = d4.w;
+      }
+      in.egn = f[C - 1];
+    };
+    float4 fpre = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (qside) {
+      const float4 f0 = load_fac(c_begin);
+      wait_vmem();
+      put_fac(c_begin, f0);
+      fpre = load_fac(min(c_begin + 1, c_end - 1));
+    }
     In in0, in1;
     load(c_begin, in0, !qside && XV == 0);
     if (!qside) {
@@ -1575,6 +1641,7 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
       } else {
         wait_vmem();
       }
+      get_fac(c, in);
       load_a(cn, nxt);
       f32x4 unused[NR];
       if (active) phase1(in, unused);
@@ -1589,8 +1656,10 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
     };
     f32x4 oprev[NR];  // outputs of the previous chunk, stored one step late
     int nprev = 0;    // (0: nothing to store)
-    auto step_q = [&](int c, const In& in, In& nxt, int cn) {
+    auto step_q = [&](int c, In& in, In& nxt, int cn) {
       wait_vmem();
+      put_fac(c + 1, fpre);  // (chunk c + 1's factors, loaded during the previous step)
+      get_fac(c, in);
       store_o(c - 1, nprev, oprev);
       f32x4 oacc[NR];
 #pragma unroll
@@ -1598,6 +1667,7 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
       if (active) phase1(in, oacc);
       __syncthreads();
       load(cn, nxt, false);
+      fpre = load_fac(min(c + 2, c_end - 1));
       __syncthreads();
       if (active) phase3_out(in, oacc);
       if (has_tile) phase3_state(in);
