@@ -617,7 +617,19 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
   // by one scan in every wave (lane s = sequence s); then the chunk-(0, 0) workgroup writes
   // the sequences' chunk offsets and the longest-first order for the inter-chunk kernel
   int4 ent;
-  if (a.table_free) {
+  if (a.table_free && a.num_seqs == 1) {
+    // one sequence: cu_seqlens is [0, total_tokens], so the chunk's place needs no load
+    const int T = a.total_tokens;
+    const int total = (T + C - 1) / C;
+    if (chunk == 0 && h == 0 && wave == 0 && lane == 0) {
+      w.chunk_off[0] = 0;
+      w.chunk_off[1] = total;
+      *w.n_chunks = total;
+      w.order[0] = 0;
+    }
+    if (chunk >= total) return;
+    ent = make_int4(0, chunk * C, min(C, T - chunk * C), chunk);
+  } else if (a.table_free) {
     const int N = a.num_seqs;
     int start = 0, len = 0;
     if (lane < N) {
