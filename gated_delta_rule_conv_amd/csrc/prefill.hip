@@ -1145,6 +1145,7 @@ struct RowTile {
 // x window of the fused v conv (see inter_chunk_kernel): positions a K-side lane reads per
 // row block, its 4 output rows and the up to 3 before them
 constexpr int kXWin = 7;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int POL, int D, int C, int NR, typename XT = float>
 struct ChunkIn {
@@ -1162,6 +1163,7 @@ struct ChunkIn {
   float egn;    // e^{gam_n}, gam_n = gam of the chunk's last token
   int n;        // tokens in the chunk
   XT xw[NR][kXWin];  // fused v conv: the raw x (or conv-state) values of the lane's window
+  u32x4 xt[NR];      // fused v conv, bf16 x: the lane's 16-byte piece of its wave's x tile
 };
 
 // What one launch of the inter-chunk kernel covers:
@@ -1213,6 +1215,11 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
   char* Us = Ut + NR * R_BYTES;       // (e^{gam_n-gam} U)^T       A operand of the update
   char* Kl = Us + NR * R_BYTES;       // K^           [C][D]       B operand of the update
   __shared__ __attribute__((aligned(16))) float Fl[2][3 * C];  // (prefetching form) e^gam, beta, e^{gam_n-gam} of two chunks
+  // fused v conv with bf16 x: each K-side wave's x tile, positions 16 tt - 3 .. 16 tt + 15
+  // of its token tile (rows) by the 16 channels of each row block (32 bytes a row)
+  constexpr bool kXTile = (XV & 3) == 1;
+  constexpr int kXPos = 19;
+  __shared__ __attribute__((aligned(16))) uint16_t Xl[kXTile ? 4 : 1][NR][kXTile ? kXPos * 16 : 8];
 
   const RecurArgs& r = a.r;
   constexpr int RB = MODE == kModeTransfer ? 2 * NBLK : NBLK / NR;  // workgroups per head
@@ -1419,7 +1426,20 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
   // the x window of chunk c (positions past the sequence's end repeat its last row; the
   // rows they would feed are masked where v is used)
   auto load_x = [&](int c, In& in) {
-    if constexpr (XV != 0) {
+    if constexpr (kXTile) {
+      // one 16-byte piece per lane: position p = lane / 2 of the tile, channels 8 (lane % 2)
+      // .. + 7 of each block (lanes past the tile repeat its last piece; positions past the
+      // sequence's end repeat its last row, before its start come from the conv state)
+      const int pl = min(lane, 2 * kXPos - 1);
+      const int P = min(c * C + tt * 16 - 3 + (pl >> 1), len - 1);
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        const int ch = vch0 - l16 + q * kDVB + 8 * (pl & 1);
+        GXT* src = P >= 0 ? xv + static_cast<int64_t>(start + P) * xs + ch
+                          : cs + static_cast<int64_t>(max(P, 1 - kw) + kw - 1) * cst + ch;
+        in.xt[q] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(src);
+      }
+    } else if constexpr (XV != 0) {
       const int pbase = c * C + tt * 16 + 4 * lg - (kw - 1);
       if (c > 0 && xs <= 0x7FFFFFFF) {
         // (past the first chunk every position is in the sequence: one base row and 32-bit
@@ -1448,7 +1468,35 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
   };
   // v at this lane's 4 rows of chunk c, from the window
   auto conv_v = [&](In& in) {
-    if constexpr (XV != 0) {
+    if constexpr (kXTile) {
+      // the wave's tile into LDS, then each lane's window of its channel from there: the
+      // LDS wait and a compiler barrier put the reads after every lane's write (a memory
+      // fence here would also wait for the next chunk's operand loads, still in flight, and
+      // measured 20 us slower at L = 4096). One 16-byte load per block and lane replaces 7
+      // two-byte ones, of the ~140 vector loads a step issues.
+      if (lane < 2 * kXPos) {
+#pragma unroll
+        for (int q = 0; q < NR; ++q) *reinterpret_cast<u32x4*>(&Xl[tt][q][8 * lane]) = in.xt[q];
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // (lgkmcnt(0): the tile's writes have landed)
+      asm volatile("" ::: "memory");
+      const int p0 = 4 * lg + 4 - kw;  // tile position of the lane's window start
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        float xwin[kXWin];
+#pragma unroll
+        for (int i = 0; i < kXWin; ++i) xwin[i] = bf16_to_f32(Xl[tt][q][min(p0 + i, kXPos - 1) * 16 + l16]);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          float acc = cb[q];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (jj < kw) acc = fmaf(cw[q][jj], xwin[rr + jj], acc);
+          if constexpr (kVAct) acc = gdn::silu(acc);
+          in.vv[q][rr] = vscale * acc;
+        }
+      }
+    } else if constexpr (XV != 0) {
 #pragma unroll
       for (int q = 0; q < NR; ++q) {
 #pragma unroll
@@ -1649,7 +1697,7 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
     // chunk c + 2 goes into this buffer's slot once its operands are loaded)
     auto step_k = [&](int c, In& in, In& nxt, int cn) {
       if constexpr (XV != 0) {
-        wait_vmem_leaving<kXWin * NR>();
+        wait_vmem_leaving<(kXTile ? 1 : kXWin) * NR>();
       } else {
         wait_vmem();
       }
