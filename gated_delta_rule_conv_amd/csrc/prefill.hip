@@ -889,8 +889,8 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
     // padding of the P fragments is written too. Fragments wholly above the diagonal are
     // neither written nor read: the inter-chunk kernel skips their products (the same
     // test, kk * KSTEP >= 16 (row tile + 1)), and A's upper triangle is never read. Nor is
-    // a lane's part of a fragment whose k range lies wholly above the diagonal (s0 >= 16
-    // (row tile + 1)): the inter-chunk kernel takes zeros for it (for T as well).
+    // a lane's part of a fragment whose k range starts past its row (s0 > t, all zeros):
+    // the inter-chunk kernel takes zeros for it (for T as well).
     for (int e = tid; e < (C / 16) * NKF * 64; e += kThreads) {
       const int blk = e / 64, ln = e % 64;
       if ((blk % NKF) * KSTEP >= (blk / NKF + 1) * 16) continue;
@@ -925,7 +925,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
           if (s < C) Am[t][s] = av;
         }
       }
-      if (s0 < (blk / NKF + 1) * 16) FIO::store(pp + static_cast<size_t>(blk) * FIO::BYTES, ln, pv);
+      if (s0 <= t) FIO::store(pp + static_cast<size_t>(blk) * FIO::BYTES, ln, pv);
     }
     __syncthreads();
 
@@ -993,7 +993,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillArgs a, Wo
 #pragma unroll
         for (int i = 0; i < KPL; ++i) tv[i] = (s0 + i <= t) ? Tm[t][s0 + i] : 0.f;
       }
-      if (s0 < (blk / NKF + 1) * 16) FIO::store(tp + static_cast<size_t>(blk) * FIO::BYTES, ln, tv);
+      if (s0 <= t) FIO::store(tp + static_cast<size_t>(blk) * FIO::BYTES, ln, tv);
     }
     __syncthreads();
   }
@@ -1554,7 +1554,7 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
         if (kk * KSTEP < tt * 16 + 16) {
           const F rf =
               (kFullK || kk * KSTEP + kl < C) ? TR::load(Rt + q * R_BYTES, l16, kk * KSTEP + kl) : SP::zero();
-          M::mma3(u3, kk * KSTEP + kl < tt * 16 + 16 ? in.mf[kk] : SP::zero(), rf);
+          M::mma3(u3, kk * KSTEP + kl <= tt * 16 + l16 ? in.mf[kk] : SP::zero(), rf);
         }
       }
       const f32x4 uacc = total(u3);
@@ -1601,7 +1601,7 @@ __global__ __launch_bounds__(kInterThreads, (PF || NR > 1) ? 1 : 2) void inter_c
         if (kk * KSTEP < tt * 16 + 16) {
           const F uf =
               (kFullK || kk * KSTEP + kl < C) ? TR::load(Ut + q * R_BYTES, l16, kk * KSTEP + kl) : SP::zero();
-          M::mma3(o3, kk * KSTEP + kl < tt * 16 + 16 ? in.mf[kk] : SP::zero(), uf);
+          M::mma3(o3, kk * KSTEP + kl <= tt * 16 + l16 ? in.mf[kk] : SP::zero(), uf);
         }
       }
       oacc[q] += total(o3);
